@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.dsa as odsa
+import oracle.hca as ohca
+import test_oracle_dsa as tdsa
+import test_oracle_hca as thca
+
+
+def _expect_caught(pins):
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return
+    pytest.fail("no pin caught the planted mistake")
+
+
+def test_window_off_by_one(monkeypatch):
+    monkeypatch.setattr(ohca, "window_bounds", lambda t, W, bs: (max(0, t - W), max(0, t - W) // bs))
+    _expect_caught([lambda: thca.test_block_one_is_dense_causal(3), thca.test_golden_tiny_case])
+
+
+def test_blocks_overlapping_window(monkeypatch):
+    def wb(t, W, bs):
+        lo = max(0, t - W + 1)
+        return lo, -(-lo // bs)     # ceil: lets a block overlap the window
+    monkeypatch.setattr(ohca, "window_bounds", wb)
+    _expect_caught([thca.test_golden_tiny_case, thca.test_equal_keys_give_uniform_weights])
+
+
+def test_missing_scale(monkeypatch):
+    real = ohca.attend_row
+    monkeypatch.setattr(ohca, "attend_row", lambda q, k, v, s: real(q, k, v, 1.0))
+    _expect_caught([lambda: thca.test_block_one_is_dense_causal(1)])
+
+
+def test_transposed_compress_weights(monkeypatch):
+    def bad(x, w, block):
+        x = np.asarray(x, dtype=np.float64)
+        B, S, H, d = x.shape
+        n = S // block
+        return np.einsum("bnihd,hi->bnhd", x[:, : n * block].reshape(B, n, block, H, d), np.asarray(w)[:, ::-1])
+    monkeypatch.setattr(oracle, "compress_kv", bad)
+    _expect_caught([thca.test_compress_brute_force_loop, thca.test_compress_one_hot_is_row_copy])
+
+
+def test_relu_dropped(monkeypatch):
+    monkeypatch.setattr(odsa, "index_scores_row",
+                        lambda qI_t, kI, w_t, t: (np.asarray(kI[: t + 1], float) @ np.asarray(qI_t, float).T) @ np.asarray(w_t, float))
+    monkeypatch.setattr(oracle, "index_scores_row", odsa.index_scores_row)
+    _expect_caught([tdsa.test_golden_scores_and_selection, tdsa.test_relu_drops_negative_heads])
+
+
+def test_tie_break_reversed(monkeypatch):
+    def bad(scores, k):
+        n = scores.shape[0]
+        if n <= k:
+            return np.arange(n)
+        order = np.lexsort((-np.arange(n), -scores.astype(np.float32).astype(np.float64)))
+        return np.sort(order[:k])
+    monkeypatch.setattr(odsa, "topk_row", bad)
+    monkeypatch.setattr(oracle, "topk_row", bad)
+    _expect_caught([tdsa.test_golden_scores_and_selection, tdsa.test_topk_matches_stable_sort])
+
+
+def test_non_causal_indexer(monkeypatch):
+    real = odsa.index_scores_row
+    monkeypatch.setattr(odsa, "index_scores_row", lambda qI_t, kI, w_t, t: real(qI_t, kI, w_t, min(t + 1, kI.shape[0] - 1)))
+    _expect_caught([tdsa.test_k_at_least_context_is_dense_causal_mqa, tdsa.test_equal_index_keys_select_first_positions])
