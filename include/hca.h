@@ -1,0 +1,191 @@
+/*
+ * hca.h -- C ABI of libhca.so: the forward path of hybrid sparse attention
+ * (HCA heavily compressed attention + DSA top-k sparse attention) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the ERNIE 5.5 Flash Base pages:
+ *   - mirrorspeed page, section "Hybrid sparse attention, 1/7 full context
+ *     access": every 128 tokens of K/V become one cache entry; HCA layers
+ *     attend over the compressed entries plus a recent short uncompressed
+ *     window; the full-context layers use DSA, where a lightweight indexer
+ *     scores past positions per query and core attention runs on the top-k.
+ *   - ai-club.cn page, section on hybrid attention (MLA + HCA): the attention
+ *     over compressed entries plus recent tokens is dense; HCA heads are 512
+ *     wide, the token-level layers use 256-wide heads.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers on the current HIP device, owned by
+ *     the caller.  The library never allocates or frees memory and keeps no
+ *     pointer after a call returns.  Scratch memory is passed in as a
+ *     caller-owned workspace whose size is given by the *_workspace_size()
+ *     queries.
+ *   - Tensors are batch/sequence/head/dim with the dim axis contiguous
+ *     (stride 1).  The other three axes take element strides through
+ *     hca_strides_t.  Base pointers must be 16-byte aligned and every stride
+ *     a multiple of 16 bytes.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; no call synchronizes.  Device faults surface at the caller's
+ *     next synchronization.
+ *   - Errors: every argument is validated before anything is launched, so a
+ *     call that returns an error has written nothing.  hca_last_error()
+ *     returns a message for the last non-OK status on the calling thread.
+ *     No exception, abort or exit crosses this ABI.  Calls are thread-safe.
+ */
+#ifndef HCA_H_
+#define HCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HCA_OK = 0,
+  HCA_ERR_INVALID = 1,     /* null pointer, bad size, misalignment, aliasing, window not covered */
+  HCA_ERR_UNSUPPORTED = 2, /* a valid request this build has no kernel for (never a silent fallback) */
+  HCA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query says */
+  HCA_ERR_HIP = 4          /* a HIP runtime or launch error; the HIP text is in hca_last_error() */
+} hca_status_t;
+
+typedef enum { HCA_DTYPE_F32 = 0, HCA_DTYPE_BF16 = 1 } hca_dtype_t;
+
+/* Element strides of a [batch, seq, head, dim] tensor whose dim axis is contiguous. */
+typedef struct {
+  int64_t batch;
+  int64_t seq;
+  int64_t head;
+} hca_strides_t;
+
+/* Version of this ABI (1). */
+int hca_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* hca_last_error(void);
+
+/*
+ * hca_compress_kv -- HCA block compression (mirrorspeed page, "Hybrid sparse
+ * attention" section: 128 tokens -> one cache entry).  For every batch b,
+ * block j < seqlen / block and KV head h:
+ *     kc[b, j, h, :] = sum_{i < block} w_k[h, i] * k[b, j*block + i, h, :]
+ *     vc[b, j, h, :] = sum_{i < block} w_v[h, i] * v[b, j*block + i, h, :]
+ * accumulated in fp32, stored in `dt`.  A trailing partial block is not
+ * compressed.
+ *   k, v   : [batch, seqlen, h_kv, head_dim] device, dtype dt (read)
+ *   w_k,w_v: [h_kv, block] fp32 device, contiguous (read)
+ *   kc, vc : [batch, seqlen/block, h_kv, head_dim] device, dtype dt (written)
+ * Supported: head_dim in {64, 128, 256, 512}; any block >= 1.
+ */
+hca_status_t hca_compress_kv(hca_dtype_t dt,
+                             const void* k, hca_strides_t sk,
+                             const void* v, hca_strides_t sv,
+                             const float* w_k, const float* w_v,
+                             void* kc, hca_strides_t skc,
+                             void* vc, hca_strides_t svc,
+                             int batch, int seqlen, int h_kv, int head_dim, int block,
+                             void* stream);
+
+/*
+ * Workspace bytes hca_attn_fwd needs for these sizes (0 when none is needed).
+ * n_blocks and window are the values that will be passed to hca_attn_fwd.
+ */
+size_t hca_attn_fwd_workspace_size(int batch, int seqlen_q, int h_q, int h_kv, int head_dim,
+                                   int n_blocks, int window);
+
+/*
+ * hca_attn_fwd -- HCA attention (mirrorspeed page, "Hybrid sparse attention"
+ * section; ai-club.cn page, hybrid attention section: dense attention over
+ * the compressed sequence plus the most recent uncompressed tokens).
+ *
+ * Query i sits at absolute position t = q_pos0 + i.  It sees
+ *   - the raw window [lo, t] with lo = max(0, t - window + 1), i.e. the
+ *     `window` most recent positions including itself, and
+ *   - the compressed entries j < n_c = floor(lo / block): exactly the blocks
+ *     that end before the window (no block overlaps the window).
+ * For query head h and KV head g = h / (h_q / h_kv):
+ *   o[b,i,h,:] = sum_x softmax_x(scale * <q[b,i,h], key_x>) * value_x
+ * over keys kc[b, 0..n_c-1, g] and k[b, lo-kv_pos0 .. t-kv_pos0, g] (values
+ * from vc and v likewise).  Softmax in fp32; output in dt.
+ *   q   : [batch, seqlen_q, h_q, head_dim]            (read)
+ *   k, v: [batch, seqlen_kv, h_kv, head_dim]          raw K/V at positions kv_pos0 + s (read)
+ *   kc, vc: [batch, n_blocks, h_kv, head_dim]         compressed entries (read)
+ *   o   : [batch, seqlen_q, h_q, head_dim]            (written)
+ *   lse : [batch, h_q, seqlen_q] fp32 contiguous, natural-log logsumexp of the
+ *         scaled logits; may be NULL.
+ * Prefill: q_pos0 = kv_pos0 = 0 and seqlen_kv = seqlen_q.  Decode: seqlen_q = 1.
+ * Errors: HCA_ERR_INVALID when some query's window is not inside
+ * [kv_pos0, kv_pos0 + seqlen_kv) or needs more than n_blocks entries, or when
+ * h_q % h_kv != 0, window < 1 or block < 1.
+ * Kernels: bf16 with head_dim 512 runs the MFMA prefill kernel (seqlen_q > 1)
+ * or the split-key decode kernel (seqlen_q == 1, which uses the workspace);
+ * fp32, and bf16 with another head_dim (multiple of 8, <= 512), run a
+ * one-query-per-workgroup kernel limited to 16384 keys per query.
+ */
+hca_status_t hca_attn_fwd(hca_dtype_t dt,
+                          const void* q, hca_strides_t sq,
+                          const void* k, hca_strides_t sk,
+                          const void* v, hca_strides_t sv,
+                          const void* kc, hca_strides_t skc,
+                          const void* vc, hca_strides_t svc,
+                          void* o, hca_strides_t so,
+                          float* lse,
+                          int batch, int seqlen_q, int64_t q_pos0,
+                          int seqlen_kv, int64_t kv_pos0, int n_blocks,
+                          int h_q, int h_kv, int head_dim, int block, int window, float scale,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes dsa_index_topk needs (score rows for one chunk of queries). */
+size_t dsa_index_topk_workspace_size(int batch, int seqlen, int topk);
+
+/*
+ * dsa_index_topk -- DSA lightweight indexer and causal top-k (mirrorspeed
+ * page, "Hybrid sparse attention" section: the indexer scores historical
+ * positions for each query; attention runs on the top-k).
+ *   s(t, u) = sum_{h < h_i} w_idx[b,t,h] * max(0, <q_idx[b,t,h,:], k_idx[b,u,:]>),  u <= t
+ * computed in fp32.  Row t of idx receives the min(t+1, topk) positions with
+ * the largest s (ties: the smaller position wins; -0 counts as +0) in
+ * unspecified order, then -1 padding.
+ *   q_idx: [batch, seqlen, h_i, d_i] fp32 contiguous (read)
+ *   k_idx: [batch, seqlen, d_i]      fp32 contiguous (read)
+ *   w_idx: [batch, seqlen, h_i]      fp32 contiguous (read)
+ *   idx  : [batch, seqlen, topk]     int32 contiguous (written)
+ * Supported: h_i <= 8, d_i a multiple of 16 and <= 128, topk <= 4096.
+ */
+hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float* w_idx,
+                            int32_t* idx,
+                            int batch, int seqlen, int h_i, int d_i, int topk,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * dsa_sparse_attn_fwd -- DSA core attention over the selected positions
+ * (mirrorspeed page, "Hybrid sparse attention" section; 256-wide heads per
+ * the ai-club.cn page).  For query t and head h, with g = h / (h_q / h_kv):
+ *   o[b,t,h,:] = sum_{u in idx[b,t,:], u >= 0} softmax_u(scale * <q[b,t,h], k[b,u,g]>) * v[b,u,g,:]
+ * Entries equal to -1 are skipped; any order is accepted; every listed
+ * position must lie in [0, seqlen) (checked on the device: a row holding an
+ * out-of-range position is written as NaN).  A row with no valid entry
+ * yields zeros and lse = -inf.
+ *   q: [batch, seqlen, h_q, d_qk]; k: [batch, seqlen, h_kv, d_qk];
+ *   v: [batch, seqlen, h_kv, d_v]; o: [batch, seqlen, h_q, d_v];
+ *   idx: [batch, seqlen, topk] int32 contiguous; lse: [batch, h_q, seqlen] fp32 or NULL.
+ * Supported: bf16, d_qk = d_v = 256, (h_q / h_kv) a multiple of 64.
+ */
+hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt,
+                                 const void* q, hca_strides_t sq,
+                                 const void* k, hca_strides_t sk,
+                                 const void* v, hca_strides_t sv,
+                                 const int32_t* idx,
+                                 void* o, hca_strides_t so,
+                                 float* lse,
+                                 int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v,
+                                 int topk, float scale,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_H_ */

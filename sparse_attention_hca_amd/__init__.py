@@ -1,0 +1,222 @@
+"""Python binding of libhca.so: HCA / DSA forward attention for MI355X (gfx950).
+
+Each function here has the name of the C entry point it wraps and only
+marshals arguments: it reads device pointers, strides and sizes from torch
+tensors, allocates outputs and workspaces with torch when the caller does not
+pass them, and calls the library on the current HIP stream.  All arithmetic
+runs in the HIP kernels of libhca.so.  Without the built library (or without a
+GPU) every call raises; there is no CPU fallback.
+
+Layouts follow the C header ``include/hca.h``: tensors are
+[batch, seq, head, dim] with the dim axis contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhca.so")
+
+HCA_OK, HCA_ERR_INVALID, HCA_ERR_UNSUPPORTED, HCA_ERR_WORKSPACE, HCA_ERR_HIP = range(5)
+HCA_DTYPE_F32, HCA_DTYPE_BF16 = 0, 1
+
+EXPORTS = (
+    "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_attn_fwd_workspace_size",
+    "hca_attn_fwd", "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
+)
+
+
+class HcaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhca.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libhca.so not found at {path}; build it with `python -m sparse_attention_hca_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    S = Strides
+    lib.hca_abi_version.restype = I
+    lib.hca_abi_version.argtypes = []
+    lib.hca_last_error.restype = ctypes.c_char_p
+    lib.hca_last_error.argtypes = []
+    lib.hca_compress_kv.restype = I
+    lib.hca_compress_kv.argtypes = [I, P, S, P, S, P, P, P, S, P, S, I, I, I, I, I, P]
+    lib.hca_attn_fwd_workspace_size.restype = SZ
+    lib.hca_attn_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.hca_attn_fwd.restype = I
+    lib.hca_attn_fwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P,
+                                 I, I, I64, I, I64, I, I, I, I, I, I, F, P, SZ, P]
+    lib.dsa_index_topk_workspace_size.restype = SZ
+    lib.dsa_index_topk_workspace_size.argtypes = [I, I, I]
+    lib.dsa_index_topk.restype = I
+    lib.dsa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, P, SZ, P]
+    lib.dsa_sparse_attn_fwd.restype = I
+    lib.dsa_sparse_attn_fwd.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != HCA_OK:
+        raise HcaError(status, load_library().hca_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HCA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return HCA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _strides(t: torch.Tensor) -> Strides:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [batch, seq, head, dim] tensor with a contiguous dim axis")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def hca_abi_version() -> int:
+    return load_library().hca_abi_version()
+
+
+def hca_last_error() -> str:
+    return load_library().hca_last_error().decode()
+
+
+def hca_compress_kv(k: torch.Tensor, v: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, block: int,
+                    kc: Optional[torch.Tensor] = None, vc: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Weighted block compression of K and V: returns (kc, vc) [B, S // block, H_kv, d]."""
+    lib = load_library()
+    _dev(k, v, w_k, w_v)
+    B, S, H, d = k.shape
+    nb = S // block
+    if kc is None:
+        kc = torch.empty((B, nb, H, d), dtype=k.dtype, device=k.device)
+    if vc is None:
+        vc = torch.empty((B, nb, H, d), dtype=v.dtype, device=v.device)
+    w_k = w_k.contiguous()
+    w_v = w_v.contiguous()
+    _check(lib.hca_compress_kv(_dt(k), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(w_k), _ptr(w_v),
+                               _ptr(kc), _strides(kc), _ptr(vc), _strides(vc), B, S, H, d, block, _stream()))
+    return kc, vc
+
+
+def hca_attn_fwd_workspace_size(batch: int, seqlen_q: int, h_q: int, h_kv: int, head_dim: int,
+                                n_blocks: int, window: int) -> int:
+    return load_library().hca_attn_fwd_workspace_size(batch, seqlen_q, h_q, h_kv, head_dim, n_blocks, window)
+
+
+def hca_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional[torch.Tensor],
+                 vc: Optional[torch.Tensor], *, window: int, block: int, scale: Optional[float] = None,
+                 q_pos0: int = 0, kv_pos0: int = 0, o: Optional[torch.Tensor] = None, return_lse: bool = True,
+                 lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """HCA attention over compressed entries plus the raw window; returns (o, lse)."""
+    lib = load_library()
+    _dev(q, k, v, kc, vc)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    nb = 0 if kc is None else kc.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Sq, Hq, v.shape[3]), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    wsz = lib.hca_attn_fwd_workspace_size(B, Sq, Hq, Hkv, d, nb, window)
+    if workspace is None and wsz:
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=q.device)
+    zs = Strides(0, 0, 0)
+    _check(lib.hca_attn_fwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                            _ptr(kc), zs if kc is None else _strides(kc), _ptr(vc), zs if vc is None else _strides(vc),
+                            _ptr(o), _strides(o), _ptr(lse), B, Sq, q_pos0, Skv, kv_pos0, nb, Hq, Hkv, d, block,
+                            window, float(scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            _stream()))
+    return o, lse
+
+
+def dsa_index_topk_workspace_size(batch: int, seqlen: int, topk: int) -> int:
+    return load_library().dsa_index_topk_workspace_size(batch, seqlen, topk)
+
+
+def dsa_index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w_idx: torch.Tensor, topk: int,
+                   idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ReLU-weighted indexer + causal top-k; returns idx [B, S, topk] int32 (-1 padded, unordered)."""
+    lib = load_library()
+    _dev(q_idx, k_idx, w_idx)
+    B, S, hi, di = q_idx.shape
+    for t in (q_idx, k_idx, w_idx):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("indexer inputs must be contiguous float32")
+    if idx is None:
+        idx = torch.empty((B, S, topk), dtype=torch.int32, device=q_idx.device)
+    wsz = lib.dsa_index_topk_workspace_size(B, S, topk)
+    if workspace is None and wsz:
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=q_idx.device)
+    _check(lib.dsa_index_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(idx), B, S, hi, di, topk,
+                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
+    return idx
+
+
+def dsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                        scale: Optional[float] = None, o: Optional[torch.Tensor] = None, return_lse: bool = True,
+                        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention over the positions listed in idx (-1 skipped); returns (o, lse)."""
+    lib = load_library()
+    _dev(q, k, v, idx)
+    B, S, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    topk = idx.shape[2]
+    if not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be contiguous int32 [B, S, topk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if o is None:
+        o = torch.empty((B, S, Hq, dv), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check(lib.dsa_sparse_attn_fwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                   _ptr(idx), _ptr(o), _strides(o), _ptr(lse), B, S, Hq, Hkv, dqk, dv, topk,
+                                   float(scale), _stream()))
+    return o, lse
+
+
+__all__ = [
+    "load_library", "HcaError", "Strides", "EXPORTS",
+    "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_attn_fwd_workspace_size", "hca_attn_fwd",
+    "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
+]

@@ -1,0 +1,136 @@
+// HCA block compression: each block of `block` consecutive K (or V) rows of one
+// head becomes one cache entry, the per-head weighted sum of those rows
+// (ERNIE 5.5 Flash Base pages, mirrorspeed page, section "Hybrid sparse
+// attention": 128 tokens per cache entry).
+//
+// HBM-bound streaming kernel: one workgroup per (block j, head h, batch b,
+// K-or-V).  Each thread owns one 16-byte column chunk of the head and walks a
+// strided subset of the block's rows with 16-byte loads (a wave reads whole
+// contiguous rows), accumulating in fp32; row groups are reduced through LDS.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace hca {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ x0, LStrides sx0, const float* __restrict__ w0,
+                                                       T* __restrict__ out0, LStrides so0, const T* __restrict__ x1,
+                                                       LStrides sx1, const float* __restrict__ w1, T* __restrict__ out1,
+                                                       LStrides so1, int block) {
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int TPR = D / EPV;         // threads covering one row
+  constexpr int RG = 256 / TPR;        // rows processed side by side
+  static_assert(256 % TPR == 0, "head_dim does not tile a 256-thread workgroup");
+  __shared__ float red[RG][D];
+
+  const int j = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z >> 1;
+  const bool second = blockIdx.z & 1;
+  const T* x = second ? x1 : x0;
+  const LStrides sx = second ? sx1 : sx0;
+  const float* w = (second ? w1 : w0) + (int64_t)h * block;
+  T* out = second ? out1 : out0;
+  const LStrides so = second ? so1 : so0;
+
+  const int tid = threadIdx.x;
+  const int c = tid % TPR, r = tid / TPR;
+  const T* base = x + (int64_t)b * sx.b + (int64_t)j * block * sx.s + (int64_t)h * sx.h + c * EPV;
+
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+
+  int i = r;
+  // 8 rows in flight per thread
+  for (; i + 7 * RG < block; i += 8 * RG) {
+    u32x4 vals[8];
+    float wi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      vals[u] = ld16(base + (int64_t)(i + u * RG) * sx.s);
+      wi[u] = w[i + u * RG];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(wi[u], __uint_as_float(vals[u][e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(wi[u], __uint_as_float(vals[u][e] & 0xffff0000u), acc[2 * e + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wi[u], __uint_as_float(vals[u][e]), acc[e]);
+      }
+    }
+  }
+  for (; i < block; i += RG) {
+    const u32x4 val = ld16(base + (int64_t)i * sx.s);
+    const float wi = w[i];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(wi, __uint_as_float(val[e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(wi, __uint_as_float(val[e] & 0xffff0000u), acc[2 * e + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wi, __uint_as_float(val[e]), acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) red[r][c * EPV + e] = acc[e];
+  __syncthreads();
+
+  T* dst = out + (int64_t)b * so.b + (int64_t)j * so.s + (int64_t)h * so.h;
+  for (int e = tid * 2; e < D; e += 512) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      s0 += red[g][e];
+      s1 += red[g][e + 1];
+    }
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint32_t*>(dst + e) = pack_bf16x2(s0, s1);
+    } else {
+      dst[e] = s0;
+      dst[e + 1] = s1;
+    }
+  }
+}
+
+template <typename T, int D>
+static void launch_t(const void* x, LStrides sx, const float* w, void* out, LStrides so, const void* x2, LStrides sx2,
+                     const float* w2, void* out2, LStrides so2, int batch, int seqlen, int h, int block,
+                     hipStream_t st) {
+  const int nb = seqlen / block;
+  dim3 grid(nb, h, 2 * batch);
+  hipLaunchKernelGGL((compress_kernel<T, D>), grid, dim3(256), 0, st, (const T*)x, sx, w, (T*)out, so, (const T*)x2,
+                     sx2, w2, (T*)out2, so2, block);
+}
+
+hipError_t launch_compress(int dt, const void* x, LStrides sx, const float* w, void* out, LStrides so, const void* x2,
+                           LStrides sx2, const float* w2, void* out2, LStrides so2, int batch, int seqlen, int h, int d,
+                           int block, hipStream_t st) {
+  if (seqlen / block == 0) return hipSuccess;
+#define HCA_COMPRESS_CASE(T, DD)                                                                        \
+  if (d == DD) {                                                                                        \
+    launch_t<T, DD>(x, sx, w, out, so, x2, sx2, w2, out2, so2, batch, seqlen, h, block, st);            \
+    return hipGetLastError();                                                                           \
+  }
+  if (dt == 1) {
+    HCA_COMPRESS_CASE(uint16_t, 64)
+    HCA_COMPRESS_CASE(uint16_t, 128)
+    HCA_COMPRESS_CASE(uint16_t, 256)
+    HCA_COMPRESS_CASE(uint16_t, 512)
+  } else {
+    HCA_COMPRESS_CASE(float, 64)
+    HCA_COMPRESS_CASE(float, 128)
+    HCA_COMPRESS_CASE(float, 256)
+    HCA_COMPRESS_CASE(float, 512)
+  }
+#undef HCA_COMPRESS_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hca

@@ -1,0 +1,278 @@
+// C-ABI layer of libhca: argument validation, error reporting and kernel
+// dispatch.  Every argument is checked before anything is launched, so a call
+// that fails has written nothing.  No exception, abort or exit crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/hca.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hca_status_t fail(hca_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hca_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(HCA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+hca::LStrides ls(hca_strides_t s) { return hca::LStrides{s.batch, s.seq, s.head}; }
+
+size_t elem_size(hca_dtype_t dt) { return dt == HCA_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte range [lo, hi) covered by a [b, s, h, d] tensor with the given strides.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range extent(const void* p, hca_strides_t st, int64_t b, int64_t s, int64_t h, int64_t d, size_t es) {
+  const int64_t last = (b - 1) * st.batch + (s - 1) * st.seq + (h - 1) * st.head + d;
+  return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * (int64_t)es)};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Strides must be non-negative multiples of 16 bytes (the kernels use 16-byte vectors).
+hca_status_t check_tensor(const char* name, const void* p, hca_strides_t st, size_t es, bool nullable = false) {
+  if (!p) {
+    if (nullable) return HCA_OK;
+    return fail(HCA_ERR_INVALID, "%s is NULL", name);
+  }
+  if (!aligned16(p)) return fail(HCA_ERR_INVALID, "%s is not 16-byte aligned", name);
+  const int64_t q = (int64_t)(16 / es);
+  if (st.batch < 0 || st.seq < 0 || st.head < 0 || st.batch % q || st.seq % q || st.head % q)
+    return fail(HCA_ERR_INVALID, "%s strides must be non-negative multiples of 16 bytes", name);
+  return HCA_OK;
+}
+
+#define HCA_TRY(x)                   \
+  do {                               \
+    hca_status_t _s = (x);           \
+    if (_s != HCA_OK) return _s;     \
+  } while (0)
+
+constexpr int64_t kPosLimit = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" {
+
+int hca_abi_version(void) { return 1; }
+
+const char* hca_last_error(void) { return g_last_error.c_str(); }
+
+hca_status_t hca_compress_kv(hca_dtype_t dt, const void* k, hca_strides_t sk, const void* v, hca_strides_t sv,
+                             const float* w_k, const float* w_v, void* kc, hca_strides_t skc, void* vc,
+                             hca_strides_t svc, int batch, int seqlen, int h_kv, int head_dim, int block,
+                             void* stream) {
+  if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (batch <= 0 || seqlen <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0)
+    return fail(HCA_ERR_INVALID, "sizes must be positive (batch %d seqlen %d h_kv %d head_dim %d block %d)", batch,
+                seqlen, h_kv, head_dim, block);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(HCA_ERR_UNSUPPORTED, "hca_compress_kv: head_dim %d not in {64,128,256,512}", head_dim);
+  if (!w_k || !w_v) return fail(HCA_ERR_INVALID, "compressor weights are NULL");
+  const size_t es = elem_size(dt);
+  const int nb = seqlen / block;
+  HCA_TRY(check_tensor("k", k, sk, es));
+  HCA_TRY(check_tensor("v", v, sv, es));
+  HCA_TRY(check_tensor("kc", kc, skc, es, nb == 0));
+  HCA_TRY(check_tensor("vc", vc, svc, es, nb == 0));
+  if (nb == 0) return HCA_OK;  // no complete block: nothing to write
+  if (nb > 0) {
+    const Range rk = extent(k, sk, batch, seqlen, h_kv, head_dim, es), rv = extent(v, sv, batch, seqlen, h_kv, head_dim, es);
+    const Range rkc = extent(kc, skc, batch, nb, h_kv, head_dim, es), rvc = extent(vc, svc, batch, nb, h_kv, head_dim, es);
+    if (overlaps(rkc, rk) || overlaps(rkc, rv) || overlaps(rvc, rk) || overlaps(rvc, rv) || overlaps(rkc, rvc))
+      return fail(HCA_ERR_INVALID, "hca_compress_kv: outputs overlap inputs or each other");
+  }
+  hipError_t e = hca::launch_compress(dt == HCA_DTYPE_BF16 ? 1 : 0, k, ls(sk), w_k, kc, ls(skc), v, ls(sv), w_v, vc,
+                                      ls(svc), batch, seqlen, h_kv, head_dim, block, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hca_compress_kv launch");
+  return HCA_OK;
+}
+
+static int n_keys_of(int64_t t, int window, int block) {
+  const int64_t lo = t - window + 1 > 0 ? t - window + 1 : 0;
+  return (int)(lo / block + (t - lo + 1));
+}
+
+size_t hca_attn_fwd_workspace_size(int batch, int seqlen_q, int h_q, int h_kv, int head_dim, int n_blocks,
+                                   int window) {
+  if (batch <= 0 || seqlen_q != 1 || h_q <= 0 || h_kv <= 0 || h_q % h_kv || head_dim != 512 || window < 1 ||
+      n_blocks < 0)
+    return 0;
+  return hca::decode512_workspace_bytes(batch, h_q, h_kv, n_blocks + window);
+}
+
+hca_status_t hca_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                          const void* v, hca_strides_t sv, const void* kc, hca_strides_t skc, const void* vc,
+                          hca_strides_t svc, void* o, hca_strides_t so, float* lse, int batch, int seqlen_q,
+                          int64_t q_pos0, int seqlen_kv, int64_t kv_pos0, int n_blocks, int h_q, int h_kv,
+                          int head_dim, int block, int window, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_kv <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0)
+    return fail(HCA_ERR_INVALID, "sizes must be positive");
+  if (n_blocks < 0) return fail(HCA_ERR_INVALID, "n_blocks must be >= 0");
+  if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q (%d) must be a multiple of h_kv (%d)", h_q, h_kv);
+  if (window < 1) return fail(HCA_ERR_INVALID, "window must be >= 1");
+  if (block < 1) return fail(HCA_ERR_INVALID, "block must be >= 1");
+  if (q_pos0 < 0 || kv_pos0 < 0) return fail(HCA_ERR_INVALID, "positions must be >= 0");
+  if (q_pos0 + seqlen_q > kPosLimit || kv_pos0 + seqlen_kv > kPosLimit)
+    return fail(HCA_ERR_UNSUPPORTED, "positions beyond 2^30 are not supported");
+  if (!(scale == scale)) return fail(HCA_ERR_INVALID, "scale is NaN");
+  const size_t es = elem_size(dt);
+  HCA_TRY(check_tensor("q", q, sq, es));
+  HCA_TRY(check_tensor("k", k, sk, es));
+  HCA_TRY(check_tensor("v", v, sv, es));
+  HCA_TRY(check_tensor("kc", kc, skc, es, n_blocks == 0));
+  HCA_TRY(check_tensor("vc", vc, svc, es, n_blocks == 0));
+  HCA_TRY(check_tensor("o", o, so, es));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is not 4-byte aligned");
+  // every query's window must be inside the raw K/V and its compressed entries inside kc/vc
+  const int64_t t0 = q_pos0, t1 = q_pos0 + seqlen_q - 1;
+  const int64_t lo0 = t0 - window + 1 > 0 ? t0 - window + 1 : 0;
+  const int64_t lo1 = t1 - window + 1 > 0 ? t1 - window + 1 : 0;
+  if (lo0 < kv_pos0 || t1 >= kv_pos0 + seqlen_kv)
+    return fail(HCA_ERR_INVALID, "raw K/V [%lld, %lld) do not cover the windows [%lld, %lld]", (long long)kv_pos0,
+                (long long)(kv_pos0 + seqlen_kv), (long long)lo0, (long long)t1);
+  if (lo1 / block > n_blocks)
+    return fail(HCA_ERR_INVALID, "queries need %lld compressed entries but n_blocks is %d", (long long)(lo1 / block),
+                n_blocks);
+  // outputs must not overlap inputs
+  {
+    const Range ro = extent(o, so, batch, seqlen_q, h_q, head_dim, es);
+    const Range ins[3] = {extent(q, sq, batch, seqlen_q, h_q, head_dim, es),
+                          extent(k, sk, batch, seqlen_kv, h_kv, head_dim, es),
+                          extent(v, sv, batch, seqlen_kv, h_kv, head_dim, es)};
+    for (const Range& r : ins)
+      if (overlaps(ro, r)) return fail(HCA_ERR_INVALID, "o overlaps an input");
+    if (n_blocks > 0 && (overlaps(ro, extent(kc, skc, batch, n_blocks, h_kv, head_dim, es)) ||
+                         overlaps(ro, extent(vc, svc, batch, n_blocks, h_kv, head_dim, es))))
+      return fail(HCA_ERR_INVALID, "o overlaps an input");
+    if (lse) {
+      const Range rl{(uintptr_t)lse, (uintptr_t)(lse + (size_t)batch * h_q * seqlen_q)};
+      if (overlaps(rl, ro) || overlaps(rl, ins[0]) || overlaps(rl, ins[1]) || overlaps(rl, ins[2]))
+        return fail(HCA_ERR_INVALID, "lse overlaps another tensor");
+    }
+  }
+
+  hca::AttnArgs a;
+  a.dt = dt == HCA_DTYPE_BF16 ? 1 : 0;
+  a.q = q; a.sq = ls(sq);
+  a.k = k; a.sk = ls(sk);
+  a.v = v; a.sv = ls(sv);
+  a.kc = kc; a.skc = ls(skc);
+  a.vc = vc; a.svc = ls(svc);
+  a.o = o; a.so = ls(so);
+  a.lse = lse;
+  a.batch = batch; a.seqlen_q = seqlen_q; a.q_pos0 = q_pos0; a.seqlen_kv = seqlen_kv; a.kv_pos0 = kv_pos0;
+  a.n_blocks = n_blocks; a.h_q = h_q; a.h_kv = h_kv; a.head_dim = head_dim; a.block = block; a.window = window;
+  a.scale = scale;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (dt == HCA_DTYPE_BF16 && head_dim == 512) {
+    if (seqlen_q == 1) {
+      const size_t need = hca::decode512_workspace_bytes(batch, h_q, h_kv, n_keys_of(q_pos0, window, block));
+      if (!workspace || workspace_bytes < need)
+        return fail(HCA_ERR_WORKSPACE, "decode needs a %zu-byte workspace (got %zu)", need, workspace_bytes);
+      if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
+      hipError_t e = hca::launch_attn_decode512(a, workspace, st);
+      if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd decode launch");
+      return HCA_OK;
+    }
+    hipError_t e = hca::launch_attn_prefill512(a, st);
+    if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd prefill launch");
+    return HCA_OK;
+  }
+  // one-query-per-workgroup kernel: fp32, or bf16 with other head sizes
+  if (head_dim > 512 || (head_dim % (16 / (int)es)) != 0)
+    return fail(HCA_ERR_UNSUPPORTED, "hca_attn_fwd: head_dim %d unsupported for this dtype", head_dim);
+  if (n_keys_of(t1, window, block) > hca::kGenericMaxKeys)
+    return fail(HCA_ERR_UNSUPPORTED, "hca_attn_fwd: more than %d keys per query needs bf16 with head_dim 512",
+                hca::kGenericMaxKeys);
+  hipError_t e = hca::launch_attn_generic(a, st);
+  if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd launch");
+  return HCA_OK;
+}
+
+size_t dsa_index_topk_workspace_size(int batch, int seqlen, int topk) {
+  if (batch <= 0 || seqlen <= 0 || topk <= 0) return 0;
+  return hca::dsa_topk_workspace_bytes(batch, seqlen, topk);
+}
+
+hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float* w_idx, int32_t* idx, int batch,
+                            int seqlen, int h_i, int d_i, int topk, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!q_idx || !k_idx || !w_idx || !idx) return fail(HCA_ERR_INVALID, "dsa_index_topk: NULL tensor");
+  if (batch <= 0 || seqlen <= 0 || h_i <= 0 || d_i <= 0 || topk <= 0)
+    return fail(HCA_ERR_INVALID, "dsa_index_topk: sizes must be positive");
+  if (h_i > 8 || d_i % 16 || d_i > 128 || topk > 4096)
+    return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk: needs h_i <= 8, d_i a multiple of 16 <= 128, topk <= 4096");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(idx))
+    return fail(HCA_ERR_INVALID, "dsa_index_topk: tensors must be 16-byte aligned");
+  if (h_i % 4) return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk: h_i must be a multiple of 4");
+  {
+    const Range ri{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)};
+    const Range rq{(uintptr_t)q_idx, (uintptr_t)(q_idx + (size_t)batch * seqlen * h_i * d_i)};
+    const Range rk{(uintptr_t)k_idx, (uintptr_t)(k_idx + (size_t)batch * seqlen * d_i)};
+    const Range rw{(uintptr_t)w_idx, (uintptr_t)(w_idx + (size_t)batch * seqlen * h_i)};
+    if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(ri, rw))
+      return fail(HCA_ERR_INVALID, "dsa_index_topk: idx overlaps an input");
+  }
+  const size_t need = hca::dsa_topk_workspace_bytes(batch, seqlen, topk);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(HCA_ERR_WORKSPACE, "dsa_index_topk needs a %zu-byte workspace (got %zu)", need, workspace_bytes);
+  if (need && !aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
+  hipError_t e = hca::launch_dsa_index_topk(q_idx, k_idx, w_idx, idx, batch, seqlen, h_i, d_i, topk, workspace,
+                                            workspace_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dsa_index_topk launch");
+  return HCA_OK;
+}
+
+hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                                 const void* v, hca_strides_t sv, const int32_t* idx, void* o, hca_strides_t so,
+                                 float* lse, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v, int topk,
+                                 float scale, void* stream) {
+  if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (batch <= 0 || seqlen <= 0 || h_q <= 0 || h_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
+    return fail(HCA_ERR_INVALID, "dsa_sparse_attn_fwd: sizes must be positive");
+  if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q must be a multiple of h_kv");
+  if (!idx) return fail(HCA_ERR_INVALID, "idx is NULL");
+  if (!aligned16(idx)) return fail(HCA_ERR_INVALID, "idx is not 16-byte aligned");
+  const size_t es = elem_size(dt);
+  HCA_TRY(check_tensor("q", q, sq, es));
+  HCA_TRY(check_tensor("k", k, sk, es));
+  HCA_TRY(check_tensor("v", v, sv, es));
+  HCA_TRY(check_tensor("o", o, so, es));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is not 4-byte aligned");
+  if (dt != HCA_DTYPE_BF16 || d_qk != 256 || d_v != 256 || (h_q / h_kv) % 64)
+    return fail(HCA_ERR_UNSUPPORTED, "dsa_sparse_attn_fwd: needs bf16, d_qk = d_v = 256, h_q/h_kv a multiple of 64");
+  {
+    const Range ro = extent(o, so, batch, seqlen, h_q, d_v, es);
+    if (overlaps(ro, extent(q, sq, batch, seqlen, h_q, d_qk, es)) ||
+        overlaps(ro, extent(k, sk, batch, seqlen, h_kv, d_qk, es)) ||
+        overlaps(ro, extent(v, sv, batch, seqlen, h_kv, d_v, es)) ||
+        overlaps(ro, Range{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)}))
+      return fail(HCA_ERR_INVALID, "o overlaps an input");
+  }
+  hipError_t e = hca::launch_dsa_sparse_attn256(q, ls(sq), k, ls(sk), v, ls(sv), idx, o, ls(so), lse, batch, seqlen,
+                                                h_q, h_kv, topk, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dsa_sparse_attn_fwd launch");
+  return HCA_OK;
+}
+
+}  // extern "C"

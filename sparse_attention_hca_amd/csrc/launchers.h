@@ -1,0 +1,52 @@
+// Host-side launcher declarations shared between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hca {
+
+struct LStrides {
+  int64_t b, s, h;
+};
+
+struct AttnArgs {
+  int dt;  // 0 = f32, 1 = bf16
+  const void* q; LStrides sq;
+  const void* k; LStrides sk;
+  const void* v; LStrides sv;
+  const void* kc; LStrides skc;
+  const void* vc; LStrides svc;
+  void* o; LStrides so;
+  float* lse;
+  int batch, seqlen_q;
+  int64_t q_pos0;
+  int seqlen_kv;
+  int64_t kv_pos0;
+  int n_blocks, h_q, h_kv, head_dim, block, window;
+  float scale;
+};
+
+hipError_t launch_compress(int dt, const void* x, LStrides sx, const float* w, void* out, LStrides so,
+                           const void* x2, LStrides sx2, const float* w2, void* out2, LStrides so2,
+                           int batch, int seqlen, int h, int d, int block, hipStream_t st);
+
+// One workgroup per (query, head): any dtype, head_dim <= 512, keys per query <= kGenericMaxKeys.
+constexpr int kGenericMaxKeys = 16384;
+hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t st);
+
+// bf16, head_dim 512, MFMA prefill.
+hipError_t launch_attn_prefill512(const AttnArgs& a, hipStream_t st);
+
+// bf16, head_dim 512, one query per sequence, split over keys.
+size_t decode512_workspace_bytes(int batch, int h_q, int h_kv, int n_keys);
+hipError_t launch_attn_decode512(const AttnArgs& a, void* ws, hipStream_t st);
+
+// DSA
+size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk);
+hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
+                                 int seqlen, int h_i, int d_i, int topk, void* ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, LStrides sk, const void* v,
+                                     LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,
+                                     int seqlen, int h_q, int h_kv, int topk, float scale, hipStream_t st);
+
+}  // namespace hca

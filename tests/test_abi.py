@@ -1,0 +1,128 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects invalid arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_hca_amd as hca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hca.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hca.LIB_PATH), reason="libhca.so not built")
+
+S = hca.Strides
+Z = S(0, 0, 0)
+FAKE = ctypes.c_void_p(1 << 20)   # aligned non-null pointer; never dereferenced on these paths
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:hca|dsa)_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_and_exports_agree():
+    names = _declared()
+    assert set(names) == set(hca.EXPORTS)
+    lib = hca.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert hca.hca_abi_version() == 1
+
+
+def _lib():
+    return hca.load_library()
+
+
+def test_compress_rejects_bad_arguments():
+    lib = _lib()
+    st = lambda **kw: lib.hca_compress_kv(kw.get("dt", 1), kw.get("k", FAKE), kw.get("sk", S(0, 512, 512)),
+                                          kw.get("v", FAKE), S(0, 512, 512), kw.get("wk", FAKE), FAKE,
+                                          kw.get("kc", ctypes.c_void_p(1 << 30)), S(0, 512, 512),
+                                          ctypes.c_void_p(1 << 31), S(0, 512, 512), 1, kw.get("s", 256), 1,
+                                          kw.get("d", 512), kw.get("block", 128), None)
+    assert st(dt=7) == hca.HCA_ERR_INVALID
+    assert st(k=None) == hca.HCA_ERR_INVALID
+    assert st(wk=None) == hca.HCA_ERR_INVALID
+    assert st(block=0) == hca.HCA_ERR_INVALID
+    assert st(s=-1) == hca.HCA_ERR_INVALID
+    assert st(d=96) == hca.HCA_ERR_UNSUPPORTED
+    assert st(k=ctypes.c_void_p((1 << 20) + 2)) == hca.HCA_ERR_INVALID          # misaligned
+    assert st(sk=S(0, 500, 512)) == hca.HCA_ERR_INVALID                          # stride not 16-byte multiple
+    assert st(kc=FAKE) == hca.HCA_ERR_INVALID                                    # output aliases input
+    assert "overlap" in hca.hca_last_error()
+
+
+def _attn(lib, **kw):
+    q = kw.get("q", FAKE)
+    return lib.hca_attn_fwd(kw.get("dt", 1), q, S(0, 512 * 4, 512), FAKE, S(0, 512 * 4, 512), FAKE,
+                            S(0, 512 * 4, 512), kw.get("kc", FAKE), S(0, 512, 512), kw.get("kc", FAKE),
+                            S(0, 512, 512), kw.get("o", ctypes.c_void_p(1 << 34)), S(0, 512 * 4, 512),
+                            kw.get("lse", None), 1, kw.get("sq", 300), kw.get("qp", 0), kw.get("skv", 300),
+                            kw.get("kvp", 0), kw.get("nb", 2), kw.get("hq", 4), kw.get("hkv", 4),
+                            kw.get("d", 512), kw.get("block", 128), kw.get("window", 64), kw.get("scale", 0.05),
+                            kw.get("ws", None), kw.get("wsb", 0), None)
+
+
+def test_attn_rejects_bad_arguments():
+    lib = _lib()
+    assert _attn(lib, hq=6, hkv=4) == hca.HCA_ERR_INVALID
+    assert _attn(lib, window=0) == hca.HCA_ERR_INVALID
+    assert _attn(lib, block=0) == hca.HCA_ERR_INVALID
+    assert _attn(lib, q=None) == hca.HCA_ERR_INVALID
+    assert _attn(lib, scale=float("nan")) == hca.HCA_ERR_INVALID
+    assert _attn(lib, kvp=5) == hca.HCA_ERR_INVALID           # window of query 0 starts before the raw K/V
+    assert _attn(lib, skv=200) == hca.HCA_ERR_INVALID         # raw K/V end before the last query
+    assert _attn(lib, o=FAKE) == hca.HCA_ERR_INVALID          # output aliases q
+    assert _attn(lib, lse=ctypes.c_void_p((1 << 34) + 2)) == hca.HCA_ERR_INVALID
+    assert _attn(lib, dt=0, d=520) == hca.HCA_ERR_UNSUPPORTED
+    # decode needs a workspace of the size the query reports
+    need = lib.hca_attn_fwd_workspace_size(1, 1, 4, 4, 512, 2, 64)
+    assert need > 0
+    assert _attn(lib, sq=1, qp=299, kvp=236, skv=64, ws=None, wsb=0) == hca.HCA_ERR_WORKSPACE
+    assert _attn(lib, sq=1, qp=299, kvp=236, skv=64, ws=ctypes.c_void_p(1 << 36), wsb=need - 1) == hca.HCA_ERR_WORKSPACE
+    assert lib.hca_attn_fwd_workspace_size(1, 5, 4, 4, 512, 2, 64) == 0
+
+
+def test_attn_needs_enough_compressed_entries():
+    lib = _lib()
+    # last query t=299, window 64 -> lo = 236 -> n_c = 1; query 0 sees none
+    assert _attn(lib, nb=0, kc=None) == hca.HCA_ERR_INVALID
+    assert "compressed" in hca.hca_last_error()
+
+
+def test_dsa_rejects_bad_arguments():
+    lib = _lib()
+    ws = lib.dsa_index_topk_workspace_size(1, 1000, 64)
+    assert ws > 0
+    call = lambda **kw: lib.dsa_index_topk(kw.get("q", FAKE), FAKE, FAKE, kw.get("idx", ctypes.c_void_p(1 << 34)),
+                                           1, 1000, kw.get("hi", 4), kw.get("di", 64), kw.get("k", 64),
+                                           kw.get("ws", ctypes.c_void_p(1 << 36)), kw.get("wsb", ws), None)
+    assert call(q=None) == hca.HCA_ERR_INVALID
+    assert call(di=65) == hca.HCA_ERR_UNSUPPORTED
+    assert call(hi=9) == hca.HCA_ERR_UNSUPPORTED
+    assert call(k=0) == hca.HCA_ERR_INVALID
+    assert call(wsb=ws - 1) == hca.HCA_ERR_WORKSPACE
+    assert call(idx=FAKE) == hca.HCA_ERR_INVALID
+    sp = lambda **kw: lib.dsa_sparse_attn_fwd(kw.get("dt", 1), FAKE, S(0, 64 * 256, 256), FAKE, S(0, 256, 256),
+                                              FAKE, S(0, 256, 256), kw.get("idx", ctypes.c_void_p(1 << 33)),
+                                              ctypes.c_void_p(1 << 34), S(0, 64 * 256, 256), None, 1, 100,
+                                              kw.get("hq", 64), 1, kw.get("d", 256), 256, 16, 0.0625, None)
+    assert sp(idx=None) == hca.HCA_ERR_INVALID
+    assert sp(d=128) == hca.HCA_ERR_UNSUPPORTED
+    assert sp(hq=32) == hca.HCA_ERR_UNSUPPORTED
+    assert sp(dt=0) == hca.HCA_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 128, 1, 64, dtype=torch.bfloat16)
+    w = torch.zeros(1, 128)
+    with pytest.raises(ValueError):
+        hca.hca_compress_kv(x, x, w, w, 128)

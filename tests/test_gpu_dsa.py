@@ -1,0 +1,154 @@
+"""GPU parity of the DSA path (indexer + causal top-k, sparse attention) against
+the float64 oracle on the same seeded inputs, called through the C-ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from dsa_inputs import make_tie_free
+from helpers import BF16_TOL, LSE_TOL, dev_bf16, dev_f32, f64, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+hca = pytest.importorskip("sparse_attention_hca_amd")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _sorted_rows(idx):
+    """Per row: the valid entries sorted ascending, then the -1 padding."""
+    out = np.full_like(idx, -1)
+    for b in range(idx.shape[0]):
+        for t in range(idx.shape[1]):
+            v = np.sort(idx[b, t][idx[b, t] >= 0])
+            out[b, t, : v.shape[0]] = v
+    return out
+
+
+@pytest.mark.parametrize("S,topk,B", [(1500, 256, 1), (700, 64, 2), (300, 512, 1), (1000, 100, 1)])
+def test_index_topk_exact_sets(S, topk, B):
+    cfg = synth.small_dsa(seqlen=S, topk=topk, batch=B)
+    _say("index_topk", cfg)
+    inp = make_tie_free(cfg)
+    idx = hca.dsa_index_topk(dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"]), topk)
+    torch.cuda.synchronize()
+    got = _sorted_rows(idx.cpu().numpy())
+    ref = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], topk)
+    assert np.array_equal(got, ref)
+
+
+def test_index_topk_ties_break_by_position():
+    """Equal index keys make every score equal: the first k positions win."""
+    S, k = 600, 64
+    qI = np.ones((1, S, 4, 64), dtype=np.float32)
+    kI = np.full((1, S, 64), 0.5, dtype=np.float32)
+    w = np.ones((1, S, 4), dtype=np.float32)
+    idx = hca.dsa_index_topk(dev_f32(qI), dev_f32(kI), dev_f32(w), k)
+    got = _sorted_rows(idx.cpu().numpy())
+    for t in range(S):
+        n = min(t + 1, k)
+        assert got[0, t, :n].tolist() == list(range(n))
+        assert (got[0, t, n:] == -1).all()
+
+
+def test_index_topk_all_zero_scores_and_negative_weights():
+    """ReLU zeros everywhere (qI = -kI direction) plus negative weights: exact zeros order by position."""
+    rng = np.random.default_rng(5)
+    S, k = 500, 32
+    kI = np.abs(rng.standard_normal((1, S, 64))).astype(np.float32)
+    qI = -np.abs(rng.standard_normal((1, S, 4, 64))).astype(np.float32)
+    w = -np.abs(rng.standard_normal((1, S, 4))).astype(np.float32)
+    idx = hca.dsa_index_topk(dev_f32(qI), dev_f32(kI), dev_f32(w), k)
+    got = _sorted_rows(idx.cpu().numpy())
+    assert np.array_equal(got, oracle.index_topk(qI, kI, w, k))
+
+
+def _sparse_case(cfg, inp, idx_np):
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).to("cuda:0")
+    o, lse = hca.dsa_sparse_attn_fwd(q, k, v, idx, scale=cfg.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("S,topk", [(400, 128), (256, 300)])
+def test_sparse_attention_parity(S, topk):
+    cfg = synth.small_dsa(seqlen=S, topk=topk)
+    _say("sparse", cfg)
+    inp = make_tie_free(cfg)
+    idx = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], topk)
+    # scramble the order inside each row: any order is accepted
+    rng = np.random.default_rng(1)
+    idx = np.stack([np.stack([rng.permutation(r) for r in idx[b]]) for b in range(idx.shape[0])])
+    o, lse = _sparse_case(cfg, inp, idx)
+    ro, rlse = oracle.sparse_attention(f64(inp["q"], True), f64(inp["k"], True), f64(inp["v"], True), idx, cfg.scale)
+    err = rel_err(host(o), ro)
+    _say(f"  rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
+def test_sparse_attention_k_covers_context_is_dense():
+    cfg = synth.small_dsa(seqlen=200, topk=256)
+    inp = synth.make_dsa(cfg)
+    idx = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], 256)
+    o, lse = _sparse_case(cfg, inp, idx)
+    q, k, v = (torch.from_numpy(f64(inp[n], True)) for n in ("q", "k", "v"))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.permute(0, 2, 1, 3), k.expand(-1, -1, 64, -1).permute(0, 2, 1, 3),
+        v.expand(-1, -1, 64, -1).permute(0, 2, 1, 3), is_causal=True, scale=cfg.scale).permute(0, 2, 1, 3)
+    assert rel_err(host(o), ref.numpy()) < BF16_TOL
+
+
+def test_sparse_attention_bad_index_poisons_row():
+    cfg = synth.small_dsa(seqlen=64, topk=16)
+    inp = synth.make_dsa(cfg)
+    idx = np.tile(np.arange(16, dtype=np.int32), (1, 64, 1))
+    idx[0, 5, 3] = 64          # out of range
+    idx[0, 9, :] = -1          # empty row
+    o, lse = _sparse_case(cfg, inp, idx)
+    on = host(o)
+    assert np.isnan(on[0, 5]).all()
+    assert (on[0, 9] == 0).all() and np.isneginf(host(lse)[0, :, 9]).all()
+    others = [t for t in range(64) if t not in (5, 9)]
+    assert not np.isnan(on[0, others]).any()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_dsa_sampled():
+    cfg = synth.CONFIGS["c5"]
+    _say("full-size", cfg)
+    inp = synth.make_dsa(cfg)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    qI, kI, w = dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"])
+    idx = hca.dsa_index_topk(qI, kI, w, cfg.topk)
+    o, lse = hca.dsa_sparse_attn_fwd(q, k, v, idx, scale=cfg.scale)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 2046, 2047, 2048, 2049, 5000, 40000, cfg.seqlen - 1]) |
+                  set(rng.integers(0, cfg.seqlen, 12).tolist()))
+    n_exact = 0
+    for t in rows:
+        got = idx_np[0, t]
+        if oracle.tie_free_row(inp["qI"][0, t], inp["kI"][0], inp["w"][0, t], t, cfg.topk):
+            ref = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], cfg.topk, rows=[t])[0, 0]
+            v_ = np.sort(got[got >= 0])
+            assert np.array_equal(np.concatenate([v_, np.full(cfg.topk - v_.size, -1)]), ref), t
+            n_exact += 1
+        else:
+            assert oracle.valid_topk_row(got, inp["qI"][0, t], inp["kI"][0], inp["w"][0, t], t, cfg.topk), t
+    _say(f"  {n_exact}/{len(rows)} sampled rows tie-free and exact")
+    ro, rlse = oracle.sparse_attention(f64(inp["q"][:, rows], True)[:, :, :, :], f64(inp["k"], True),
+                                       f64(inp["v"], True), idx_np[:, rows], cfg.scale,
+                                       rows=list(range(len(rows))))
+    err = rel_err(host(o[:, rows]), ro)
+    _say(f"  sparse attention rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse[:, :, rows]) - rlse)) < LSE_TOL

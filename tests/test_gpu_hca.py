@@ -1,0 +1,267 @@
+"""GPU parity of the HCA path (compression, prefill attention, decode attention)
+against the float64 oracle on the same seeded inputs, called through the C-ABI."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import BF16_TOL, F32_TOL, LSE_TOL, dev_bf16, dev_f32, f64, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+hca = pytest.importorskip("sparse_attention_hca_amd")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(inp, name):
+    return dev_bf16(inp[name]) if inp["bf16"] else dev_f32(inp[name])
+
+
+def _run_prefill(cfg, inp, compress_on_gpu=True):
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
+    torch.cuda.synchronize()
+    return kc, vc, o, lse
+
+
+def _oracle_prefill(cfg, inp, rows=None, heads=None):
+    q, k, v = (f64(inp[n], inp["bf16"]) for n in ("q", "k", "v"))
+    if heads is not None:
+        q, k, v = q[:, :, heads], k[:, :, heads], v[:, :, heads]
+        w = inp["w"][heads]
+    else:
+        w = inp["w"]
+    kc, vc = oracle.compress_kv(k, w, cfg.block), oracle.compress_kv(v, w, cfg.block)
+    o, lse = oracle.hca_attention(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale, rows=rows)
+    return kc, vc, o, lse
+
+
+# ------------------------------------------------------------------ compression
+
+@pytest.mark.parametrize("dtype,d,block,S", [("bf16", 512, 128, 1000), ("f32", 128, 128, 2048),
+                                             ("bf16", 256, 64, 333), ("f32", 64, 7, 100), ("bf16", 512, 1, 40)])
+def test_compress_parity(dtype, d, block, S):
+    cfg = synth.small_prefill("c2" if dtype == "bf16" else "c1", dtype=dtype, seqlen=S, h_q=3, h_kv=3,
+                              head_dim=d, block=block, batch=2)
+    _say("compress", cfg)
+    inp = synth.make_prefill(cfg)
+    k, v = _to_dev(inp, "k"), _to_dev(inp, "v")
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, block)
+    torch.cuda.synchronize()
+    rk = oracle.compress_kv(f64(inp["k"], inp["bf16"]), inp["w"], block)
+    rv = oracle.compress_kv(f64(inp["v"], inp["bf16"]), inp["w"], block)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    assert kc.shape == rk.shape
+    assert rel_err(host(kc), rk) < tol and rel_err(host(vc), rv) < tol
+
+
+def test_compress_one_hot_is_bit_exact_and_strided_views_work():
+    cfg = synth.small_prefill("c2", seqlen=640, h_q=2, h_kv=2)
+    inp = synth.make_prefill(cfg)
+    big = torch.zeros(1, 640, 5, 512, dtype=torch.bfloat16, device="cuda:0")
+    big[:, :, 1:3] = dev_bf16(inp["k"])
+    k = big[:, :, 1:3]                                  # non-contiguous head stride
+    w = torch.zeros(2, 128, device="cuda:0")
+    w[0, 17] = 1.0
+    w[1, 127] = 1.0
+    kc, vc = hca.hca_compress_kv(k, k, w, w, 128)
+    torch.cuda.synchronize()
+    ref = torch.stack([dev_bf16(inp["k"])[0, 17::128, 0], dev_bf16(inp["k"])[0, 127::128, 1]], dim=1)[None]
+    assert torch.equal(kc, ref) and torch.equal(vc, ref)
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    # name, dtype, S, H, Hkv, d, block, W
+    ("c1-full", "f32", 2048, 2, 2, 128, 128, 128),
+    ("bf16-ragged", "bf16", 1000, 2, 2, 512, 128, 128),
+    ("bf16-w200-b64", "bf16", 777, 2, 2, 512, 64, 200),
+    ("bf16-gqa", "bf16", 600, 4, 2, 512, 128, 256),
+    ("bf16-window-covers", "bf16", 300, 2, 2, 512, 128, 400),
+    ("bf16-window1", "bf16", 400, 1, 1, 512, 32, 1),
+    ("bf16-block1", "bf16", 150, 1, 1, 512, 1, 5),
+    ("bf16-tiny", "bf16", 2, 1, 1, 512, 128, 128),
+    ("f32-d64", "f32", 500, 2, 1, 64, 16, 40),
+]
+
+
+@pytest.mark.parametrize("name,dtype,S,H,Hkv,d,block,W", PREFILL_CASES)
+def test_prefill_parity(name, dtype, S, H, Hkv, d, block, W):
+    base = "c1" if dtype == "f32" else "c2"
+    cfg = synth.small_prefill(base, name=name, dtype=dtype, seqlen=S, h_q=H, h_kv=Hkv, head_dim=d, block=block,
+                              window=W, std=1.0 if dtype == "f32" else 1.0 / math.sqrt(d))
+    _say("prefill", cfg)
+    inp = synth.make_prefill(cfg)
+    kc, vc, o, lse = _run_prefill(cfg, inp)
+    _, _, ro, rlse = _oracle_prefill(cfg, inp)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    err = rel_err(host(o), ro)
+    _say(f"  rel err {err:.3e}")
+    assert err < tol
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
+def test_prefill_unit_variance_logits():
+    """N(0,1) inputs at d=512 give logits of std ~1, a real softmax test."""
+    cfg = synth.small_prefill("c2", name="n01", seqlen=900, h_q=2, h_kv=2, std=1.0, window=128)
+    _say("prefill", cfg)
+    inp = synth.make_prefill(cfg)
+    # feed the oracle the GPU's bf16 cache so only the attention kernel is compared
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.hca_attention(f64(inp["q"], True), f64(inp["k"], True), f64(inp["v"], True), host(kc),
+                                    host(vc), window=cfg.window, block=cfg.block, scale=cfg.scale)
+    assert rel_err(host(o), ro) < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
+def test_prefill_deterministic_and_writes_every_output():
+    cfg = synth.small_prefill("c2", name="det", seqlen=700, h_q=2, h_kv=2, window=128)
+    inp = synth.make_prefill(cfg)
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o1 = torch.full_like(q, float("nan"))
+    l1 = torch.full((1, 2, 700), float("nan"), device="cuda:0")
+    hca.hca_attn_fwd(q, k, v, kc, vc, window=128, block=128, o=o1, lse=l1)
+    o2, l2 = hca.hca_attn_fwd(q, k, v, kc, vc, window=128, block=128)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o1).any() and not torch.isnan(l1).any()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_chunked_prefill_matches_full_prefill():
+    """Queries [400, 700) with raw K/V starting at the first needed window position."""
+    cfg = synth.small_prefill("c2", name="chunk", seqlen=700, h_q=2, h_kv=2, window=128)
+    inp = synth.make_prefill(cfg)
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o_full, l_full = hca.hca_attn_fwd(q, k, v, kc, vc, window=128, block=128)
+    lo = 400 - 127
+    o_part, l_part = hca.hca_attn_fwd(q[:, 400:], k[:, lo:], v[:, lo:], kc, vc, window=128, block=128,
+                                      q_pos0=400, kv_pos0=lo)
+    torch.cuda.synchronize()
+    assert rel_err(host(o_part), host(o_full[:, 400:])) < 1e-2
+    assert float((l_part - l_full[:, :, 400:]).abs().max()) < 1e-3
+
+
+# ------------------------------------------------------------------ decode
+
+DECODE_CASES = [
+    # B, Hq, Hkv, n_blocks, W, q_pos (None -> newest token of the window after n_blocks blocks)
+    (4, 16, 1, 300, 128, None),
+    (3, 8, 1, 50, 128, None),          # fewer than 16 heads per KV head
+    (2, 32, 2, 77, 64, None),          # two KV heads
+    (2, 16, 1, 0, 100, 37),            # early token: no compressed entry yet
+    (2, 16, 1, 5, 128, 700),           # window not aligned to a block end
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,nb,W,qpos", DECODE_CASES)
+def test_decode_parity(B, Hq, Hkv, nb, W, qpos):
+    cfg = synth.small_decode(batch=B, h_q=Hq, h_kv=Hkv, n_blocks=nb, window=W)
+    _say("decode", cfg, qpos)
+    inp = synth.make_decode(cfg)
+    t = cfg.q_pos if qpos is None else qpos
+    lo = max(0, t - W + 1)
+    n_c = lo // cfg.block
+    kw_len = t - lo + 1
+    q = dev_bf16(inp["q"])
+    kw, vw = dev_bf16(inp["kw"][:, :kw_len]), dev_bf16(inp["vw"][:, :kw_len])
+    kc = dev_bf16(inp["kc"]) if nb else None
+    vc = dev_bf16(inp["vc"]) if nb else None
+    assert n_c <= nb
+    o, lse = hca.hca_attn_fwd(q, kw, vw, kc, vc, window=W, block=cfg.block, scale=cfg.scale, q_pos0=t, kv_pos0=lo)
+    torch.cuda.synchronize()
+    z = np.zeros((B, 1, Hkv, 512))
+    ro, rlse = oracle.hca_attention(f64(inp["q"], True), f64(inp["kw"][:, :kw_len], True),
+                                    f64(inp["vw"][:, :kw_len], True),
+                                    f64(inp["kc"], True) if nb else z, f64(inp["vc"], True) if nb else z,
+                                    window=W, block=cfg.block, scale=cfg.scale, q_pos0=t, kv_pos0=lo)
+    err = rel_err(host(o), ro)
+    _say(f"  rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
+def test_decode_equals_prefill_row():
+    cfg = synth.small_prefill("c2", name="dec-vs-pre", seqlen=1100, h_q=4, h_kv=1, window=128, std=1.0)
+    inp = synth.make_prefill(cfg)
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=128, block=128)
+    for t in (0, 127, 128, 700, 1099):
+        lo = max(0, t - 127)
+        od, ld = hca.hca_attn_fwd(q[:, t:t + 1], k[:, lo:t + 1], v[:, lo:t + 1], kc, vc, window=128, block=128,
+                                  q_pos0=t, kv_pos0=lo)
+        torch.cuda.synchronize()
+        assert rel_err(host(od[:, 0]), host(o[:, t])) < 1e-2
+        assert float((ld[..., 0] - lse[..., t]).abs().max()) < 1e-3
+
+
+# ------------------------------------------------------------------ full-size configurations, sampled
+
+def _sample_rows(S, W, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, W - 1, W, W + 127, W + 128, S // 2, S - 129, S - 128, S - 1]
+    return sorted(set(fixed) | set(rng.integers(0, S, n).tolist()))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_full_size_prefill_sampled(name):
+    cfg = synth.CONFIGS[name]
+    _say("full-size", cfg)
+    inp = synth.make_prefill(cfg)
+    kc, vc, o, lse = _run_prefill(cfg, inp)
+    heads = [0, cfg.h_q // 2, cfg.h_q - 1]
+    rows = _sample_rows(cfg.seqlen, cfg.window)
+    # compression on the sampled heads, every block (convert only those heads)
+    q, k, v = (f64(inp[n][:, :, heads], True) for n in ("q", "k", "v"))
+    kch = oracle.compress_kv(k, inp["w"][heads], cfg.block)
+    vch = oracle.compress_kv(v, inp["w"][heads], cfg.block)
+    assert rel_err(host(kc[:, :, heads]), kch) < BF16_TOL
+    assert rel_err(host(vc[:, :, heads]), vch) < BF16_TOL
+    ro, rlse = oracle.hca_attention(q, k, v, kch, vch, window=cfg.window,
+                                    block=cfg.block, scale=cfg.scale, rows=rows)
+    got = host(o[:, rows][:, :, heads])
+    err = rel_err(got, ro)
+    _say(f"  rel err {err:.3e} on {len(rows)} rows x {len(heads)} heads")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse[:, heads][:, :, rows]) - rlse)) < LSE_TOL
+    assert not torch.isnan(o).any()
+
+
+@pytest.mark.timeout(600)
+def test_full_size_decode_sampled():
+    cfg = synth.CONFIGS["c4"]
+    _say("full-size", cfg)
+    inp = synth.make_decode(cfg)
+    q, kc, vc, kw, vw = (dev_bf16(inp[n]) for n in ("q", "kc", "vc", "kw", "vw"))
+    o, lse = hca.hca_attn_fwd(q, kw, vw, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale,
+                              q_pos0=cfg.q_pos, kv_pos0=cfg.kv_pos0)
+    torch.cuda.synchronize()
+    for b in (0, 31, 63):
+        ro, rlse = oracle.hca_attention(f64(inp["q"][b:b + 1], True), f64(inp["kw"][b:b + 1], True),
+                                        f64(inp["vw"][b:b + 1], True), f64(inp["kc"][b:b + 1], True),
+                                        f64(inp["vc"][b:b + 1], True), window=cfg.window, block=cfg.block,
+                                        scale=cfg.scale, q_pos0=cfg.q_pos, kv_pos0=cfg.kv_pos0)
+        assert rel_err(host(o[b:b + 1]), ro) < BF16_TOL
+        assert np.max(np.abs(host(lse[b:b + 1]) - rlse)) < LSE_TOL
