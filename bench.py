@@ -1,0 +1,337 @@
+"""Benchmark of the HCA / DSA forward path on one MI355X.
+
+The timed step is HCA prefill at 32768 tokens (bf16, 16 heads, head_dim 512,
+block 128, window 128): block compression of K and V followed by attention.
+`value` is tokens per second of that step.  The other workloads of the path
+are timed in the same run and reported under `components`:
+  * HCA prefill at 131072 tokens (window 256): compression, attention, both;
+  * HCA decode: 64 sequences x 1 query over 8192 compressed entries + 128 raw;
+  * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention.
+
+Inputs are seeded synthetic draws (the library's own generators) already
+resident in HBM when timing starts.  Kernel times come from HIP events on the
+stream the kernels are launched on.  `roofline` is for the dominant kernel of
+the step (prefill attention, HBM-bound at this size): algorithmic bytes per
+launch divided by its mean launch time.  `cpu_baseline` times the float64
+oracle on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill512_kernel": "sparse_attention_hca_amd/csrc/attn_prefill512.hip",
+    "decode512_kernel": "sparse_attention_hca_amd/csrc/attn_decode512.hip",
+    "compress_kernel": "sparse_attention_hca_amd/csrc/compress.hip",
+    "index_scores_kernel": "sparse_attention_hca_amd/csrc/dsa_index_topk.hip",
+    "sparse_attn256_kernel": "sparse_attention_hca_amd/csrc/dsa_attn256.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current source of this kernel; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def prefill_work(cfg):
+    """(FLOPs, algorithmic bytes) of HCA prefill attention: 4*d FLOPs per visible
+    (query head, key) pair; Q, O, K, V each moved once plus the compressed cache."""
+    import numpy as np
+    t = np.arange(cfg.seqlen, dtype=np.int64)
+    lo = np.maximum(0, t - cfg.window + 1)
+    keys = int((lo // cfg.block + (t - lo + 1)).sum())
+    flops = 4.0 * cfg.head_dim * keys * cfg.h_q * cfg.batch
+    e = 2
+    q = cfg.batch * cfg.seqlen * cfg.h_q * cfg.head_dim * e
+    kv = 2 * cfg.batch * cfg.seqlen * cfg.h_kv * cfg.head_dim * e
+    cache = 2 * cfg.batch * cfg.n_blocks * cfg.h_kv * cfg.head_dim * e
+    return flops, 2 * q + kv + cache
+
+
+def compress_bytes(cfg):
+    e = 2 if cfg.dtype == "bf16" else 4
+    nb = cfg.n_blocks
+    return 2 * cfg.batch * (nb * cfg.block + nb) * cfg.h_kv * cfg.head_dim * e + 2 * cfg.h_kv * cfg.block * 4
+
+
+def decode_work(cfg):
+    n_keys = cfg.n_blocks + cfg.window
+    e = 2
+    kv = 2 * cfg.batch * n_keys * cfg.h_kv * cfg.head_dim * e
+    qo = 2 * cfg.batch * cfg.h_q * cfg.head_dim * e
+    flops = 4.0 * cfg.head_dim * n_keys * cfg.h_q * cfg.batch
+    return flops, kv + qo
+
+
+def dsa_work(cfg):
+    S, k = cfg.seqlen, cfg.topk
+    pairs_idx = S * (S + 1) // 2
+    idx_flops = pairs_idx * (cfg.h_i * (2 * cfg.d_i + 2))
+    sel = sum(min(t + 1, k) for t in range(S))
+    attn_flops = 2.0 * (cfg.d_qk + cfg.d_v) * cfg.h_q * sel
+    return idx_flops, attn_flops, sel
+
+
+class Timer:
+    """Mean duration of repeated launches, from HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        out = fn()
+        b.record()
+        self.pairs.append((a, b))
+        return out
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def bench_prefill(torch, hca, synth, cfg, steps, warmup):
+    import numpy as np
+    t0 = time.time()
+    inp = synth.make_prefill(cfg)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp["q"], inp["k"], inp["v"]
+    w = torch.from_numpy(inp["w"]).to("cuda:0")
+    log(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s")
+    nb = cfg.n_blocks
+    kc = torch.empty((cfg.batch, nb, cfg.h_kv, cfg.head_dim), dtype=torch.bfloat16, device="cuda:0")
+    vc = torch.empty_like(kc)
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, cfg.h_q, cfg.seqlen), dtype=torch.float32, device="cuda:0")
+
+    def step(tc=None, ta=None):
+        f1 = lambda: hca.hca_compress_kv(k, v, w, w, cfg.block, kc=kc, vc=vc)
+        f2 = lambda: hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale,
+                                      o=o, lse=lse)
+        tc(f1) if tc else f1()
+        ta(f2) if ta else f2()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    tc, ta = Timer(torch), Timer(torch)
+    start = time.perf_counter()
+    for _ in range(steps):
+        step(tc, ta)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - start) * 1e3 / steps
+    res = {"compress_ms": tc.mean_ms(), "attn_ms": ta.mean_ms(), "step_ms": wall_ms}
+    del q, k, v, o, kc, vc, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(torch, hca, synth, cfg, steps, warmup):
+    import numpy as np
+    inp = synth.make_decode(cfg)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    q, kc, vc, kw, vw = (dev(inp[n]) for n in ("q", "kc", "vc", "kw", "vw"))
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, cfg.h_q, 1), dtype=torch.float32, device="cuda:0")
+    wsz = hca.hca_attn_fwd_workspace_size(cfg.batch, 1, cfg.h_q, cfg.h_kv, cfg.head_dim, cfg.n_blocks, cfg.window)
+    ws = torch.empty(wsz, dtype=torch.uint8, device="cuda:0")
+    f = lambda: hca.hca_attn_fwd(q, kw, vw, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale,
+                                 q_pos0=cfg.q_pos, kv_pos0=cfg.kv_pos0, o=o, lse=lse, workspace=ws)
+    for _ in range(warmup):
+        f()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    res = {"ms": tm.mean_ms()}
+    del q, kc, vc, kw, vw, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_dsa(torch, hca, synth, cfg, steps, warmup):
+    import numpy as np
+    t0 = time.time()
+    inp = synth.make_dsa(cfg)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    qI, kI, w = (torch.from_numpy(inp[n]).to("cuda:0") for n in ("qI", "kI", "w"))
+    del inp
+    log(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s")
+    idx = torch.empty((cfg.batch, cfg.seqlen, cfg.topk), dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(hca.dsa_index_topk_workspace_size(cfg.batch, cfg.seqlen, cfg.topk), dtype=torch.uint8,
+                     device="cuda:0")
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, cfg.h_q, cfg.seqlen), dtype=torch.float32, device="cuda:0")
+    fi = lambda: hca.dsa_index_topk(qI, kI, w, cfg.topk, idx=idx, workspace=ws)
+    fa = lambda: hca.dsa_sparse_attn_fwd(q, k, v, idx, scale=cfg.scale, o=o, lse=lse)
+    for _ in range(warmup):
+        fi()
+        fa()
+    ti, ta = Timer(torch), Timer(torch)
+    for _ in range(steps):
+        ti(fi)
+        ta(fa)
+    res = {"index_topk_ms": ti.mean_ms(), "attn_ms": ta.mean_ms()}
+    del q, k, v, qI, kI, w, idx, ws, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(synth, cfg, heads=4):
+    """The float64 oracle on a bounded sample of the headline workload: block
+    compression of K and V for `heads` heads and attention for every query row
+    of those heads; scaled to tokens/s of the whole step (all heads)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    inp = synth.make_prefill(cfg)
+    h = list(range(heads))
+    q = synth.bf16_bits_to_f32(inp["q"][:, :, h]).astype(np.float64)
+    k = synth.bf16_bits_to_f32(inp["k"][:, :, h]).astype(np.float64)
+    v = synth.bf16_bits_to_f32(inp["v"][:, :, h]).astype(np.float64)
+    del inp["q"], inp["k"], inp["v"]
+    t0 = time.perf_counter()
+    kc = oracle.compress_kv(k, inp["w"][h], cfg.block)
+    vc = oracle.compress_kv(v, inp["w"][h], cfg.block)
+    oracle.hca_attention(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
+    dt = time.perf_counter() - t0
+    est = dt * cfg.h_q / heads
+    return {"value": cfg.seqlen / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 oracle, {heads} of {cfg.h_q} heads of the {cfg.seqlen}-token prefill "
+                      f"(compression of all blocks + attention for every query row): {dt:.1f}s, "
+                      f"scaled by {cfg.h_q}/{heads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="c2,c3,c4,c5", help="comma list of workloads to run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the path needs no cross-GPU exchange; see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_hca_amd as hca
+    import synth
+    hca.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    only = set(args.only.split(","))
+    comps = {}
+
+    c2 = synth.CONFIGS["c2"]
+    r2 = bench_prefill(torch, hca, synth, c2, args.steps, args.warmup)
+    f2, b2 = prefill_work(c2)
+    comps["hca_prefill_32k"] = {
+        "compress_ms": r2["compress_ms"], "attn_ms": r2["attn_ms"],
+        "attn_tflops": f2 / r2["attn_ms"] / 1e9, "attn_mfma_frac": f2 / r2["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+        "attn_gbs": b2 / r2["attn_ms"] / 1e6, "attn_hbm_frac": b2 / r2["attn_ms"] / 1e6 / PEAK_HBM_GBS,
+        "compress_gbs": compress_bytes(c2) / r2["compress_ms"] / 1e6,
+    }
+    log(f"[bench] c2 done: {comps['hca_prefill_32k']}")
+
+    if "c3" in only:
+        c3 = synth.CONFIGS["c3"]
+        r3 = bench_prefill(torch, hca, synth, c3, max(3, args.steps // 4), 2)
+        f3, b3 = prefill_work(c3)
+        e2e = r3["compress_ms"] + r3["attn_ms"]
+        comps["hca_prefill_128k"] = {
+            "compress_ms": r3["compress_ms"], "attn_ms": r3["attn_ms"], "e2e_ms": e2e,
+            "tokens_per_s": c3.seqlen / e2e * 1e3,
+            "attn_tflops": f3 / r3["attn_ms"] / 1e9, "attn_mfma_frac": f3 / r3["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+            "attn_gbs": b3 / r3["attn_ms"] / 1e6,
+            "compress_gbs": compress_bytes(c3) / r3["compress_ms"] / 1e6,
+            "compress_hbm_frac": compress_bytes(c3) / r3["compress_ms"] / 1e6 / PEAK_HBM_GBS,
+        }
+        log(f"[bench] c3 done: {comps['hca_prefill_128k']}")
+    if "c4" in only:
+        c4 = synth.CONFIGS["c4"]
+        r4 = bench_decode(torch, hca, synth, c4, args.steps, args.warmup)
+        f4, b4 = decode_work(c4)
+        comps["hca_decode_1m"] = {
+            "ms": r4["ms"], "gbs": b4 / r4["ms"] / 1e6, "hbm_frac": b4 / r4["ms"] / 1e6 / PEAK_HBM_GBS,
+            "tokens_per_s": c4.batch / r4["ms"] * 1e3, "tflops": f4 / r4["ms"] / 1e9,
+        }
+        log(f"[bench] c4 done: {comps['hca_decode_1m']}")
+    if "c5" in only:
+        c5 = synth.CONFIGS["c5"]
+        r5 = bench_dsa(torch, hca, synth, c5, max(2, args.steps // 5), 1)
+        fi, fa, sel = dsa_work(c5)
+        tot = r5["index_topk_ms"] + r5["attn_ms"]
+        comps["dsa_prefill_64k"] = {
+            "index_topk_ms": r5["index_topk_ms"], "attn_ms": r5["attn_ms"], "e2e_ms": tot,
+            "tokens_per_s": c5.seqlen / tot * 1e3,
+            "index_tflops_f32": fi / r5["index_topk_ms"] / 1e9,
+            "attn_tflops": fa / r5["attn_ms"] / 1e9, "attn_mfma_frac": fa / r5["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+        }
+        log(f"[bench] c5 done: {comps['dsa_prefill_64k']}")
+
+    value = c2.seqlen / r2["step_ms"] * 1e3
+    achieved = b2 / r2["attn_ms"] / 1e6
+    line = {
+        "metric": "HCA prefill tokens/s + TFLOP/s (% MFMA peak); decode GB/s (% HBM peak)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r2["step_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "HCA prefill bf16: batch 1, seq 32768, 16 heads, head_dim 512, block 128, "
+                               "window 128; step = hca_compress_kv + hca_attn_fwd",
+                   "global_batch": 1, "seq_len": c2.seqlen, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "prefill512_kernel", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic("prefill512_kernel"),
+                     "algorithmic_bytes_per_launch": b2, "launch_ms": r2["attn_ms"]},
+        "components": comps,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        line["cpu_baseline"] = cpu_baseline(synth, c2)
+        log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
