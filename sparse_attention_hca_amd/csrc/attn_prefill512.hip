@@ -65,7 +65,10 @@ void prefill512_kernel(PrefillParams p) {
   const int b = bh / a.h_q;
   const int g = h / (a.h_q / a.h_kv);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: everything derived from it (row choice, tile
+  // classification) stays in SGPRs and scalar branches
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int W = a.window, blk = a.block;
 
@@ -86,13 +89,15 @@ void prefill512_kernel(PrefillParams p) {
   const int tq = qp0 + iq;
   const int lo_q = max(0, tq - W + 1);
   const int nc_q = lo_q / blk;
-  // this wave's query range (for skipping tiles nobody in the wave sees)
+  // this wave's query range: tiles nobody in the wave sees are skipped, tiles
+  // every query of the wave sees entirely need no mask
   const int iw0 = i0 + WQ * w;
   const int iw1 = min(iw0 + WQ - 1, i_last);
   const bool wave_has_q = iw0 <= i_last;
+  const bool wave_full = iw0 + WQ - 1 <= i_last;
   const int tw0 = qp0 + iw0, tw1 = qp0 + iw1;
-  const int nc_w1 = max(0, tw1 - W + 1) / blk;
-  const int lo_w0 = max(0, tw0 - W + 1);
+  const int lo_w0 = max(0, tw0 - W + 1), lo_w1 = max(0, tw1 - W + 1);
+  const int nc_w0 = lo_w0 / blk, nc_w1 = lo_w1 / blk;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query `col`, dims 32ks + 8grp .. +8
   bf16x8 qf[16];
@@ -106,34 +111,44 @@ void prefill512_kernel(PrefillParams p) {
     for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  const uint16_t* kcb = (const uint16_t*)a.kc + b * a.skc.b + (int64_t)g * a.skc.h;
-  const uint16_t* vcb = (const uint16_t*)a.vc + b * a.svc.b + (int64_t)g * a.svc.h;
-  const uint16_t* kb = (const uint16_t*)a.k + b * a.sk.b + (int64_t)g * a.sk.h;
-  const uint16_t* vb = (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h;
-
   // Tile loads: wave w < 4 loads K rows 4w..4w+3, wave w >= 4 loads V rows
-  // 4(w-4)..+3; lane = 16-byte chunk.  Rows past the valid range re-read a
-  // valid row: K logits there are masked, V rows are zeroed.
+  // 4(w-4)..+3; lane = 16-byte chunk of the row.  The row choice is
+  // wave-uniform, so the address is a scalar base plus the lane offset.  Rows
+  // past the valid range re-read a valid row: K logits there are masked, V
+  // rows are zeroed.
   const bool is_v = w >= 4;
   const int r0 = 4 * (w & 3);
+  const uint16_t* cbase = is_v ? (const uint16_t*)a.vc + b * a.svc.b + (int64_t)g * a.svc.h
+                               : (const uint16_t*)a.kc + b * a.skc.b + (int64_t)g * a.skc.h;
+  const int64_t cstride = is_v ? a.svc.s : a.skc.s;
+  const uint16_t* rbase = is_v ? (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h
+                               : (const uint16_t*)a.k + b * a.sk.b + (int64_t)g * a.sk.h;
+  const int64_t rstride = is_v ? a.sv.s : a.sk.s;
   auto load_tile = [&](int tt, u32x4 (&R)[4]) __attribute__((always_inline)) {
+    const uint16_t* base;
+    int64_t stride;
+    int row0, row_max;
+    if (tt < n_ct) {
+      base = cbase;
+      stride = cstride;
+      row0 = tt * BN + r0;
+      row_max = nc_max - 1;
+    } else {
+      base = rbase;
+      stride = rstride;
+      row0 = lo_first + (tt - n_ct) * BN + r0 - kvp0;
+      row_max = t_last - kvp0;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kk = r0 + i;
-      const uint16_t* src;
-      bool ok;
-      if (tt < n_ct) {
-        const int j = tt * BN + kk;
-        ok = j < nc_max;
-        src = (is_v ? vcb : kcb) + (int64_t)min(j, nc_max - 1) * (is_v ? a.svc.s : a.skc.s);
-      } else {
-        const int pos = lo_first + (tt - n_ct) * BN + kk;
-        ok = pos <= t_last;
-        src = (is_v ? vb : kb) + (int64_t)(min(pos, t_last) - kvp0) * (is_v ? a.sv.s : a.sk.s);
-      }
-      R[i] = ld16(src + 8 * lane) & ((ok || !is_v) ? ~0u : 0u);
+      const int row = row0 + i;
+      const uint32_t keep = (row <= row_max || !is_v) ? ~0u : 0u;
+      R[i] = ld16(base + (int64_t)min(row, row_max) * stride + 8 * lane) & keep;
     }
   };
+  // V^T store offsets of this lane: dim = 8*lane + e; the chunk swizzle depends on e only through e >> 2
+  const int vt_off0 = (8 * lane) * BN + (((w & 3) ^ vt_swz(8 * lane)) << 2);
+  const int vt_off1 = (8 * lane + 4) * BN + (((w & 3) ^ vt_swz(8 * lane + 4)) << 2);
   auto store_tile = [&](const u32x4 (&R)[4], int st) __attribute__((always_inline)) {
     if (!is_v) {
 #pragma unroll
@@ -143,14 +158,14 @@ void prefill512_kernel(PrefillParams p) {
       }
     } else {
       // 4 keys x 8 dims -> 8 dims x 4 keys
+      uint16_t* vbase = Vt + st * (D * BN);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         u32x2 x;
         x[0] = __builtin_amdgcn_perm(R[1][e >> 1], R[0][e >> 1], sel);
         x[1] = __builtin_amdgcn_perm(R[3][e >> 1], R[2][e >> 1], sel);
-        const int dim = 8 * lane + e;
-        *reinterpret_cast<u32x2*>(Vt + st * (D * BN) + dim * BN + (((w & 3) ^ vt_swz(dim)) << 2)) = x;
+        *reinterpret_cast<u32x2*>(vbase + ((e < 4) ? vt_off0 : vt_off1) + (e & 3) * BN) = x;
       }
     }
   };
@@ -160,64 +175,61 @@ void prefill512_kernel(PrefillParams p) {
   for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_used = -INFINITY, l_run = 0.f;
   const float c = p.c;
+  // per-lane LDS offsets of the S^T A-operand reads: chunk (4ks + grp) ^ (col & 7)
+  // of row col equals 4(ks ^ h) + (grp ^ (col & 3)) with h = (col >> 2) & 1
+  const int k_even = col * D + ((grp ^ (col & 3)) << 3) + 32 * ((col >> 2) & 1);
+  const int k_odd = col * D + ((grp ^ (col & 3)) << 3) - 32 * ((col >> 2) & 1);
+  const int v_rd = col * BN + ((grp ^ vt_swz(col)) << 2);
 
   auto compute = [&](int tt, int st) __attribute__((always_inline)) {
     const bool comp = tt < n_ct;
     const int j0 = tt * BN;
     const int p0 = lo_first + (tt - n_ct) * BN;
-    // does any query of this wave see a key of this tile?
+    // does any query of this wave see a key of this tile? (wave-uniform)
     const bool active = wave_has_q && (comp ? (j0 < nc_w1) : (p0 <= tw1 && p0 + BN - 1 >= lo_w0));
     if (!active) return;
+    const bool full = wave_full && (comp ? (j0 + BN - 1 < nc_w0) : (p0 >= lo_w1 && p0 + BN - 1 <= tw0));
     const uint16_t* kst = Ks + st * (BN * D);
     const uint16_t* vst = Vt + st * (D * BN);
-    // S^T = K Q^T : 16 keys x 16 queries.  Chunk (4ks + grp) ^ (col & 7) of
-    // row col equals 4(ks ^ h) + (grp ^ (col & 3)) with h = (col >> 2) & 1, so
-    // the address is one of two per-lane bases plus a compile-time 64*ks bytes.
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const int h1 = (col >> 2) & 1;
-      const uint16_t* kbase = kst + col * D + ((grp ^ (col & 3)) << 3);
-      const uint16_t* keven = kbase + 32 * h1;
-      const uint16_t* kodd = kbase - 32 * h1;
+    // S^T = K Q^T : 16 keys x 16 queries, two independent accumulation chains
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const uint16_t* kp = ((ks & 1) ? kodd : keven) + 32 * ks;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s, 0, 0, 0);
-      }
+    for (int ks = 0; ks < 16; ks += 2) {
+      const bf16x8 ka0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kst + k_even + 32 * ks));
+      const bf16x8 ka1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kst + k_odd + 32 * (ks + 1)));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks + 1], s1, 0, 0, 0);
     }
-    // mask + online softmax (log2 domain); lane holds keys 4grp + r of query `col`
+    // online softmax (log2 domain); lane holds keys 4grp + r of query `col`
     float sv[4];
-    float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = 4 * grp + r;
-      bool valid;
-      if (comp) valid = qvalid && (j0 + kk < nc_q);
-      else {
-        const int pos = p0 + kk;
-        valid = qvalid && pos >= lo_q && pos <= tq;
+    for (int r = 0; r < 4; ++r) sv[r] = (s0[r] + s1[r]) * c;
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = 4 * grp + r;
+        const bool valid = comp ? (qvalid && j0 + kk < nc_q) : (qvalid && p0 + kk >= lo_q && p0 + kk <= tq);
+        sv[r] = valid ? sv[r] : -INFINITY;
       }
-      sv[r] = valid ? s[r] * c : -INFINITY;
-      mt = fmaxf(mt, sv[r]);
     }
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const bool need = mt > m_used + kLazy;
     if (__any(need)) {
       const float new_m = need ? mt : m_used;
-      const float alpha = need ? exp2f(m_used - new_m) : 1.f;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - new_m) : 1.f;
       m_used = new_m;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
     }
+    // masked logits are -inf and m_used is finite once any key was seen: exp2 gives 0
+    const float msafe = m_used == -INFINITY ? 0.f : m_used;
     float ps[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ps[r] = sv[r] == -INFINITY ? 0.f : exp2f(sv[r] - m_used);
-      l_run += ps[r];
-    }
+    for (int r = 0; r < 4; ++r) ps[r] = __builtin_amdgcn_exp2f(sv[r] - msafe);
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     u32x2 pk;
     pk[0] = pack_bf16x2(ps[0], ps[1]);
     pk[1] = pack_bf16x2(ps[2], ps[3]);
@@ -225,9 +237,7 @@ void prefill512_kernel(PrefillParams p) {
     // O^T += V^T P^T : 32 dim tiles, one 16-key step each
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const int dim = 16 * dt + col;
-      const bf16x4 va =
-          __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(vst + dim * BN + ((grp ^ vt_swz(dim)) << 2)));
+      const bf16x4 va = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(vst + v_rd + 16 * BN * dt));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pf, o[dt], 0, 0, 0);
     }
   };
