@@ -10,17 +10,25 @@
 // two waves per SIMD):
 //   * Each wave owns 16 queries and keeps them in registers as the B operand
 //     of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 16 k-steps over d = 512).
-//   * Keys stream in tiles of 16: first the compressed entries, then the raw
-//     window band.  Each tile (16 K rows + 16 V rows of 1 KB) is loaded into
-//     registers one tile ahead with coalesced 16-byte loads (one row per wave
-//     instruction) and stored to one of two LDS stages: K row-major with its
-//     16-byte chunks XOR-swizzled by key, V transposed in registers (4 keys x
-//     8 dims per thread) into V^T so that V^T is the A operand of
-//     O^T = V^T P^T (v_mfma_f32_16x16x16_bf16).  One barrier per tile.
+//   * Keys stream in tiles of 32: first the compressed entries, then the raw
+//     window band.  K rows go global -> LDS with global_load_lds_dwordx4
+//     (one 1-KB row per wave instruction).  V rows are loaded into registers
+//     (4 keys x 8 dims per lane), transposed with byte permutes and stored as
+//     V^T, the A operand of O^T = V^T P^T (v_mfma_f32_16x16x32_bf16).  Both
+//     are double-buffered one tile ahead; one barrier per tile.
+//   * LDS layouts are chosen for the 64-bank LDS: a K row (1 KB) is stored
+//     shifted right by (key & 15) 16-byte chunks inside a 1280-B slot, so the
+//     16 lanes of a read phase hit 16 distinct bank groups, the DMA needs no
+//     per-lane permutation, and every S^T read is one lane offset plus an
+//     immediate; V^T rows (64 B) swizzle their chunks by a Gray code of the
+//     row, conflict-free for the 16-byte reads and 2-way for the 8-byte
+//     transposed writes.
 //   * Computing S^T rather than S puts one query per lane column, so the
 //     online-softmax state and all O^T accumulator rows of a lane belong to
-//     the same query: no cross-lane row shuffles, and the S^T accumulator
-//     layout is exactly the P^T operand layout of the PV product.
+//     the same query: no cross-lane row shuffles.  The S^T accumulators of
+//     the two 16-key halves are the P^T operand with the keys of each 32-key
+//     step in the order {4g..4g+3, 16+4g..16+4g+3} for lane group g, and V^T
+//     is stored in that order.
 //   * Online softmax in fp32 (log2 domain) with a lazy rescale: the reference
 //     maximum only moves when a tile exceeds it by more than 2^8, so O is
 //     rescaled rarely and exactly (the final normalisation uses the same
@@ -28,6 +36,11 @@
 //   * Workgroup ids are remapped so each XCD receives a contiguous range of
 //     (head, query tile) work: same-head tiles share that XCD's L2 for the
 //     compressed cache.  Within a head, the longest query tiles go first.
+//   * Each LDS stage is its own object and the loop handles two tiles per
+//     trip with fixed stages, so the compiler can tell the in-flight DMA of
+//     the next tile from the stage being read and keeps it in flight during
+//     the step.  The explicit vmcnt wait before the per-tile barrier orders
+//     DMA and reads.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -38,7 +51,8 @@ constexpr int D = 512;
 constexpr int BM = 128;  // queries per workgroup
 constexpr int WQ = 16;   // queries per wave
 constexpr int NWAVE = 8;
-constexpr int BN = 16;   // keys per tile
+constexpr int BN = 32;   // keys per tile
+constexpr int KROW = D + 128;  // K row slot in LDS (elements): 1 KB of data + 256 B for the shift
 constexpr float kLazy = 8.f;
 
 struct PrefillParams {
@@ -48,13 +62,17 @@ struct PrefillParams {
   float c;    // scale * log2(e)
 };
 
-// V^T row = 16 keys = 4 chunks of 8 B (chunk g = keys 4g..4g+3), chunk index XOR-swizzled.
-__device__ __forceinline__ int vt_swz(int dim) { return (dim >> 2) & 3; }
+// V^T row = 32 keys = 4 chunks of 16 B; chunk g holds keys {4g..4g+3, 16+4g..16+4g+3};
+// physical chunk = g ^ vt_swz(row).
+__device__ __forceinline__ int vt_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 3; }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill512_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * BN * D];  // 2 stages x [key][dim], chunk c at c ^ (key & 7)
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * D * BN];  // 2 stages x [dim][key], chunk swizzle
+  // one LDS object per stage: the compiler tracks DMA/read aliasing per object
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[BN * KROW];  // [key][shifted dims]
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[BN * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt0[D * BN];     // [dim][key']
+  __shared__ __attribute__((aligned(16))) uint16_t Vt1[D * BN];
 
   const AttnArgs& a = p.a;
   const int L = xcd_remap(blockIdx.x, p.total);
@@ -66,8 +84,7 @@ void prefill512_kernel(PrefillParams p) {
   const int g = h / (a.h_q / a.h_kv);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave index as a scalar: everything derived from it (row choice, tile
-  // classification) stays in SGPRs and scalar branches
+  // wave index as a scalar: everything derived from it stays in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int W = a.window, blk = a.block;
@@ -111,62 +128,67 @@ void prefill512_kernel(PrefillParams p) {
     for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  // Tile loads: wave w < 4 loads K rows 4w..4w+3, wave w >= 4 loads V rows
-  // 4(w-4)..+3; lane = 16-byte chunk of the row.  The row choice is
-  // wave-uniform, so the address is a scalar base plus the lane offset.  Rows
-  // past the valid range re-read a valid row: K logits there are masked, V
-  // rows are zeroed.
-  const bool is_v = w >= 4;
-  const int r0 = 4 * (w & 3);
-  const uint16_t* cbase = is_v ? (const uint16_t*)a.vc + b * a.svc.b + (int64_t)g * a.svc.h
-                               : (const uint16_t*)a.kc + b * a.skc.b + (int64_t)g * a.skc.h;
-  const int64_t cstride = is_v ? a.svc.s : a.skc.s;
-  const uint16_t* rbase = is_v ? (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h
-                               : (const uint16_t*)a.k + b * a.sk.b + (int64_t)g * a.sk.h;
-  const int64_t rstride = is_v ? a.sv.s : a.sk.s;
-  auto load_tile = [&](int tt, u32x4 (&R)[4]) __attribute__((always_inline)) {
+  const uint16_t* kcb = (const uint16_t*)a.kc + b * a.skc.b + (int64_t)g * a.skc.h;
+  const uint16_t* kb = (const uint16_t*)a.k + b * a.sk.b + (int64_t)g * a.sk.h;
+  const uint16_t* vcb = (const uint16_t*)a.vc + b * a.svc.b + (int64_t)g * a.svc.h;
+  const uint16_t* vb = (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h;
+
+  // ---- K tile: wave w moves rows w, w+8, w+16, w+24 with one DMA each (lane l
+  // = 16-byte chunk l) into the row slot shifted by (row & 15) chunks.  Rows past
+  // the valid range re-read a valid row (their logits are masked).
+  auto issue_k = [&](int tt, uint16_t* kdst, const uint16_t* kcp, const uint16_t* kp) __attribute__((always_inline)) {
     const uint16_t* base;
     int64_t stride;
     int row0, row_max;
     if (tt < n_ct) {
-      base = cbase;
-      stride = cstride;
-      row0 = tt * BN + r0;
-      row_max = nc_max - 1;
+      base = kcp; stride = a.skc.s; row0 = tt * BN; row_max = nc_max - 1;
     } else {
-      base = rbase;
-      stride = rstride;
-      row0 = lo_first + (tt - n_ct) * BN + r0 - kvp0;
-      row_max = t_last - kvp0;
+      base = kp; stride = a.sk.s; row0 = lo_first + (tt - n_ct) * BN - kvp0; row_max = t_last - kvp0;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = w + 8 * rr;
+      const uint16_t* src = base + (int64_t)min(row0 + r, row_max) * stride + 8 * lane;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(kdst + r * KROW + 8 * (r & 15)),
+                                       16, 0, 0);
+    }
+  };
+
+  // ---- V tile: wave w = 4*dh + vg, lane = 2*dgrp + hi holds keys 16hi + 4vg + i
+  // (i < 4) at dims 256dh + 8dgrp .. +8.  Rows past the valid range re-read the
+  // last valid row, a row some query of this workgroup attends to; their
+  // probabilities are exactly 0, so they add nothing.
+  const int vg = w & 3, dh = w >> 2;
+  const int hi = lane & 1, dgrp = lane >> 1;
+  const int vdim0 = 256 * dh + 8 * dgrp;
+  u32x4 vr[4];
+  auto load_v = [&](int tt) __attribute__((always_inline)) {
+    const uint16_t* base;
+    int64_t stride;
+    int row0, row_max;
+    if (tt < n_ct) {
+      base = vcb; stride = a.svc.s; row0 = tt * BN; row_max = nc_max - 1;
+    } else {
+      base = vb; stride = a.sv.s; row0 = lo_first + (tt - n_ct) * BN - kvp0; row_max = t_last - kvp0;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = row0 + i;
-      const uint32_t keep = (row <= row_max || !is_v) ? ~0u : 0u;
-      R[i] = ld16(base + (int64_t)min(row, row_max) * stride + 8 * lane) & keep;
+      const int row = row0 + 16 * hi + 4 * vg + i;
+      vr[i] = ld16(base + (int64_t)min(row, row_max) * stride + vdim0);
     }
   };
-  // V^T store offsets of this lane: dim = 8*lane + e; the chunk swizzle depends on e only through e >> 2
-  const int vt_off0 = (8 * lane) * BN + (((w & 3) ^ vt_swz(8 * lane)) << 2);
-  const int vt_off1 = (8 * lane + 4) * BN + (((w & 3) ^ vt_swz(8 * lane + 4)) << 2);
-  auto store_tile = [&](const u32x4 (&R)[4], int st) __attribute__((always_inline)) {
-    if (!is_v) {
+  // V^T write offsets (elements) for dims vdim0 + e: the swizzle depends on e only via e >> 2
+  const int vw0 = vdim0 * BN + ((vg ^ vt_swz(vdim0)) << 3) + 4 * hi;
+  const int vw1 = (vdim0 + 4) * BN + ((vg ^ vt_swz(vdim0 + 4)) << 3) + 4 * hi - 4 * BN;
+  auto store_v = [&](uint16_t* vdst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = r0 + i;
-        *reinterpret_cast<u32x4*>(Ks + st * (BN * D) + key * D + ((lane ^ (key & 7)) << 3)) = R[i];
-      }
-    } else {
-      // 4 keys x 8 dims -> 8 dims x 4 keys
-      uint16_t* vbase = Vt + st * (D * BN);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 x;
-        x[0] = __builtin_amdgcn_perm(R[1][e >> 1], R[0][e >> 1], sel);
-        x[1] = __builtin_amdgcn_perm(R[3][e >> 1], R[2][e >> 1], sel);
-        *reinterpret_cast<u32x2*>(vbase + ((e < 4) ? vt_off0 : vt_off1) + (e & 3) * BN) = x;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 x;
+      x[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
+      x[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
+      *reinterpret_cast<u32x2*>(vdst + ((e < 4) ? vw0 : vw1) + e * BN) = x;
     }
   };
 
@@ -175,13 +197,21 @@ void prefill512_kernel(PrefillParams p) {
   for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_used = -INFINITY, l_run = 0.f;
   const float c = p.c;
-  // per-lane LDS offsets of the S^T A-operand reads: chunk (4ks + grp) ^ (col & 7)
-  // of row col equals 4(ks ^ h) + (grp ^ (col & 3)) with h = (col >> 2) & 1
-  const int k_even = col * D + ((grp ^ (col & 3)) << 3) + 32 * ((col >> 2) & 1);
-  const int k_odd = col * D + ((grp ^ (col & 3)) << 3) - 32 * ((col >> 2) & 1);
-  const int v_rd = col * BN + ((grp ^ vt_swz(col)) << 2);
 
-  auto compute = [&](int tt, int st) __attribute__((always_inline)) {
+  // per-lane LDS read offsets (elements).  K: logical chunk 4ks + grp of key
+  // 16kt + col sits at slot chunk 4ks + grp + col.
+  const int k_off = col * KROW + 8 * (grp + col);
+  // V^T: row 16dt + col, chunk grp ^ vt_swz(row); the swizzle depends on dt only via dt & 1
+  const int v_rd0 = col * BN + ((grp ^ vt_swz(col)) << 3);
+  const int v_rd1 = (16 + col) * BN + ((grp ^ vt_swz(16 + col)) << 3) - 16 * BN;
+
+  const int last = max(ntiles - 1, 0);
+  auto compute = [&](int tt, const uint16_t* __restrict__ kst, const uint16_t* __restrict__ vst,
+                     uint16_t* __restrict__ knext, const uint16_t* __restrict__ kcp,
+                     const uint16_t* __restrict__ kp) __attribute__((always_inline)) {
+    // next tile's K DMA (stage pointers are per-object, see the file comment)
+    issue_k(min(tt + 1, last), knext, kcp, kp);
+    if (tt >= ntiles) return;  // the odd trip past the last tile only keeps the pipeline uniform
     const bool comp = tt < n_ct;
     const int j0 = tt * BN;
     const int p0 = lo_first + (tt - n_ct) * BN;
@@ -189,30 +219,33 @@ void prefill512_kernel(PrefillParams p) {
     const bool active = wave_has_q && (comp ? (j0 < nc_w1) : (p0 <= tw1 && p0 + BN - 1 >= lo_w0));
     if (!active) return;
     const bool full = wave_full && (comp ? (j0 + BN - 1 < nc_w0) : (p0 >= lo_w1 && p0 + BN - 1 <= tw0));
-    const uint16_t* kst = Ks + st * (BN * D);
-    const uint16_t* vst = Vt + st * (D * BN);
-    // S^T = K Q^T : 16 keys x 16 queries, two independent accumulation chains
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    // S^T = K Q^T : two 16-key halves x 16 queries (two independent chains)
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < 16; ks += 2) {
-      const bf16x8 ka0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kst + k_even + 32 * ks));
-      const bf16x8 ka1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kst + k_odd + 32 * (ks + 1)));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qf[ks + 1], s1, 0, 0, 0);
-    }
-    // online softmax (log2 domain); lane holds keys 4grp + r of query `col`
-    float sv[4];
+    for (int ks = 0; ks < 16; ++ks) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (s0[r] + s1[r]) * c;
-    if (!full) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = 4 * grp + r;
-        const bool valid = comp ? (qvalid && j0 + kk < nc_q) : (qvalid && p0 + kk >= lo_q && p0 + kk <= tq);
-        sv[r] = valid ? sv[r] : -INFINITY;
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 ka = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(kst + k_off + 16 * KROW * kt + 32 * ks));
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[kt], 0, 0, 0);
       }
     }
-    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    // online softmax (log2 domain); lane holds keys 16kt + 4grp + r of query `col`
+    float sv[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[4 * kt + r] = s[kt][r] * c;
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 16 * (e >> 2) + 4 * grp + (e & 3);
+        const bool valid = comp ? (qvalid && j0 + kk < nc_q) : (qvalid && p0 + kk >= lo_q && p0 + kk <= tq);
+        sv[e] = valid ? sv[e] : -INFINITY;
+      }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const bool need = mt > m_used + kLazy;
@@ -226,33 +259,43 @@ void prefill512_kernel(PrefillParams p) {
     }
     // masked logits are -inf and m_used is finite once any key was seen: exp2 gives 0
     const float msafe = m_used == -INFINITY ? 0.f : m_used;
-    float ps[4];
+    float ps[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ps[r] = __builtin_amdgcn_exp2f(sv[r] - msafe);
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    u32x2 pk;
-    pk[0] = pack_bf16x2(ps[0], ps[1]);
-    pk[1] = pack_bf16x2(ps[2], ps[3]);
-    const bf16x4 pf = __builtin_bit_cast(bf16x4, pk);
-    // O^T += V^T P^T : 32 dim tiles, one 16-key step each
+    for (int e = 0; e < 8; ++e) ps[e] = __builtin_amdgcn_exp2f(sv[e] - msafe);
+    l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(ps[2 * e], ps[2 * e + 1]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+    // O^T += V^T P^T : 32 dim tiles, one 32-key step each
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const bf16x4 va = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(vst + v_rd + 16 * BN * dt));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pf, o[dt], 0, 0, 0);
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(vst + ((dt & 1) ? v_rd1 : v_rd0) + 16 * BN * dt));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
     }
   };
 
-  // One tile in flight in registers, two LDS stages, one barrier per tile.
+  // Pipeline: tile tt's K DMA and V loads are issued one iteration ahead.
   // Loads are unconditional (past the end they re-read the last tile) so the
-  // compiler's load counting stays exact.
-  u32x4 R[4];
-  const int last = max(ntiles - 1, 0);
-  if (ntiles > 0) load_tile(0, R);
-  for (int tt = 0; tt < ntiles; ++tt) {
-    store_tile(R, tt & 1);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    load_tile(min(tt + 1, last), R);
-    compute(tt, tt & 1);
+  // load counting stays exact.
+  // Two tiles per trip with fixed stages (even tiles in stage 0, odd in stage 1).
+  // The trip for tile tt stores its V^T, waits for its K DMA and V loads, then
+  // issues the next tile's loads and computes.  Loads are unconditional (past
+  // the end they re-read the last tile) so the load counting stays exact.
+  if (ntiles > 0) {
+    issue_k(0, Ks0, kcb, kb);
+    load_v(0);
+    for (int tt = 0; tt < ntiles; tt += 2) {
+      store_v(Vt0);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_v(min(tt + 1, last));
+      compute(tt, Ks0, Vt0, Ks1, kcb, kb);
+      store_v(Vt1);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_v(min(tt + 2, last));
+      compute(tt + 1, Ks1, Vt1, Ks0, kcb, kb);
+    }
   }
 
   // ---- epilogue: normalise, store bf16 O and the LSE
