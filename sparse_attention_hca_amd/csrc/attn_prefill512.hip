@@ -16,13 +16,14 @@
 //     (4 keys x 8 dims per lane), transposed with byte permutes and stored as
 //     V^T, the A operand of O^T = V^T P^T (v_mfma_f32_16x16x32_bf16).  Both
 //     are double-buffered one tile ahead; one barrier per tile.
-//   * LDS layouts are chosen for the 64-bank LDS: a K row (1 KB) is stored
-//     shifted right by (key & 15) 16-byte chunks inside a 1280-B slot, so the
-//     16 lanes of a read phase hit 16 distinct bank groups, the DMA needs no
-//     per-lane permutation, and every S^T read is one lane offset plus an
-//     immediate; V^T rows (64 B) swizzle their chunks by a Gray code of the
-//     row, conflict-free for the 16-byte reads and 2-way for the 8-byte
-//     transposed writes.
+//   * LDS layouts are chunk-major so that the 16 lanes of every 16-byte read
+//     phase touch one contiguous 256-byte span (the measured full-rate case
+//     on gfx950; spans shifted between lane groups run at half rate): K is
+//     [chunk][key][16 B] and V^T is [chunk][dim + dim/16][16 B] (the padding
+//     row every 16 dims also makes the 8-byte transposed writes
+//     conflict-free).  Every MFMA operand read is one lane offset plus a
+//     compile-time immediate.  A K DMA instruction fills one chunk pair for
+//     all 32 keys of the tile.
 //   * Computing S^T rather than S puts one query per lane column, so the
 //     online-softmax state and all O^T accumulator rows of a lane belong to
 //     the same query: no cross-lane row shuffles.  The S^T accumulators of
@@ -52,7 +53,9 @@ constexpr int BM = 128;  // queries per workgroup
 constexpr int WQ = 16;   // queries per wave
 constexpr int NWAVE = 8;
 constexpr int BN = 32;   // keys per tile
-constexpr int KROW = D + 128;  // K row slot in LDS (elements): 1 KB of data + 256 B for the shift
+constexpr int KSTAGE = (D / 8) * BN * 8;      // K stage: 64 chunks x 32 keys x 8 elements
+constexpr int VCH = (D + D / 16) * 8;         // V^T chunk plane: padded dims x 8 elements
+constexpr int VSTAGE = 4 * VCH;               // V^T stage: 4 chunks (32 keys)
 constexpr float kLazy = 8.f;
 
 struct PrefillParams {
@@ -62,17 +65,16 @@ struct PrefillParams {
   float c;    // scale * log2(e)
 };
 
-// V^T row = 32 keys = 4 chunks of 16 B; chunk g holds keys {4g..4g+3, 16+4g..16+4g+3};
-// physical chunk = g ^ vt_swz(row).
-__device__ __forceinline__ int vt_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 3; }
+// V^T: chunk g of dim d holds keys {4g..4g+3, 16+4g..16+4g+3} of the tile and
+// sits at element g*VCH + (d + d/16)*8.
 
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill512_kernel(PrefillParams p) {
   // one LDS object per stage: the compiler tracks DMA/read aliasing per object
-  __shared__ __attribute__((aligned(16))) uint16_t Ks0[BN * KROW];  // [key][shifted dims]
-  __shared__ __attribute__((aligned(16))) uint16_t Ks1[BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt0[D * BN];     // [dim][key']
-  __shared__ __attribute__((aligned(16))) uint16_t Vt1[D * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[KSTAGE];  // [chunk][key][8]
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[KSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt0[VSTAGE];  // [chunk][padded dim][8]
+  __shared__ __attribute__((aligned(16))) uint16_t Vt1[VSTAGE];
 
   const AttnArgs& a = p.a;
   const int L = xcd_remap(blockIdx.x, p.total);
@@ -133,9 +135,11 @@ void prefill512_kernel(PrefillParams p) {
   const uint16_t* vcb = (const uint16_t*)a.vc + b * a.svc.b + (int64_t)g * a.svc.h;
   const uint16_t* vb = (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h;
 
-  // ---- K tile: wave w moves rows w, w+8, w+16, w+24 with one DMA each (lane l
-  // = 16-byte chunk l) into the row slot shifted by (row & 15) chunks.  Rows past
-  // the valid range re-read a valid row (their logits are masked).
+  // ---- K tile: one DMA instruction fills chunk pair cp (chunks 2cp, 2cp+1) of all
+  // 32 keys: lane l fetches chunk 2cp + (l >> 5) of key l & 31.  Wave w owns chunk
+  // pairs w, w+8, w+16, w+24.  Keys past the valid range re-read a valid row
+  // (their logits are masked).
+  const int kkey = lane & 31, khalf = lane >> 5;
   auto issue_k = [&](int tt, uint16_t* kdst, const uint16_t* kcp, const uint16_t* kp) __attribute__((always_inline)) {
     const uint16_t* base;
     int64_t stride;
@@ -145,13 +149,12 @@ void prefill512_kernel(PrefillParams p) {
     } else {
       base = kp; stride = a.sk.s; row0 = lo_first + (tt - n_ct) * BN - kvp0; row_max = t_last - kvp0;
     }
+    const uint16_t* rowp = base + (int64_t)min(row0 + kkey, row_max) * stride + 8 * khalf;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = w + 8 * rr;
-      const uint16_t* src = base + (int64_t)min(row0 + r, row_max) * stride + 8 * lane;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(kdst + r * KROW + 8 * (r & 15)),
-                                       16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int cp = w + 8 * i;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(rowp + 16 * cp),
+                                       (__attribute__((address_space(3))) void*)(kdst + cp * (2 * BN * 8)), 16, 0, 0);
     }
   };
 
@@ -178,9 +181,9 @@ void prefill512_kernel(PrefillParams p) {
       vr[i] = ld16(base + (int64_t)min(row, row_max) * stride + vdim0);
     }
   };
-  // V^T write offsets (elements) for dims vdim0 + e: the swizzle depends on e only via e >> 2
-  const int vw0 = vdim0 * BN + ((vg ^ vt_swz(vdim0)) << 3) + 4 * hi;
-  const int vw1 = (vdim0 + 4) * BN + ((vg ^ vt_swz(vdim0 + 4)) << 3) + 4 * hi - 4 * BN;
+  // V^T write offset (elements) of dim vdim0: chunk vg, half hi (vdim0 % 16 + e < 16,
+  // so the padding term is the same for all eight dims of the lane)
+  const int vw = vg * VCH + (vdim0 + vdim0 / 16) * 8 + 4 * hi;
   auto store_v = [&](uint16_t* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -188,7 +191,7 @@ void prefill512_kernel(PrefillParams p) {
       u32x2 x;
       x[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
       x[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
-      *reinterpret_cast<u32x2*>(vdst + ((e < 4) ? vw0 : vw1) + e * BN) = x;
+      *reinterpret_cast<u32x2*>(vdst + vw + 8 * e) = x;
     }
   };
 
@@ -198,12 +201,10 @@ void prefill512_kernel(PrefillParams p) {
   float m_used = -INFINITY, l_run = 0.f;
   const float c = p.c;
 
-  // per-lane LDS read offsets (elements).  K: logical chunk 4ks + grp of key
-  // 16kt + col sits at slot chunk 4ks + grp + col.
-  const int k_off = col * KROW + 8 * (grp + col);
-  // V^T: row 16dt + col, chunk grp ^ vt_swz(row); the swizzle depends on dt only via dt & 1
-  const int v_rd0 = col * BN + ((grp ^ vt_swz(col)) << 3);
-  const int v_rd1 = (16 + col) * BN + ((grp ^ vt_swz(16 + col)) << 3) - 16 * BN;
+  // per-lane LDS read offsets (elements).  K: chunk 4ks + grp of key 16kt + col.
+  // V^T: chunk grp of dim 16dt + col (padded index 17dt + col).
+  const int k_off = grp * (BN * 8) + col * 8;
+  const int v_off = grp * VCH + col * 8;
 
   const int last = max(ntiles - 1, 0);
   auto compute = [&](int tt, const uint16_t* __restrict__ kst, const uint16_t* __restrict__ vst,
@@ -226,7 +227,7 @@ void prefill512_kernel(PrefillParams p) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(kst + k_off + 16 * KROW * kt + 32 * ks));
+            bf16x8, *reinterpret_cast<const u32x4*>(kst + k_off + 4 * BN * 8 * ks + 16 * 8 * kt));
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[kt], 0, 0, 0);
       }
     }
@@ -270,8 +271,7 @@ void prefill512_kernel(PrefillParams p) {
     // O^T += V^T P^T : 32 dim tiles, one 32-key step each
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const bf16x8 va = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(vst + ((dt & 1) ? v_rd1 : v_rd0) + 16 * BN * dt));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vst + v_off + 17 * 8 * dt));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
     }
   };
