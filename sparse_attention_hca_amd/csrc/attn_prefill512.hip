@@ -6,30 +6,28 @@
 // and the raw window [lo(t), t], lo(t) = max(0, t - W + 1), with 512-wide
 // heads.
 //
-// Design (one workgroup = 8 waves = 128 consecutive queries of one head,
-// two waves per SIMD):
-//   * Each wave owns 16 queries and keeps them in registers as the B operand
-//     of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 16 k-steps over d = 512).
-//   * Keys stream in tiles of 32: first the compressed entries, then the raw
-//     window band.  K rows go global -> LDS with global_load_lds_dwordx4
-//     (one 1-KB row per wave instruction).  V rows are loaded into registers
-//     (4 keys x 8 dims per lane), transposed with byte permutes and stored as
-//     V^T, the A operand of O^T = V^T P^T (v_mfma_f32_16x16x32_bf16).  Both
-//     are double-buffered one tile ahead; one barrier per tile.
-//   * LDS layouts are chunk-major so that the 16 lanes of every 16-byte read
-//     phase touch one contiguous 256-byte span (the measured full-rate case
-//     on gfx950; spans shifted between lane groups run at half rate): K is
-//     [chunk][key][16 B] and V^T is [chunk][dim + dim/16][16 B] (the padding
-//     row every 16 dims also makes the 8-byte transposed writes
-//     conflict-free).  Every MFMA operand read is one lane offset plus a
-//     compile-time immediate.  A K DMA instruction fills one chunk pair for
-//     all 32 keys of the tile.
-//   * Computing S^T rather than S puts one query per lane column, so the
-//     online-softmax state and all O^T accumulator rows of a lane belong to
-//     the same query: no cross-lane row shuffles.  The S^T accumulators of
-//     the two 16-key halves are the P^T operand with the keys of each 32-key
-//     step in the order {4g..4g+3, 16+4g..16+4g+3} for lane group g, and V^T
-//     is stored in that order.
+// Design (one workgroup = 4 waves = 128 consecutive queries of one head; one
+// wave per SIMD with the whole 512-entry register file):
+//   * Each wave owns 32 queries.  Q^T stays in registers as the B operand of
+//     S^T = K Q^T (v_mfma_f32_32x32x16_bf16, 32 k-steps over d = 512) and the
+//     O^T accumulators (512 dims x 32 queries, fp32) take 256 registers.
+//     32 queries per wave halve the LDS bytes read per MFMA flop compared
+//     with 16, which keeps the operand reads well under LDS bandwidth.
+//   * Keys stream in tiles of 32 (compressed entries first, then the raw
+//     window band).  Both K and V rows go global -> LDS with 16-byte LDS DMA,
+//     one 1-KB row per wave instruction, double-buffered one tile ahead; one
+//     barrier per tile.
+//   * K rows are stored with a 16-byte pad (row stride 1040 B): the 16-byte
+//     A-operand reads of 16 consecutive keys then hit 16 distinct bank
+//     groups.  V rows are padded by 64 B (stride 1088 B) and read with the
+//     gfx950 transposing LDS load (ds_read_b64_tr_b16), which hands each lane
+//     four consecutive keys of one dim: exactly the V^T A operand of
+//     O^T = V^T P^T, with no register transpose.  With that stride the four
+//     rows x four 16-byte chunks read by 32 lanes fall in 16 distinct bank
+//     groups.
+//   * The S^T accumulator of a lane (one query, 16 keys) is the P^T operand
+//     once converted to bf16; the V^T reads fetch the keys in the matching
+//     order, so no data moves between lanes.
 //   * Online softmax in fp32 (log2 domain) with a lazy rescale: the reference
 //     maximum only moves when a tile exceeds it by more than 2^8, so O is
 //     rescaled rarely and exactly (the final normalisation uses the same
@@ -37,11 +35,6 @@
 //   * Workgroup ids are remapped so each XCD receives a contiguous range of
 //     (head, query tile) work: same-head tiles share that XCD's L2 for the
 //     compressed cache.  Within a head, the longest query tiles go first.
-//   * Each LDS stage is its own object and the loop handles two tiles per
-//     trip with fixed stages, so the compiler can tell the in-flight DMA of
-//     the next tile from the stage being read and keeps it in flight during
-//     the step.  The explicit vmcnt wait before the per-tile barrier orders
-//     DMA and reads.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -49,14 +42,18 @@ namespace hca {
 namespace {
 
 constexpr int D = 512;
-constexpr int BM = 128;  // queries per workgroup
-constexpr int WQ = 16;   // queries per wave
-constexpr int NWAVE = 8;
-constexpr int BN = 32;   // keys per tile
-constexpr int KSTAGE = (D / 8) * BN * 8;      // K stage: 64 chunks x 32 keys x 8 elements
-constexpr int VCH = (D + D / 16) * 8;         // V^T chunk plane: padded dims x 8 elements
-constexpr int VSTAGE = 4 * VCH;               // V^T stage: 4 chunks (32 keys)
-constexpr float kLazy = 8.f;
+constexpr int BM = 128;             // queries per workgroup
+constexpr int WQ = 32;              // queries per wave
+constexpr int NWAVE = 4;
+constexpr int BN = 32;              // keys per tile
+constexpr int KROW = 2 * D + 16;    // LDS bytes per K row
+constexpr int VROW = 2 * D + 64;    // LDS bytes per V row
+constexpr int KST = BN * KROW;      // K stage bytes
+constexpr int VST = BN * VROW;      // V stage bytes
+constexpr int STAGE = KST + VST;
+constexpr float kGuard = 64.f;  // log2 headroom of the fixed softmax reference
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 struct PrefillParams {
   AttnArgs a;
@@ -65,16 +62,47 @@ struct PrefillParams {
   float c;    // scale * log2(e)
 };
 
-// V^T: chunk g of dim d holds keys {4g..4g+3, 16+4g..16+4g+3} of the tile and
-// sits at element g*VCH + (d + d/16)*8.
+// 16-byte LDS DMA of one wave: lane l copies 16 bytes from g (per lane) to LDS
+// byte address lds + 16 l (lds travels in M0).  Written as asm so that the
+// compiler does not track it as an LDS store (it would wait for it before
+// unrelated LDS reads); the explicit vmcnt wait and barrier of each tile order
+// DMA and reads.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
 
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+// The two products are written as inline asm so that S^T accumulates in VGPRs
+// (the softmax reads it) while O^T accumulates in AGPRs: O^T takes all 256
+// AGPRs, and the compiler would otherwise put every MFMA accumulator in AGPRs
+// and spill.  The compiler does not see these as MFMAs, so the wait states
+// the ISA requires around them are explicit: after the last S^T step (its
+// result is read by VALU), before the first O^T step of a tile (P^T was just
+// written by VALU), before an MFMA that reads a VALU-written operand and
+// before O^T is read back.  Back-to-back MFMAs on the same accumulator need
+// none.
+__device__ __forceinline__ void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 15" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void zero_o(f32x16& acc, const bf16x8& z) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=&a"(acc) : "v"(z));
+}
+__device__ __forceinline__ void mfma_o_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void prefill512_kernel(PrefillParams p) {
-  // one LDS object per stage: the compiler tracks DMA/read aliasing per object
-  __shared__ __attribute__((aligned(16))) uint16_t Ks0[KSTAGE];  // [chunk][key][8]
-  __shared__ __attribute__((aligned(16))) uint16_t Ks1[KSTAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt0[VSTAGE];  // [chunk][padded dim][8]
-  __shared__ __attribute__((aligned(16))) uint16_t Vt1[VSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  __shared__ int redo_flag;
 
   const AttnArgs& a = p.a;
   const int L = xcd_remap(blockIdx.x, p.total);
@@ -88,7 +116,7 @@ void prefill512_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar: everything derived from it stays in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
+  const int col = lane & 31, hf = lane >> 5;
   const int W = a.window, blk = a.block;
 
   // Positions fit in 32 bits (checked by the host before launch).
@@ -118,101 +146,66 @@ void prefill512_kernel(PrefillParams p) {
   const int lo_w0 = max(0, tw0 - W + 1), lo_w1 = max(0, tw1 - W + 1);
   const int nc_w0 = lo_w0 / blk, nc_w1 = lo_w1 / blk;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query `col`, dims 32ks + 8grp .. +8
-  bf16x8 qf[16];
+  // ---- Q^T fragments (B operand): lane holds query `col`, dims 16ks + 8hf .. +8
+  bf16x8 qf[32];
   {
     const uint16_t* qp = (const uint16_t*)a.q + b * a.sq.b + (int64_t)min(iq, a.seqlen_q - 1) * a.sq.s +
-                         (int64_t)h * a.sq.h + 8 * grp;
+                         (int64_t)h * a.sq.h + 8 * hf;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
-    // settle the Q loads here so the tile pipeline's load counting starts clean
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * ks));
+    // settle the Q loads before the DMA pipeline (its waits are explicit)
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < 32; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   const uint16_t* kcb = (const uint16_t*)a.kc + b * a.skc.b + (int64_t)g * a.skc.h;
   const uint16_t* kb = (const uint16_t*)a.k + b * a.sk.b + (int64_t)g * a.sk.h;
   const uint16_t* vcb = (const uint16_t*)a.vc + b * a.svc.b + (int64_t)g * a.svc.h;
   const uint16_t* vb = (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
 
-  // ---- K tile: one DMA instruction fills chunk pair cp (chunks 2cp, 2cp+1) of all
-  // 32 keys: lane l fetches chunk 2cp + (l >> 5) of key l & 31.  Wave w owns chunk
-  // pairs w, w+8, w+16, w+24.  Keys past the valid range re-read a valid row
-  // (their logits are masked).
-  const int kkey = lane & 31, khalf = lane >> 5;
-  auto issue_k = [&](int tt, uint16_t* kdst, const uint16_t* kcp, const uint16_t* kp) __attribute__((always_inline)) {
-    const uint16_t* base;
-    int64_t stride;
+  // ---- DMA of tile tt into stage st: wave w copies K rows and V rows 8w .. 8w+7.
+  // Rows past the valid range re-read the last valid row: their logits are
+  // masked and their probabilities are exactly 0.
+  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
+    const uint16_t *kbase, *vbase;
+    int64_t ks_, vs_;
     int row0, row_max;
     if (tt < n_ct) {
-      base = kcp; stride = a.skc.s; row0 = tt * BN; row_max = nc_max - 1;
+      kbase = kcb; vbase = vcb; ks_ = a.skc.s; vs_ = a.svc.s; row0 = tt * BN; row_max = nc_max - 1;
     } else {
-      base = kp; stride = a.sk.s; row0 = lo_first + (tt - n_ct) * BN - kvp0; row_max = t_last - kvp0;
+      kbase = kb; vbase = vb; ks_ = a.sk.s; vs_ = a.sv.s;
+      row0 = lo_first + (tt - n_ct) * BN - kvp0; row_max = t_last - kvp0;
     }
-    const uint16_t* rowp = base + (int64_t)min(row0 + kkey, row_max) * stride + 8 * khalf;
+    const uint32_t kl = lds0 + st * STAGE, vl = kl + KST;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cp = w + 8 * i;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(rowp + 16 * cp),
-                                       (__attribute__((address_space(3))) void*)(kdst + cp * (2 * BN * 8)), 16, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * w + i;
+      const int64_t row = min(row0 + r, row_max);
+      dma16(kbase + row * ks_ + 8 * lane, kl + r * KROW);
+      dma16(vbase + row * vs_ + 8 * lane, vl + r * VROW);
     }
   };
 
-  // ---- V tile: wave w = 4*dh + vg, lane = 2*dgrp + hi holds keys 16hi + 4vg + i
-  // (i < 4) at dims 256dh + 8dgrp .. +8.  Rows past the valid range re-read the
-  // last valid row, a row some query of this workgroup attends to; their
-  // probabilities are exactly 0, so they add nothing.
-  const int vg = w & 3, dh = w >> 2;
-  const int hi = lane & 1, dgrp = lane >> 1;
-  const int vdim0 = 256 * dh + 8 * dgrp;
-  u32x4 vr[4];
-  auto load_v = [&](int tt) __attribute__((always_inline)) {
-    const uint16_t* base;
-    int64_t stride;
-    int row0, row_max;
-    if (tt < n_ct) {
-      base = vcb; stride = a.svc.s; row0 = tt * BN; row_max = nc_max - 1;
-    } else {
-      base = vb; stride = a.sv.s; row0 = lo_first + (tt - n_ct) * BN - kvp0; row_max = t_last - kvp0;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + 16 * hi + 4 * vg + i;
-      vr[i] = ld16(base + (int64_t)min(row, row_max) * stride + vdim0);
-    }
-  };
-  // V^T write offset (elements) of dim vdim0: chunk vg, half hi (vdim0 % 16 + e < 16,
-  // so the padding term is the same for all eight dims of the lane)
-  const int vw = vg * VCH + (vdim0 + vdim0 / 16) * 8 + 4 * hi;
-  auto store_v = [&](uint16_t* vdst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 x;
-      x[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
-      x[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
-      *reinterpret_cast<u32x2*>(vdst + vw + 8 * e) = x;
-    }
-  };
-
-  f32x4 o[32];
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_used = -INFINITY, l_run = 0.f;
+  f32x16 o[16];
+  // Softmax reference (log2 domain, per query): fixed at the maximum of the
+  // first tile the query sees, never moved afterwards, so O^T is never
+  // rescaled.  m_true tracks the real running maximum; `risk` records a tile
+  // exceeding the reference by more than 2^kGuard (probabilities that large
+  // could overflow fp32), in which case the whole loop runs again with the
+  // exact maximum as reference.
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+  bool risk = false;
   const float c = p.c;
 
-  // per-lane LDS read offsets (elements).  K: chunk 4ks + grp of key 16kt + col.
-  // V^T: chunk grp of dim 16dt + col (padded index 17dt + col).
-  const int k_off = grp * (BN * 8) + col * 8;
-  const int v_off = grp * VCH + col * 8;
+  // Per-lane LDS read offsets (bytes within a stage).
+  //   K (A operand of step ks): key `col`, dims 16ks + 8hf .. +8.
+  //   V^T (A operand of dim tile dt, key step ks, read e): dim 32dt + 16((lane>>4)&1) + lane%16,
+  //   rows 16ks + 8e + 4hf + (lane%16)/4 (each lane of a 16-lane group fetches 4 dims of one row).
+  const uint32_t k_off = col * KROW + 16 * hf;
+  const uint32_t v_off = KST + (4 * hf + ((lane & 15) >> 2)) * VROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-  const int last = max(ntiles - 1, 0);
-  auto compute = [&](int tt, const uint16_t* __restrict__ kst, const uint16_t* __restrict__ vst,
-                     uint16_t* __restrict__ knext, const uint16_t* __restrict__ kcp,
-                     const uint16_t* __restrict__ kp) __attribute__((always_inline)) {
-    // next tile's K DMA (stage pointers are per-object, see the file comment)
-    issue_k(min(tt + 1, last), knext, kcp, kp);
-    if (tt >= ntiles) return;  // the odd trip past the last tile only keeps the pipeline uniform
+  auto compute = [&](int tt, int st) __attribute__((always_inline)) {
     const bool comp = tt < n_ct;
     const int j0 = tt * BN;
     const int p0 = lo_first + (tt - n_ct) * BN;
@@ -220,98 +213,132 @@ void prefill512_kernel(PrefillParams p) {
     const bool active = wave_has_q && (comp ? (j0 < nc_w1) : (p0 <= tw1 && p0 + BN - 1 >= lo_w0));
     if (!active) return;
     const bool full = wave_full && (comp ? (j0 + BN - 1 < nc_w0) : (p0 >= lo_w1 && p0 + BN - 1 <= tw0));
-    // S^T = K Q^T : two 16-key halves x 16 queries (two independent chains)
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const unsigned char* sb = smem + st * STAGE;
+    // S^T = K Q^T : 32 keys x 32 queries, 32 k-steps.  Operand reads run four
+    // steps ahead; the scheduling barriers keep that order (left alone, the
+    // scheduler hoists every read and runs out of registers).
+    auto ldk = [&](int ks) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + k_off + 32 * ks));
+    };
+    f32x16 s;
+    bf16x8 kq[4];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
+    for (int i = 0; i < 4; ++i) kq[i] = ldk(i);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(kst + k_off + 4 * BN * 8 * ks + 16 * 8 * kt));
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[kt], 0, 0, 0);
-      }
+    for (int ks = 0; ks < 32; ++ks) {
+      const bf16x8 ka = kq[ks & 3];
+      if (ks + 4 < 32) kq[ks & 3] = ldk(ks + 4);
+      if (ks == 0) mfma_s_first(s, ka, qf[ks]);
+      else if (ks == 31) mfma_s_last(s, ka, qf[ks]);
+      else mfma_s(s, ka, qf[ks]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // online softmax (log2 domain); lane holds keys 16kt + 4grp + r of query `col`
-    float sv[8];
+    // online softmax (log2 domain); lane holds keys 8(r/4) + 4hf + r%4 of query `col`
+    float sv[16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[4 * kt + r] = s[kt][r] * c;
+    for (int r = 0; r < 16; ++r) sv[r] = s[r] * c;
     if (!full) {
+      // this query's visible keys, relative to the tile: [klo, klo + kn)
+      const int klo = comp ? 0 : lo_q - p0;
+      const int kn = !qvalid ? 0 : comp ? max(nc_q - j0, 0) : tq - lo_q + 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = 16 * (e >> 2) + 4 * grp + (e & 3);
-        const bool valid = comp ? (qvalid && j0 + kk < nc_q) : (qvalid && p0 + kk >= lo_q && p0 + kk <= tq);
-        sv[e] = valid ? sv[e] : -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
+        sv[r] = (unsigned)(kk - klo) < (unsigned)kn ? sv[r] : -INFINITY;
       }
     }
-    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    float mt = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sv[r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool need = mt > m_used + kLazy;
-    if (__any(need)) {
-      const float new_m = need ? mt : m_used;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - new_m) : 1.f;
-      m_used = new_m;
-      l_run *= alpha;
+    m_true = fmaxf(m_true, mt);
+    // first tile with a visible key for this query: O^T is still zero, so the
+    // reference may be set freely
+    if (m_ref == -INFINITY) m_ref = mt;
+    risk |= mt > m_ref + kGuard;
+    // masked logits are -inf: exp2 gives 0 (also while m_ref is still -inf)
+    const float msafe = m_ref == -INFINITY ? 0.f : m_ref;
+    float ps[16];
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
+    for (int r = 0; r < 16; ++r) ps[r] = __builtin_amdgcn_exp2f(fminf(sv[r] - msafe, kGuard));
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum += ps[r];
+    l_run += lsum;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(ps[8 * ks + 2 * e], ps[8 * ks + 2 * e + 1]);
+      pf[ks] = __builtin_bit_cast(bf16x8, pk);
     }
-    // masked logits are -inf and m_used is finite once any key was seen: exp2 gives 0
-    const float msafe = m_used == -INFINITY ? 0.f : m_used;
-    float ps[8];
+    // O^T += V^T P^T : 16 dim tiles x 2 key steps; V^T reads run four MFMAs ahead
+    auto ldv = [&](int i) __attribute__((always_inline)) {  // MFMA i: dim tile i%16, key step i/16
+      const unsigned char* vp = sb + v_off + 64 * (i & 15) + (16 * (i >> 4)) * VROW;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
+      const s16x4 hi4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * VROW));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // key step major (i = 16 ks + dt), so consecutive MFMAs use different accumulators
+    bf16x8 vq[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ps[e] = __builtin_amdgcn_exp2f(sv[e] - msafe);
-    l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-    u32x4 pk;
+    for (int i = 0; i < 4; ++i) vq[i] = ldv(i);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(ps[2 * e], ps[2 * e + 1]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
-    // O^T += V^T P^T : 32 dim tiles, one 32-key step each
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vst + v_off + 17 * 8 * dt));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
+    for (int i = 0; i < 32; ++i) {
+      const bf16x8 va = vq[i & 3];
+      if (i + 4 < 32) vq[i & 3] = ldv(i + 4);
+      if (i == 0) mfma_o_first(o[i & 15], va, pf[i >> 4]);
+      else mfma_o(o[i & 15], va, pf[i >> 4]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Pipeline: tile tt's K DMA and V loads are issued one iteration ahead.
-  // Loads are unconditional (past the end they re-read the last tile) so the
-  // load counting stays exact.
-  // Two tiles per trip with fixed stages (even tiles in stage 0, odd in stage 1).
-  // The trip for tile tt stores its V^T, waits for its K DMA and V loads, then
-  // issues the next tile's loads and computes.  Loads are unconditional (past
-  // the end they re-read the last tile) so the load counting stays exact.
-  if (ntiles > 0) {
-    issue_k(0, Ks0, kcb, kb);
-    load_v(0);
-    for (int tt = 0; tt < ntiles; tt += 2) {
-      store_v(Vt0);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      load_v(min(tt + 1, last));
-      compute(tt, Ks0, Vt0, Ks1, kcb, kb);
-      store_v(Vt1);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      load_v(min(tt + 2, last));
-      compute(tt + 1, Ks1, Vt1, Ks0, kcb, kb);
+  const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  if (tid == 0) redo_flag = 0;
+  // Pipeline: tile tt+1's DMA is issued right after the barrier that opens
+  // tile tt, into the stage tile tt-1 used (every wave has left it by then).
+  // The second pass (rare, see m_ref) is decided for the whole workgroup, as
+  // the loop holds barriers.
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) zero_o(o[dt], zero8);
+    l_run = 0.f;
+    if (ntiles > 0) {
+      issue(0, 0);
+      for (int tt = 0; tt < ntiles; ++tt) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (tt + 1 < ntiles) issue(tt + 1, (tt + 1) & 1);
+        compute(tt, tt & 1);
+      }
     }
+    if (pass == 1) break;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (__any(risk) && lane == 0) redo_flag = 1;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (redo_flag == 0) break;
+    m_ref = m_true;  // exact maximum: every probability is at most 1
+    risk = false;
   }
 
-  // ---- epilogue: normalise, store bf16 O and the LSE
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  // ---- epilogue: normalise, store bf16 O and the LSE (wait states: O^T is
+  // read right after the last MFMA wrote it)
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* op = (uint16_t*)a.o + b * a.so.b + (int64_t)iq * a.so.s + (int64_t)h * a.so.h + 4 * grp;
+  uint16_t* op = (uint16_t*)a.o + b * a.so.b + (int64_t)iq * a.so.s + (int64_t)h * a.so.h + 4 * hf;
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) {
-    u32x2 pk;
-    pk[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-    pk[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-    *reinterpret_cast<u32x2*>(op + 16 * dt) = pk;
-  }
-  if (a.lse && grp == 0) a.lse[((int64_t)b * a.h_q + h) * a.seqlen_q + iq] = m_used * kLn2 + __logf(l_tot);
+  for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv);
+      pk[1] = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q4) = pk;
+    }
+  if (a.lse && hf == 0) a.lse[((int64_t)b * a.h_q + h) * a.seqlen_q + iq] = m_ref * kLn2 + __logf(l_tot);
 }
 
 }  // namespace

@@ -130,6 +130,31 @@ def test_prefill_unit_variance_logits():
     assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
 
 
+def test_prefill_extreme_logits():
+    """Logits with a spread of hundreds: later tiles exceed the first tile's
+    maximum by far more than fp32 exp range allows for a fixed reference, so
+    the kernel must fall back to its exact-maximum pass.  The oracle is plain
+    max-subtracted softmax."""
+    cfg = synth.small_prefill("c2", name="extreme", seqlen=640, h_q=2, h_kv=2, std=1.0, window=128)
+    _say("prefill", cfg)
+    inp = synth.make_prefill(cfg)
+    # scale q by 64 (exact in bf16): logit std about 64
+    q64 = synth.bf16_round_bits(synth.bf16_bits_to_f32(inp["q"]) * np.float32(64.0))
+    q = dev_bf16(q64)
+    k, v = dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.hca_attention(f64(q64, True), f64(inp["k"], True), f64(inp["v"], True), host(kc), host(vc),
+                                    window=cfg.window, block=cfg.block, scale=cfg.scale)
+    assert np.all(np.isfinite(host(o))) and np.all(np.isfinite(host(lse)))
+    err = rel_err(host(o), ro)
+    _say(f"  rel err {err:.3e}, lse range {rlse.min():.1f} .. {rlse.max():.1f}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
 def test_prefill_deterministic_and_writes_every_output():
     cfg = synth.small_prefill("c2", name="det", seqlen=700, h_q=2, h_kv=2, window=128)
     inp = synth.make_prefill(cfg)
