@@ -246,7 +246,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c3,c4,c5", help="comma list of workloads to run")
+    ap.add_argument("--only", default="c2,c3,c4,c5",
+                    help="comma list of workloads to run (c2 always runs; 'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -262,6 +263,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     only = set(args.only.split(","))
+    if "copy" in only:
+        # Calibration leg for the HBM traffic counters: a plain device copy of a
+        # known size, profiled with the same counters as the attention kernels.
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": 5}), flush=True)
+        return
     comps = {}
 
     c2 = synth.CONFIGS["c2"]
