@@ -225,6 +225,28 @@ def test_decode_parity(B, Hq, Hkv, nb, W, qpos):
     assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
 
 
+def test_decode_workspace_reuse_across_calls_and_shapes():
+    """One workspace serves consecutive decode calls of different shapes
+    (different chunk counts), each call fully overwriting what it uses."""
+    shapes = [(4, 16, 1, 300, 128), (2, 32, 2, 77, 64), (3, 16, 1, 20, 128), (4, 16, 1, 300, 128)]
+    cfgs = [synth.small_decode(batch=B, h_q=Hq, h_kv=Hkv, n_blocks=nb, window=W, seed=10 + i)
+            for i, (B, Hq, Hkv, nb, W) in enumerate(shapes)]
+    wsz = max(hca.hca_attn_fwd_workspace_size(c.batch, 1, c.h_q, c.h_kv, 512, c.n_blocks, c.window) for c in cfgs)
+    ws = torch.zeros(wsz, dtype=torch.uint8, device="cuda:0")
+    for cfg in cfgs:
+        _say("decode reuse", cfg)
+        inp = synth.make_decode(cfg)
+        q, kw, vw, kc, vc = (dev_bf16(inp[n]) for n in ("q", "kw", "vw", "kc", "vc"))
+        o, lse = hca.hca_attn_fwd(q, kw, vw, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale,
+                                  q_pos0=cfg.q_pos, kv_pos0=cfg.kv_pos0, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rlse = oracle.hca_attention(*(f64(inp[n], True) for n in ("q", "kw", "vw", "kc", "vc")),
+                                        window=cfg.window, block=cfg.block, scale=cfg.scale, q_pos0=cfg.q_pos,
+                                        kv_pos0=cfg.kv_pos0)
+        assert rel_err(host(o), ro) < BF16_TOL
+        assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
 def test_decode_equals_prefill_row():
     cfg = synth.small_prefill("c2", name="dec-vs-pre", seqlen=1100, h_q=4, h_kv=1, window=128, std=1.0)
     inp = synth.make_prefill(cfg)
