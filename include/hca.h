@@ -171,7 +171,7 @@ hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float*
  *   q: [batch, seqlen, h_q, d_qk]; k: [batch, seqlen, h_kv, d_qk];
  *   v: [batch, seqlen, h_kv, d_v]; o: [batch, seqlen, h_q, d_v];
  *   idx: [batch, seqlen, topk] int32 contiguous; lse: [batch, h_q, seqlen] fp32 or NULL.
- * Supported: bf16, d_qk = d_v = 256, (h_q / h_kv) a multiple of 64.
+ * Supported: bf16, d_qk = d_v = 256, (h_q / h_kv) a multiple of 64, topk <= 4096.
  */
 hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt,
                                  const void* q, hca_strides_t sq,

@@ -259,8 +259,9 @@ hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq
   HCA_TRY(check_tensor("v", v, sv, es));
   HCA_TRY(check_tensor("o", o, so, es));
   if (lse && ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is not 4-byte aligned");
-  if (dt != HCA_DTYPE_BF16 || d_qk != 256 || d_v != 256 || (h_q / h_kv) % 64)
-    return fail(HCA_ERR_UNSUPPORTED, "dsa_sparse_attn_fwd: needs bf16, d_qk = d_v = 256, h_q/h_kv a multiple of 64");
+  if (dt != HCA_DTYPE_BF16 || d_qk != 256 || d_v != 256 || (h_q / h_kv) % 64 || topk > 4096)
+    return fail(HCA_ERR_UNSUPPORTED,
+                "dsa_sparse_attn_fwd: needs bf16, d_qk = d_v = 256, h_q/h_kv a multiple of 64, topk <= 4096");
   {
     const Range ro = extent(o, so, batch, seqlen, h_q, d_v, es);
     if (overlaps(ro, extent(q, sq, batch, seqlen, h_q, d_qk, es)) ||

@@ -113,11 +113,13 @@ def test_dsa_rejects_bad_arguments():
     sp = lambda **kw: lib.dsa_sparse_attn_fwd(kw.get("dt", 1), FAKE, S(0, 64 * 256, 256), FAKE, S(0, 256, 256),
                                               FAKE, S(0, 256, 256), kw.get("idx", ctypes.c_void_p(1 << 33)),
                                               ctypes.c_void_p(1 << 34), S(0, 64 * 256, 256), None, 1, 100,
-                                              kw.get("hq", 64), 1, kw.get("d", 256), 256, 16, 0.0625, None)
+                                              kw.get("hq", 64), 1, kw.get("d", 256), 256, kw.get("k", 16), 0.0625,
+                                              None)
     assert sp(idx=None) == hca.HCA_ERR_INVALID
     assert sp(d=128) == hca.HCA_ERR_UNSUPPORTED
     assert sp(hq=32) == hca.HCA_ERR_UNSUPPORTED
     assert sp(dt=0) == hca.HCA_ERR_UNSUPPORTED
+    assert sp(k=4097) == hca.HCA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
