@@ -12,9 +12,12 @@
 //      as w * relu(.) into the score tile; operands come straight from global
 //      memory (every lane reads contiguous 16-byte runs), no LDS.
 //   2. topk_select: one workgroup per query row.  Scores map to
-//      order-preserving uint32 keys (-0 counts as +0); three LDS histogram
-//      passes (11 + 11 + 10 bits) find the exact k-th largest key T; a final
-//      ordered pass emits every key > T and the lowest-position keys == T.
+//      order-preserving uint32 keys (-0 counts as +0).  A 12-bit LDS
+//      histogram locates the bin of the k-th largest key; one ordered pass
+//      emits everything above that bin and gathers the bin into LDS, where
+//      two 10-bit passes find the exact k-th largest key T; keys > T and the
+//      lowest positions with key == T are emitted (two reads of the row; rows
+//      whose boundary bin is too large use four radix passes over the row).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -109,14 +112,118 @@ struct SelectParams {
   int r0, topk;
 };
 
-constexpr int NB = 2048;
+constexpr int NB = 2048;   // bins of the general radix passes (11 + 11 + 10 bits)
+constexpr int HB = 4096;   // bins of the first pass of the fast path (top 12 bits)
+constexpr int CAP = 4096;  // candidates the fast path resolves in LDS
 
+// Descending prefix over nb bins held in hist[] (256 threads, nb a multiple
+// of 256): returns in sel[0] the bin holding the need-th largest element and in
+// sel[1] the number of elements in higher bins.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* part,
+                                         uint32_t* sel) {
+  const int tid = threadIdx.x;
+  const int per = nb / 256;
+  uint32_t csum = 0;
+  for (int j = 0; j < per; ++j) csum += hist[nb - 1 - (tid * per + j)];
+  part[tid] = csum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const uint32_t before = tid ? part[tid - 1] : 0u;
+  if (before < need && part[tid] >= need) {
+    uint32_t acc = before;
+    for (int j = 0; j < per; ++j) {
+      const uint32_t bin = nb - 1 - (tid * per + j);
+      const uint32_t c = hist[bin];
+      if (acc + c >= need) {
+        sel[0] = bin;
+        sel[1] = acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Ordered compaction helper: every thread of the workgroup has one flag; the
+// flagged threads get consecutive ranks in thread order (wave ballots plus a
+// cross-wave prefix in LDS).  Returns this thread's rank and the total.
+__device__ __forceinline__ uint32_t ordered_rank(bool flag, uint32_t* wave_cnt, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t m = __ballot(flag);
+  const uint32_t below = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wave_cnt[w] = __popcll(m);
+  __syncthreads();
+  uint32_t off = 0;
+  for (int i = 0; i < w; ++i) off += wave_cnt[i];
+  total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+  __syncthreads();
+  return off + below;
+}
+
+// Wave-aggregated LDS slot allocation: the flagged lanes of a wave get
+// consecutive slots from *ctr (one atomic per wave).  Returns the lane's slot.
+__device__ __forceinline__ uint32_t wave_alloc(bool flag, uint32_t* ctr) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t m = __ballot(flag);
+  uint32_t base = 0;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  if (m && lane == leader) base = atomicAdd(ctr, (uint32_t)__popcll(m));
+  base = __shfl(base, leader < 0 ? 0 : leader);
+  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
+
+// Workgroup-wide exclusive prefix of a per-thread count in [0, 31], in thread
+// order, from ballots of the count's bits (no atomics).  wave_cnt needs 4
+// entries; total receives the workgroup sum.  Contains two barriers.
+__device__ __forceinline__ uint32_t wg_prefix(uint32_t cnt, uint32_t* wave_cnt, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t pre = 0, wtot = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t m = __ballot((cnt >> bit) & 1u);
+    pre += (uint32_t)__popcll(m & lt) << bit;
+    wtot += (uint32_t)__popcll(m) << bit;
+  }
+  if (lane == 0) wave_cnt[w] = wtot;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int i = 0; i < w; ++i) off += wave_cnt[i];
+  total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+  __syncthreads();
+  return off + pre;
+}
+
+constexpr int NS = 1024;  // samples of a row used to bracket the k-th largest key
+
+// One workgroup per query row: the k largest scores (ties to the lower
+// position) of positions 0 .. t.
+//   Fast path: a 12-bit histogram finds the bin B holding the k-th largest
+//   key; one ordered pass emits every position above B and collects the
+//   positions in B (in position order) into LDS; two 10-bit passes over that
+//   short list find the exact threshold key T; positions above T are emitted
+//   and the lowest positions equal to T complete the set.  Two reads of the
+//   row in all.
+//   General path (bin B holds more than CAP positions, e.g. massive ties): three
+//   radix passes over the row find T, then one ordered pass emits the set.
+//   Long rows first try a sampling path: 1024 strided samples, sorted in LDS,
+//   bracket the k-th largest key; one pass emits the keys above the bracket
+//   and collects the keys inside it (at most CAP), where T and the tie-break
+//   are resolved in LDS.  When the bracket misses, the paths above run.
 __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
-  __shared__ uint32_t hist[NB];
+  __shared__ uint32_t hist[HB];
+  __shared__ uint32_t ckey[CAP];
+  __shared__ int cpos[CAP];
   __shared__ uint32_t part[256];
   __shared__ uint32_t sel_info[4];
   __shared__ uint32_t wave_cnt[4];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int t = p.r0 + row;
   const int n = t + 1;
@@ -128,10 +235,249 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
   }
   const float* srow = p.sc + (int64_t)row * p.ld;
 
-  // radix passes: bits [31:21], [20:10], [9:0]
-  uint32_t prefix = 0;       // fixed high bits so far
-  uint32_t prefix_mask = 0;
-  int need = k;              // how many still to take among elements matching the prefix
+  // ---- sampling path: bracket the k-th largest key with a sorted sample,
+  // then one pass over the row emits the keys above the bracket and collects
+  // the keys inside it; the exact threshold is resolved in LDS.
+  if (n >= 4 * NS) {
+    uint32_t* skey = hist;  // the sample lives in the histogram space
+    for (int i = tid; i < NS; i += 256) skey[i] = okey(srow[(int64_t)i * n / NS]);
+    if (tid == 0) sel_info[2] = sel_info[3] = 0;
+    __syncthreads();
+    // bitonic sort, descending
+    for (int size = 2; size <= NS; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < NS / 2; i += 256) {
+          const int lo_i = 2 * i - (i & (stride - 1));
+          const int hi_i = lo_i + stride;
+          const uint32_t x = skey[lo_i], y = skey[hi_i];
+          const bool desc = (lo_i & size) == 0;
+          if (desc ? x < y : x > y) {
+            skey[lo_i] = y;
+            skey[hi_i] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const int r = (int)((int64_t)k * NS / n);
+    const int delta = (int)(4.f * sqrtf((float)r * (1.f - (float)r / NS))) + 8;
+    const uint32_t hi = r - delta >= 0 ? skey[r - delta] : 0xffffffffu;  // keys > hi are in
+    const uint32_t lo = r + delta < NS ? skey[r + delta] : 0u;           // keys < lo are out
+    __syncthreads();
+    {
+      // Steps of 4096 elements: thread tid classifies elements
+      // base + 1024e + 4tid + j (e, j < 4) into bit masks, a workgroup prefix of
+      // the mask counts gives every flagged element its slot.
+      uint32_t run_a = 0, run_i = 0;  // slots used so far (workgroup-uniform)
+      for (int base = 0; base < n; base += 4096) {
+        f32x4 v[4];
+        uint32_t fa = 0, fi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int u0 = base + 1024 * e + 4 * tid;
+          if (u0 + 3 < n) {
+            v[e] = *reinterpret_cast<const f32x4*>(srow + u0);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[e][j] = u0 + j < n ? srow[u0 + j] : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t key = okey(v[e][j]);
+            const bool valid = u0 + j < n;
+            const bool above = valid && key > hi;
+            const bool inside = valid && !above && key >= lo;
+            fa |= (uint32_t)above << (4 * e + j);
+            fi |= (uint32_t)inside << (4 * e + j);
+          }
+        }
+        uint32_t tot_a, tot_i;
+        const uint32_t oa = run_a + wg_prefix((uint32_t)__popc(fa), wave_cnt, tot_a);
+        const uint32_t oi = run_i + wg_prefix((uint32_t)__popc(fi), wave_cnt, tot_i);
+        uint32_t ra = 0, ri = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int u = base + 1024 * e + 4 * tid + j;
+            if ((fa >> (4 * e + j)) & 1u) {
+              if (oa + ra < (uint32_t)k) out[oa + ra] = u;
+              ++ra;
+            }
+            if ((fi >> (4 * e + j)) & 1u) {
+              if (oi + ri < (uint32_t)CAP) {
+                ckey[oi + ri] = okey(v[e][j]);
+                cpos[oi + ri] = u;
+              }
+              ++ri;
+            }
+          }
+        run_a += tot_a;
+        run_i += tot_i;
+      }
+      if (tid == 0) {
+        sel_info[2] = run_a;
+        sel_info[3] = run_i;
+      }
+    }
+    __syncthreads();
+    const uint32_t c_hi = sel_info[2], nc = sel_info[3];
+    if (c_hi < (uint32_t)k && nc <= (uint32_t)CAP && c_hi + nc >= (uint32_t)k) {
+      // exact threshold among the candidates: need-th largest key
+      uint32_t need = (uint32_t)k - c_hi;
+      uint32_t prefix = 0, pmask = 0;
+      for (int pass = 0; pass < 3; ++pass) {
+        const int sh = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+        const uint32_t nb = pass == 2 ? 1024u : 2048u;  // bits 31..21, 20..10, 9..0
+        __syncthreads();
+        for (int i = tid; i < (int)nb; i += 256) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < (int)nc; i += 256)
+          if ((ckey[i] & pmask) == prefix) atomicAdd(&hist[(ckey[i] >> sh) & (nb - 1)], 1u);
+        __syncthreads();
+        find_bin(hist, (int)nb, need, part, sel_info);
+        need -= sel_info[1];
+        prefix |= sel_info[0] << sh;
+        pmask |= (nb - 1) << sh;
+      }
+      const uint32_t T = prefix;
+      const uint32_t n_gt = (uint32_t)k - need;  // keys > T in the whole row
+      // candidates above T, and the number equal to T
+      __syncthreads();
+      if (tid == 0) sel_info[2] = c_hi, sel_info[3] = 0;
+      __syncthreads();
+      for (int base = 0; base < (int)nc; base += 256) {
+        const int i = base + tid;
+        const bool valid = i < (int)nc;
+        const uint32_t key = valid ? ckey[i] : 0u;
+        const int pos = valid ? cpos[i] : 0;
+        const bool gt = valid && key > T;
+        const uint32_t sa = wave_alloc(gt, &sel_info[2]);
+        if (gt) out[sa] = pos;
+        const bool eq = valid && key == T;
+        const uint32_t se = wave_alloc(eq, &sel_info[3]);
+        // compact the tied positions into ckey; every slot written here is below
+        // base + 256, i.e. already read by its owner before this barrier
+        __syncthreads();
+        if (eq) ckey[se] = (uint32_t)pos;
+        __syncthreads();
+      }
+      __syncthreads();
+      const uint32_t neq = sel_info[3];
+      // the `need` lowest positions among the ties: need-th largest of ~position
+      uint32_t pmax = 0xffffffffu;
+      if (neq > need) {
+        uint32_t nd = need, pre = 0, pm = 0;
+        for (int pass = 0; pass < 3; ++pass) {
+          const int sh = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+          const uint32_t nb = pass == 2 ? 1024u : 2048u;  // bits 31..21, 20..10, 9..0
+          __syncthreads();
+          for (int i = tid; i < (int)nb; i += 256) hist[i] = 0;
+          __syncthreads();
+          for (int i = tid; i < (int)neq; i += 256) {
+            const uint32_t kp = ~ckey[i];
+            if ((kp & pm) == pre) atomicAdd(&hist[(kp >> sh) & (nb - 1)], 1u);
+          }
+          __syncthreads();
+          find_bin(hist, (int)nb, nd, part, sel_info);
+          nd -= sel_info[1];
+          pre |= sel_info[0] << sh;
+          pm |= (nb - 1) << sh;
+        }
+        pmax = ~pre;  // the need-th lowest tied position
+      }
+      __syncthreads();
+      if (tid == 0) sel_info[2] = n_gt;
+      __syncthreads();
+      for (int base = 0; base < (int)neq; base += 256) {
+        const int i = base + tid;
+        const bool take = i < (int)neq && ckey[i] <= pmax;
+        const uint32_t sa = wave_alloc(take, &sel_info[2]);
+        if (take) out[sa] = (int)ckey[i];
+      }
+      return;
+    }
+    __syncthreads();
+  }
+
+  // ---- pass 1: histogram of the top 12 bits
+  for (int i = tid; i < HB; i += 256) hist[i] = 0;
+  if (tid == 0) sel_info[2] = 0;
+  __syncthreads();
+  {
+    const int n4 = n & ~3;
+    for (int u = 4 * tid; u < n4; u += 1024) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(srow + u);
+      atomicAdd(&hist[okey(v[0]) >> 20], 1u);
+      atomicAdd(&hist[okey(v[1]) >> 20], 1u);
+      atomicAdd(&hist[okey(v[2]) >> 20], 1u);
+      atomicAdd(&hist[okey(v[3]) >> 20], 1u);
+    }
+    for (int u = n4 + tid; u < n; u += 256) atomicAdd(&hist[okey(srow[u]) >> 20], 1u);
+  }
+  __syncthreads();
+  find_bin(hist, HB, (uint32_t)k, part, sel_info);
+  const uint32_t B = sel_info[0];
+  const uint32_t above_b = sel_info[1];
+  const uint32_t in_b = hist[B];
+
+  if (in_b <= (uint32_t)CAP) {
+    // ---- pass 2: emit bins above B, collect bin B in position order
+    uint32_t nc = 0;
+    for (int base = 0; base < n; base += 256) {
+      const int u = base + tid;
+      uint32_t key = 0;
+      const bool valid = u < n;
+      if (valid) key = okey(srow[u]);
+      const uint32_t bin = key >> 20;
+      if (valid && bin > B) out[atomicAdd(&sel_info[2], 1u)] = u;
+      uint32_t tot;
+      const bool inb = valid && bin == B;
+      const uint32_t r = ordered_rank(inb, wave_cnt, tot);
+      if (inb) {
+        ckey[nc + r] = key;
+        cpos[nc + r] = u;
+      }
+      nc += tot;
+    }
+    __syncthreads();
+    // ---- resolve the threshold among the nc = in_b candidates (bits 19..0)
+    uint32_t need = (uint32_t)k - above_b;
+    uint32_t prefix = B << 20, pmask = 0xfff00000u;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int sh = pass == 0 ? 10 : 0;
+      for (int i = tid; i < 1024; i += 256) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < (int)nc; i += 256)
+        if ((ckey[i] & pmask) == prefix) atomicAdd(&hist[(ckey[i] >> sh) & 1023u], 1u);
+      __syncthreads();
+      find_bin(hist, 1024, need, part, sel_info);
+      need -= sel_info[1];
+      prefix |= sel_info[0] << sh;
+      pmask |= 1023u << sh;
+      __syncthreads();
+    }
+    const uint32_t T = prefix;
+    const uint32_t n_gt = (uint32_t)k - need;  // keys > T, all emitted below
+    // candidates above T (unordered), then the `need` lowest positions equal to T
+    uint32_t eq_base = 0;
+    for (int base = 0; base < (int)nc; base += 256) {
+      const int i = base + tid;
+      const bool valid = i < (int)nc;
+      const uint32_t key = valid ? ckey[i] : 0u;
+      if (valid && key > T) out[atomicAdd(&sel_info[2], 1u)] = cpos[i];
+      uint32_t tot;
+      const bool eq = valid && key == T;
+      const uint32_t r = ordered_rank(eq, wave_cnt, tot);
+      if (eq && eq_base + r < need) out[n_gt + eq_base + r] = cpos[i];
+      eq_base += tot;
+    }
+    return;
+  }
+
+  // ---- general path: radix passes over the row (bits [31:21], [20:10], [9:0])
+  uint32_t prefix = 0, prefix_mask = 0;
+  uint32_t need = (uint32_t)k;
   const int shifts[3] = {21, 10, 0};
   const int widths[3] = {11, 11, 10};
   for (int pass = 0; pass < 3; ++pass) {
@@ -144,68 +490,30 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       if ((key & prefix_mask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // descending scan: thread i owns bins [nb - 8(i+1), nb - 8i)
-    const int per = nb / 256;
-    uint32_t csum = 0;
-    for (int j = 0; j < per; ++j) csum += hist[nb - 1 - (tid * per + j)];
-    part[tid] = csum;
-    __syncthreads();
-    // inclusive scan over part[] (Hillis-Steele)
-    for (int off = 1; off < 256; off <<= 1) {
-      const uint32_t v = tid >= off ? part[tid - off] : 0u;
-      __syncthreads();
-      part[tid] += v;
-      __syncthreads();
-    }
-    const uint32_t before = tid ? part[tid - 1] : 0u;
-    if (before < (uint32_t)need && part[tid] >= (uint32_t)need) {
-      uint32_t acc = before;
-      for (int j = 0; j < per; ++j) {
-        const uint32_t bin = nb - 1 - (tid * per + j);
-        const uint32_t c = hist[bin];
-        if (acc + c >= (uint32_t)need) {
-          sel_info[0] = bin;
-          sel_info[1] = acc;  // elements above this bin (within the prefix)
-          break;
-        }
-        acc += c;
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = sel_info[0];
-    need -= (int)sel_info[1];
-    prefix |= bin << sh;
+    find_bin(hist, (int)nb, need, part, sel_info);
+    need -= sel_info[1];
+    prefix |= sel_info[0] << sh;
     prefix_mask |= (nb - 1) << sh;
     __syncthreads();
   }
   // prefix is now the exact threshold key T; take every key > T and the `need`
   // lowest positions with key == T
   const uint32_t T = prefix;
-  const int n_above = k - need;
+  const uint32_t n_above = (uint32_t)k - need;
   if (tid == 0) sel_info[2] = 0;
   __syncthreads();
   uint32_t eq_base = 0;
   for (int base = 0; base < n; base += 256) {
     const int u = base + tid;
     uint32_t key = 0;
-    bool valid = u < n;
+    const bool valid = u < n;
     if (valid) key = okey(srow[u]);
-    const bool gt = valid && key > T;
+    if (valid && key > T) out[atomicAdd(&sel_info[2], 1u)] = u;
+    uint32_t tot;
     const bool eq = valid && key == T;
-    if (gt) {
-      const uint32_t slot = atomicAdd(&sel_info[2], 1u);
-      out[slot] = u;
-    }
-    const uint64_t m = __ballot(eq);
-    const uint32_t below = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[w] = __popcll(m);
-    __syncthreads();
-    uint32_t off = eq_base;
-    for (int i = 0; i < w; ++i) off += wave_cnt[i];
-    const uint32_t total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-    if (eq && off + below < (uint32_t)need) out[n_above + off + below] = u;
-    eq_base += total;
-    __syncthreads();
+    const uint32_t r = ordered_rank(eq, wave_cnt, tot);
+    if (eq && eq_base + r < need) out[n_above + eq_base + r] = u;
+    eq_base += tot;
   }
 }
 

@@ -43,6 +43,42 @@ def test_index_topk_exact_sets(S, topk, B):
     assert np.array_equal(got, ref)
 
 
+def test_index_topk_long_rows_exact():
+    """Rows of 4096+ positions take the sampling selection path; tie-free rows
+    must give exactly the oracle's sets."""
+    S, k = 6000, 512
+    cfg = synth.small_dsa(seqlen=S, topk=k)
+    _say("index_topk long rows", cfg)
+    inp = synth.make_dsa(cfg)
+    rows = list(range(4096, S, 7)) + [S - 1]
+    for attempt in range(1, 13):
+        bad = [(0, t) for t in rows if not oracle.tie_free_row(inp["qI"][0, t], inp["kI"][0], inp["w"][0, t], t, k)]
+        if not bad:
+            break
+        synth.redraw_dsa_rows(inp, bad, attempt)
+    assert not bad
+    idx = hca.dsa_index_topk(dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"]), k)
+    got = _sorted_rows(idx.cpu().numpy())
+    ref = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], k, rows=rows)
+    assert np.array_equal(got[:, rows], ref)
+
+
+def test_index_topk_long_rows_heavy_ties():
+    """Integer-valued scores with thousands of ties per value on long rows: the
+    tie-break by position must be exact on every selection path."""
+    S, k = 6000, 512
+    rng = np.random.default_rng(11)
+    kI = np.zeros((1, S, 64), dtype=np.float32)
+    kI[0, np.arange(S), np.arange(S) % 8] = 1.0
+    qI = rng.integers(0, 2, (1, S, 4, 64)).astype(np.float32)
+    w = rng.integers(1, 3, (1, S, 4)).astype(np.float32)
+    idx = hca.dsa_index_topk(dev_f32(qI), dev_f32(kI), dev_f32(w), k)
+    got = _sorted_rows(idx.cpu().numpy())
+    rows = list(range(4090, S, 13)) + [S - 1]
+    ref = oracle.index_topk(qI, kI, w, k, rows=rows)
+    assert np.array_equal(got[:, rows], ref)
+
+
 def test_index_topk_ties_break_by_position():
     """Equal index keys make every score equal: the first k positions win."""
     S, k = 600, 64
