@@ -12,12 +12,16 @@
 //      as w * relu(.) into the score tile; operands come straight from global
 //      memory (every lane reads contiguous 16-byte runs), no LDS.
 //   2. topk_select: one workgroup per query row.  Scores map to
-//      order-preserving uint32 keys (-0 counts as +0).  A 12-bit LDS
-//      histogram locates the bin of the k-th largest key; one ordered pass
-//      emits everything above that bin and gathers the bin into LDS, where
-//      two 10-bit passes find the exact k-th largest key T; keys > T and the
-//      lowest positions with key == T are emitted (two reads of the row; rows
-//      whose boundary bin is too large use four radix passes over the row).
+//      order-preserving uint32 keys (-0 counts as +0).  Rows of 4096 keys or
+//      more first bracket the k-th largest key with two order statistics of a
+//      1024-key sample (256 spread groups of 4 adjacent keys); one pass over
+//      the row emits the keys above the bracket and gathers those inside it
+//      into LDS, where radix passes find the exact k-th largest key T.
+//      Otherwise (short rows, or a bracket that missed) an 11-bit LDS
+//      histogram locates the bin of T, one ordered pass emits everything above
+//      that bin and gathers the bin, and 11- and 10-bit passes find T; rows
+//      whose boundary bin is too large use four radix passes over the row.  In
+//      every path keys > T and the lowest positions with key == T are emitted.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -113,28 +117,33 @@ struct SelectParams {
 };
 
 constexpr int NB = 2048;   // bins of the general radix passes (11 + 11 + 10 bits)
-constexpr int HB = 4096;   // bins of the first pass of the fast path (top 12 bits)
-constexpr int CAP = 4096;  // candidates the fast path resolves in LDS
+constexpr int HB = 2048;   // bins of the first pass of the fast path (top 11 bits)
+// candidates resolved in LDS; with HB this keeps the selection under 40 KB of
+// LDS, so four workgroups share a CU
+constexpr int CAP = 3840;
 
 // Descending prefix over nb bins held in hist[] (256 threads, nb a multiple
 // of 256): returns in sel[0] the bin holding the need-th largest element and in
-// sel[1] the number of elements in higher bins.
+// sel[1] the number of elements in higher bins.  Wave scans by lane shuffles,
+// one LDS exchange of the wave totals (part[] holds 4 entries).
 __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* part,
                                          uint32_t* sel) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = nb / 256;
   uint32_t csum = 0;
   for (int j = 0; j < per; ++j) csum += hist[nb - 1 - (tid * per + j)];
-  part[tid] = csum;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  uint32_t x = csum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const uint32_t before = tid ? part[tid - 1] : 0u;
-  if (before < need && part[tid] >= need) {
+  if (lane == 63) part[w] = x;
+  __syncthreads();
+  uint32_t wbase = 0;
+  for (int i = 0; i < w; ++i) wbase += part[i];
+  const uint32_t incl = x + wbase, before = incl - csum;
+  if (before < need && incl >= need) {
     uint32_t acc = before;
     for (int j = 0; j < per; ++j) {
       const uint32_t bin = nb - 1 - (tid * per + j);
@@ -174,53 +183,69 @@ __device__ __forceinline__ uint32_t wave_alloc(bool flag, uint32_t* ctr) {
   uint32_t base = 0;
   const int leader = __ffsll((unsigned long long)m) - 1;
   if (m && lane == leader) base = atomicAdd(ctr, (uint32_t)__popcll(m));
-  base = __shfl(base, leader < 0 ? 0 : leader);
+  base = __builtin_amdgcn_readlane(base, leader < 0 ? 0 : leader);
   return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
-// Workgroup-wide exclusive prefix of a per-thread count in [0, 31], in thread
-// order, from ballots of the count's bits (no atomics).  wave_cnt needs 4
-// entries; total receives the workgroup sum.  Contains two barriers.
-__device__ __forceinline__ uint32_t wg_prefix(uint32_t cnt, uint32_t* wave_cnt, uint32_t& total) {
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// (the next step of a row scan) are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup-wide exclusive prefixes, in thread order, of two per-thread
+// counts in [0, 31] packed as a | b << 16 (ballots of the count bits; one LDS
+// exchange).  Returns the packed prefix; total receives the packed sums.
+__device__ __forceinline__ uint32_t wg_prefix2(uint32_t cnt, uint32_t* wave_cnt, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t pre = 0, wtot = 0;
 #pragma unroll
-  for (int bit = 0; bit < 5; ++bit) {
-    const uint64_t m = __ballot((cnt >> bit) & 1u);
-    pre += (uint32_t)__popcll(m & lt) << bit;
-    wtot += (uint32_t)__popcll(m) << bit;
-  }
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+      const int sh = 16 * f + bit;
+      const uint64_t m = __ballot((cnt >> sh) & 1u);
+      pre += (uint32_t)__popcll(m & lt) << sh;
+      wtot += (uint32_t)__popcll(m) << sh;
+    }
   if (lane == 0) wave_cnt[w] = wtot;
-  __syncthreads();
+  lds_barrier();
   uint32_t off = 0;
   for (int i = 0; i < w; ++i) off += wave_cnt[i];
   total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-  __syncthreads();
+  lds_barrier();
   return off + pre;
+}
+
+// The float F with okey(x) >= K  <=>  x >= F for every non-NaN x (IEEE
+// compares; fp32 denormals are preserved in these kernels): the key's inverse
+// image, -inf below the key of -inf and NaN (never true) above that of +inf.
+__device__ __forceinline__ float key_ge_float(uint32_t K) {
+  if (K <= 0x007fffffu) return -INFINITY;
+  if (K > 0xff800000u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((K & 0x80000000u) ? (K & 0x7fffffffu) : ~K);
 }
 
 constexpr int NS = 1024;  // samples of a row used to bracket the k-th largest key
 
 // One workgroup per query row: the k largest scores (ties to the lower
 // position) of positions 0 .. t.
-//   Fast path: a 12-bit histogram finds the bin B holding the k-th largest
+//   Fast path: an 11-bit histogram finds the bin B holding the k-th largest
 //   key; one ordered pass emits every position above B and collects the
-//   positions in B (in position order) into LDS; two 10-bit passes over that
+//   positions in B (in position order) into LDS; 11- and 10-bit passes over that
 //   short list find the exact threshold key T; positions above T are emitted
 //   and the lowest positions equal to T complete the set.  Two reads of the
 //   row in all.
 //   General path (bin B holds more than CAP positions, e.g. massive ties): three
 //   radix passes over the row find T, then one ordered pass emits the set.
-//   Long rows first try a sampling path: 1024 strided samples, sorted in LDS,
-//   bracket the k-th largest key; one pass emits the keys above the bracket
-//   and collects the keys inside it (at most CAP), where T and the tie-break
-//   are resolved in LDS.  When the bracket misses, the paths above run.
+//   Long rows first try a sampling path: two order statistics of 1024 sampled
+//   keys (256 spread groups of 4) bracket the k-th largest key; one pass emits
+//   the keys above the bracket and collects the keys inside it (at most CAP),
+//   where T and the tie-break are resolved in LDS.  When the bracket misses, the paths above run.
 __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
   __shared__ uint32_t hist[HB];
   __shared__ uint32_t ckey[CAP];
   __shared__ int cpos[CAP];
-  __shared__ uint32_t part[256];
+  __shared__ uint32_t part[4];
   __shared__ uint32_t sel_info[4];
   __shared__ uint32_t wave_cnt[4];
   const int tid = threadIdx.x;
@@ -235,85 +260,134 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
   }
   const float* srow = p.sc + (int64_t)row * p.ld;
 
-  // ---- sampling path: bracket the k-th largest key with a sorted sample,
-  // then one pass over the row emits the keys above the bracket and collects
-  // the keys inside it; the exact threshold is resolved in LDS.
+  // ---- sampling path: bracket the k-th largest key with two order
+  // statistics of a sample of 256 spread groups of 4 adjacent keys, then one
+  // pass over the row emits the keys above the bracket and collects the keys
+  // inside it; the exact threshold is resolved in LDS.
   if (n >= 4 * NS) {
     uint32_t* skey = hist;  // the sample lives in the histogram space
-    for (int i = tid; i < NS; i += 256) skey[i] = okey(srow[(int64_t)i * n / NS]);
+    {
+      // 256 aligned groups of 4 adjacent keys (one 16-byte load per thread,
+      // 256 cache lines of the row)
+      const int u = (int)(((int64_t)tid * (n - 4) / 255) & ~3ll);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(srow + u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) skey[4 * tid + j] = okey(x[j]) >> 16;
+    }
     if (tid == 0) sel_info[2] = sel_info[3] = 0;
     __syncthreads();
-    // bitonic sort, descending
-    for (int size = 2; size <= NS; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < NS / 2; i += 256) {
-          const int lo_i = 2 * i - (i & (stride - 1));
-          const int hi_i = lo_i + stride;
-          const uint32_t x = skey[lo_i], y = skey[hi_i];
-          const bool desc = (lo_i & size) == 0;
-          if (desc ? x < y : x > y) {
-            skey[lo_i] = y;
-            skey[hi_i] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
+    // Bracket the k-th largest key between two order statistics of the
+    // 1024-key sample (ranks r -+ delta, about 3.5 standard deviations of the sample
+    // rank of the row's k-th key), on the top 16 key bits: a coarser bracket
+    // stays correct, it only admits a few more candidates.  One wave per
+    // statistic bisects over the whole sample (16 keys per lane, counts by
+    // ballot): the largest T with #(sample >= T) >= rank + 1 is the sample key
+    // of that rank (0 = largest).
     const int r = (int)((int64_t)k * NS / n);
-    const int delta = (int)(4.f * sqrtf((float)r * (1.f - (float)r / NS))) + 8;
-    const uint32_t hi = r - delta >= 0 ? skey[r - delta] : 0xffffffffu;  // keys > hi are in
-    const uint32_t lo = r + delta < NS ? skey[r + delta] : 0u;           // keys < lo are out
-    __syncthreads();
+    const int delta = (int)(3.5f * sqrtf((float)r * (1.f - (float)r / NS))) + 6;
+    uint32_t hi = 0xffffffffu, lo = 0u;  // keys > hi are in, keys < lo are out
+    {
+      // wave 0 finds the upper statistic, wave 1 the lower one
+      const int lane = tid & 63, wv = tid >> 6;
+      if (wv < 2) {
+        uint32_t sv[NS / 64];
+#pragma unroll
+        for (int j = 0; j < NS / 64; ++j) sv[j] = skey[lane + 64 * j];
+        const int rank = wv == 0 ? r - delta : r + delta;
+        uint32_t res = 0xffffffffu;
+        if (rank >= 0 && rank < NS) {
+          uint32_t t = 0;
+          for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t cand = t | (1u << bit);
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int j = 0; j < NS / 64; ++j) cnt += (uint32_t)__popcll(__ballot(sv[j] >= cand));
+            if (cnt >= (uint32_t)rank + 1) t = cand;
+          }
+          res = t;
+        }
+        if (lane == 0) wave_cnt[wv] = res;
+      }
+      lds_barrier();
+      if (wave_cnt[0] != 0xffffffffu) hi = (wave_cnt[0] << 16) | 0xffffu;
+      if (wave_cnt[1] != 0xffffffffu) lo = wave_cnt[1] << 16;
+      lds_barrier();
+    }
     {
       // Steps of 4096 elements: thread tid classifies elements
-      // base + 1024e + 4tid + j (e, j < 4) into bit masks, a workgroup prefix of
-      // the mask counts gives every flagged element its slot.
+      // base + 1024e + 4tid + j (bit 4e + j of its masks) with two float
+      // compares; a workgroup prefix of the mask counts gives every flagged
+      // element its slot.  The loads of step s+1 are issued before step s is
+      // classified.
+      const float f_above = hi == 0xffffffffu ? __uint_as_float(0x7fc00000u) : key_ge_float(hi + 1u);
+      const float f_in = key_ge_float(lo);
       uint32_t run_a = 0, run_i = 0;  // slots used so far (workgroup-uniform)
-      for (int base = 0; base < n; base += 4096) {
-        f32x4 v[4];
+      auto classify = [&](const f32x4 v0, const f32x4 v1, const f32x4 v2, const f32x4 v3, int base)
+                          __attribute__((always_inline)) {
+        const f32x4 v[4] = {v0, v1, v2, v3};
         uint32_t fa = 0, fi = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int u0 = base + 1024 * e + 4 * tid;
-          if (u0 + 3 < n) {
-            v[e] = *reinterpret_cast<const f32x4*>(srow + u0);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[e][j] = u0 + j < n ? srow[u0 + j] : 0.f;
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t key = okey(v[e][j]);
-            const bool valid = u0 + j < n;
-            const bool above = valid && key > hi;
-            const bool inside = valid && !above && key >= lo;
-            fa |= (uint32_t)above << (4 * e + j);
-            fi |= (uint32_t)inside << (4 * e + j);
-          }
-        }
-        uint32_t tot_a, tot_i;
-        const uint32_t oa = run_a + wg_prefix((uint32_t)__popc(fa), wave_cnt, tot_a);
-        const uint32_t oi = run_i + wg_prefix((uint32_t)__popc(fi), wave_cnt, tot_i);
-        uint32_t ra = 0, ri = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int u = base + 1024 * e + 4 * tid + j;
-            if ((fa >> (4 * e + j)) & 1u) {
-              if (oa + ra < (uint32_t)k) out[oa + ra] = u;
-              ++ra;
-            }
-            if ((fi >> (4 * e + j)) & 1u) {
-              if (oi + ri < (uint32_t)CAP) {
-                ckey[oi + ri] = okey(v[e][j]);
-                cpos[oi + ri] = u;
-              }
-              ++ri;
-            }
+            const float x = v[e][j];
+            const bool above = x >= f_above;
+            const bool in_or_above = x >= f_in;
+            fa |= (uint32_t)above << (4 * e + j);
+            fi |= (uint32_t)(in_or_above && !above) << (4 * e + j);
           }
-        run_a += tot_a;
-        run_i += tot_i;
+        uint32_t tot;
+        const uint32_t pre = wg_prefix2((uint32_t)__popc(fa) | ((uint32_t)__popc(fi) << 16), wave_cnt, tot);
+        uint32_t oa = run_a + (pre & 0xffffu), oi = run_i + (pre >> 16);
+        const int ub = base + 4 * tid;
+        // emit: one iteration per flagged element of this thread
+        for (uint32_t m = fa; m; m &= m - 1u) {
+          const int bit = __builtin_ctz(m);
+          if (oa < (uint32_t)k) out[oa] = ub + 1024 * (bit >> 2) + (bit & 3);
+          ++oa;
+        }
+        for (uint32_t m = fi; m; m &= m - 1u) {
+          const int bit = __builtin_ctz(m);
+          // select the element by the bits of its index (no dynamic register indexing)
+          const f32x4 h = (bit & 8) ? ((bit & 4) ? v3 : v2) : ((bit & 4) ? v1 : v0);
+          const float x = (bit & 2) ? ((bit & 1) ? h[3] : h[2]) : ((bit & 1) ? h[1] : h[0]);
+          if (oi < (uint32_t)CAP) {
+            ckey[oi] = okey(x);
+            cpos[oi] = ub + 1024 * (bit >> 2) + (bit & 3);
+          }
+          ++oi;
+        }
+        run_a += tot & 0xffffu;
+        run_i += tot >> 16;
+      };
+      // full steps: unguarded loads, those of step s+1 issued before step s
+      // is classified
+      const int n_full = n & ~4095;
+      auto load_full = [&](int base, f32x4 (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const f32x4*>(srow + base + 1024 * e + 4 * tid);
+      };
+      if (n_full > 0) {
+        f32x4 v[4], vn[4];
+        load_full(0, v);
+        for (int base = 0; base < n_full; base += 4096) {
+          if (base + 4096 < n_full) load_full(base + 4096, vn);
+          classify(v[0], v[1], v[2], v[3], base);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = vn[e];
+        }
+      }
+      if (n_full < n) {
+        // the partial step: keys past the row read as NaN, neither above nor inside
+        f32x4 v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int u = n_full + 1024 * e + 4 * tid + j;
+            v[e][j] = u < n ? srow[u] : __uint_as_float(0x7fc00000u);
+          }
+        classify(v[0], v[1], v[2], v[3], n_full);
       }
       if (tid == 0) {
         sel_info[2] = run_a;
@@ -326,7 +400,14 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       // exact threshold among the candidates: need-th largest key
       uint32_t need = (uint32_t)k - c_hi;
       uint32_t prefix = 0, pmask = 0;
-      for (int pass = 0; pass < 3; ++pass) {
+      // every candidate lies in [lo, hi]: bits they all share need no pass
+      int pass0 = 0;
+      if ((lo >> 21) == (hi >> 21)) {
+        prefix = hi & 0xffe00000u;
+        pmask = 0xffe00000u;
+        pass0 = 1;
+      }
+      for (int pass = pass0; pass < 3; ++pass) {
         const int sh = pass == 0 ? 21 : pass == 1 ? 10 : 0;
         const uint32_t nb = pass == 2 ? 1024u : 2048u;  // bits 31..21, 20..10, 9..0
         __syncthreads();
@@ -342,7 +423,9 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       }
       const uint32_t T = prefix;
       const uint32_t n_gt = (uint32_t)k - need;  // keys > T in the whole row
-      // candidates above T, and the number equal to T
+      // candidates above T go out directly; the slots of the candidates equal
+      // to T are listed in hist (free now), then their positions gathered
+      // into ckey[0, neq)
       __syncthreads();
       if (tid == 0) sel_info[2] = c_hi, sel_info[3] = 0;
       __syncthreads();
@@ -350,17 +433,41 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
         const int i = base + tid;
         const bool valid = i < (int)nc;
         const uint32_t key = valid ? ckey[i] : 0u;
-        const int pos = valid ? cpos[i] : 0;
         const bool gt = valid && key > T;
         const uint32_t sa = wave_alloc(gt, &sel_info[2]);
-        if (gt) out[sa] = pos;
+        if (gt) out[sa] = cpos[i];
         const bool eq = valid && key == T;
         const uint32_t se = wave_alloc(eq, &sel_info[3]);
-        // compact the tied positions into ckey; every slot written here is below
-        // base + 256, i.e. already read by its owner before this barrier
+        if (eq && se < (uint32_t)NB) hist[se] = (uint32_t)i;
+      }
+      __syncthreads();
+      if (sel_info[3] <= (uint32_t)NB) {
+        const uint32_t ne = sel_info[3];
+        uint32_t tp[CAP / 256];
+#pragma unroll
+        for (int j = 0; j < CAP / 256; ++j) {
+          const int i = tid + 256 * j;
+          tp[j] = i < (int)ne ? (uint32_t)cpos[hist[i]] : 0u;
+        }
         __syncthreads();
-        if (eq) ckey[se] = (uint32_t)pos;
+#pragma unroll
+        for (int j = 0; j < CAP / 256; ++j)
+          if (tid + 256 * j < (int)ne) ckey[tid + 256 * j] = tp[j];
+      } else {
+        // many ties: compact their positions in place, in steps of 256 (every
+        // slot written in a step is below its end, i.e. already read)
+        if (tid == 0) sel_info[3] = 0;
         __syncthreads();
+        for (int base = 0; base < (int)nc; base += 256) {
+          const int i = base + tid;
+          const bool valid = i < (int)nc;
+          const bool eq = valid && ckey[i] == T;
+          const int pos = valid ? cpos[i] : 0;
+          const uint32_t se = wave_alloc(eq, &sel_info[3]);
+          __syncthreads();
+          if (eq) ckey[se] = (uint32_t)pos;
+          __syncthreads();
+        }
       }
       __syncthreads();
       const uint32_t neq = sel_info[3];
@@ -400,7 +507,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     __syncthreads();
   }
 
-  // ---- pass 1: histogram of the top 12 bits
+  // ---- pass 1: histogram of the top 11 bits
   for (int i = tid; i < HB; i += 256) hist[i] = 0;
   if (tid == 0) sel_info[2] = 0;
   __syncthreads();
@@ -408,12 +515,12 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     const int n4 = n & ~3;
     for (int u = 4 * tid; u < n4; u += 1024) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(srow + u);
-      atomicAdd(&hist[okey(v[0]) >> 20], 1u);
-      atomicAdd(&hist[okey(v[1]) >> 20], 1u);
-      atomicAdd(&hist[okey(v[2]) >> 20], 1u);
-      atomicAdd(&hist[okey(v[3]) >> 20], 1u);
+      atomicAdd(&hist[okey(v[0]) >> 21], 1u);
+      atomicAdd(&hist[okey(v[1]) >> 21], 1u);
+      atomicAdd(&hist[okey(v[2]) >> 21], 1u);
+      atomicAdd(&hist[okey(v[3]) >> 21], 1u);
     }
-    for (int u = n4 + tid; u < n; u += 256) atomicAdd(&hist[okey(srow[u]) >> 20], 1u);
+    for (int u = n4 + tid; u < n; u += 256) atomicAdd(&hist[okey(srow[u]) >> 21], 1u);
   }
   __syncthreads();
   find_bin(hist, HB, (uint32_t)k, part, sel_info);
@@ -429,7 +536,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       uint32_t key = 0;
       const bool valid = u < n;
       if (valid) key = okey(srow[u]);
-      const uint32_t bin = key >> 20;
+      const uint32_t bin = key >> 21;
       if (valid && bin > B) out[atomicAdd(&sel_info[2], 1u)] = u;
       uint32_t tot;
       const bool inb = valid && bin == B;
@@ -441,20 +548,21 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       nc += tot;
     }
     __syncthreads();
-    // ---- resolve the threshold among the nc = in_b candidates (bits 19..0)
+    // ---- resolve the threshold among the nc = in_b candidates (bits 20..10, 9..0)
     uint32_t need = (uint32_t)k - above_b;
-    uint32_t prefix = B << 20, pmask = 0xfff00000u;
+    uint32_t prefix = B << 21, pmask = 0xffe00000u;
     for (int pass = 0; pass < 2; ++pass) {
       const int sh = pass == 0 ? 10 : 0;
-      for (int i = tid; i < 1024; i += 256) hist[i] = 0;
+      const uint32_t nb = pass == 0 ? 2048u : 1024u;
+      for (int i = tid; i < (int)nb; i += 256) hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < (int)nc; i += 256)
-        if ((ckey[i] & pmask) == prefix) atomicAdd(&hist[(ckey[i] >> sh) & 1023u], 1u);
+        if ((ckey[i] & pmask) == prefix) atomicAdd(&hist[(ckey[i] >> sh) & (nb - 1)], 1u);
       __syncthreads();
-      find_bin(hist, 1024, need, part, sel_info);
+      find_bin(hist, (int)nb, need, part, sel_info);
       need -= sel_info[1];
       prefix |= sel_info[0] << sh;
-      pmask |= 1023u << sh;
+      pmask |= (nb - 1) << sh;
       __syncthreads();
     }
     const uint32_t T = prefix;
