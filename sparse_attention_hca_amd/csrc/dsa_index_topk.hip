@@ -102,6 +102,92 @@ __global__ __launch_bounds__(256) void index_scores_kernel(ScoreParams p) {
   }
 }
 
+// Q-stationary variant for h_i * d_i / 2 <= 128: a wave keeps the B operands
+// of its 32 queries (all index heads, 128 floats per lane at most) in
+// registers and walks KG key tiles of 32, prefetching the next key tile's A
+// operand while the current one runs.  Each query block's Q is then read once
+// per KG key tiles instead of once per tile.  Two heads' MFMA chains are
+// interleaved so consecutive MFMAs are independent.
+constexpr int KG = 8;  // key tiles per wave
+
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int qt0 = blockIdx.y * QT;                  // first query (chunk-relative)
+  const int t0 = p.r0 + qt0;                        // absolute position
+  const int t_last = min(t0 + QT, p.r0 + p.rows) - 1;
+  const int kbase = (blockIdx.x * WAVES + w) * (KG * KT);
+  if (kbase > t_last) return;                       // keys all in the future of every query
+  const int col = lane & 31, hf = lane >> 5;
+  constexpr int HALF = DI / 2;
+
+  // B operands: this lane's query, d in [hf*HALF, hf*HALF + HALF), every head
+  const int tq = min(t0 + col, p.seqlen - 1);
+  float qb[HI][HALF];
+  float wq[HI];
+#pragma unroll
+  for (int h = 0; h < HI; ++h) {
+    const float* qsrc = p.qI + ((int64_t)tq * HI + h) * DI + hf * HALF;
+#pragma unroll
+    for (int i = 0; i < HALF; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(qsrc + i);
+      qb[h][i] = v[0]; qb[h][i + 1] = v[1]; qb[h][i + 2] = v[2]; qb[h][i + 3] = v[3];
+    }
+    wq[h] = p.w[(int64_t)tq * HI + h];
+  }
+  // A operand of key tile kt: this lane's key row
+  auto load_k = [&](int kt, float (&ka)[HALF]) __attribute__((always_inline)) {
+    const int key = min(kbase + kt * KT + col, p.seqlen - 1);
+    const float* src = p.kI + (int64_t)key * DI + hf * HALF;
+#pragma unroll
+    for (int i = 0; i < HALF; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
+      ka[i] = v[0]; ka[i + 1] = v[1]; ka[i + 2] = v[2]; ka[i + 3] = v[3];
+    }
+  };
+  const int n_kt = min(KG, (t_last - kbase) / KT + 1);
+  const int qrow = qt0 + col;
+  float ka[HALF], kn[HALF];
+  load_k(0, ka);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    if (kt + 1 < n_kt) load_k(kt + 1, kn);
+    f32x16_t score;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) score[r] = 0.f;
+#pragma unroll
+    for (int h = 0; h < HI; h += 2) {
+      f32x16_t a0, a1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a0[r] = a1[r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) {
+        a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[i], qb[h][i], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[i], qb[h + 1][i], a1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        score[r] = fmaf(wq[h], fmaxf(a0[r], 0.f), score[r]);
+        score[r] = fmaf(wq[h + 1], fmaxf(a1[r], 0.f), score[r]);
+      }
+    }
+    // lane holds query col, keys 8*(r/4) + 4*hf + (r%4) of the tile
+    const int k0 = kbase + kt * KT;
+    if (qrow < p.rows) {
+      float* dst = p.sc + (int64_t)qrow * p.ld + k0 + 4 * hf;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int kk = k0 + 8 * rg + 4 * hf;
+        if (kk < p.seqlen) {  // ld is a multiple of 4 and >= seqlen rounded up to 4
+          f32x4 v = f32x4{score[4 * rg], score[4 * rg + 1], score[4 * rg + 2], score[4 * rg + 3]};
+          *reinterpret_cast<f32x4*>(dst + 8 * rg) = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) ka[i] = kn[i];
+  }
+}
+
 // Order-preserving map float -> uint32 (larger float -> larger key); -0 -> +0.
 __device__ __forceinline__ uint32_t okey(float f) {
   uint32_t u = __float_as_uint(f);
@@ -626,8 +712,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
 }
 
 int chunk_rows(int seqlen) {
-  // keep one chunk of scores near 256 MB
-  int64_t r = ((int64_t)1 << 26) / (((int64_t)seqlen + 3) & ~3ll);
+  // keep one chunk of scores near 1 GB: few, large launches fill the GPU
+  int64_t r = ((int64_t)1 << 28) / (((int64_t)seqlen + 3) & ~3ll);
   if (r < 32) r = 32;
   r = r / 32 * 32;
   if (r > seqlen) r = ((seqlen + 31) / 32) * 32;
@@ -664,7 +750,16 @@ hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* 
       sp.rows = rows;
       const int key_tiles = (r0 + rows + KT * WAVES - 1) / (KT * WAVES);
       dim3 grid(key_tiles, (rows + QT - 1) / QT);
-      switch (d_i) {
+      const dim3 grid_qs((r0 + rows + KT * WAVES * KG - 1) / (KT * WAVES * KG), (rows + QT - 1) / QT);
+      bool qs = true;
+      if (h_i == 4 && d_i == 16) hipLaunchKernelGGL((index_scores_qs_kernel<16, 4>), grid_qs, dim3(256), 0, st, sp);
+      else if (h_i == 4 && d_i == 32) hipLaunchKernelGGL((index_scores_qs_kernel<32, 4>), grid_qs, dim3(256), 0, st, sp);
+      else if (h_i == 4 && d_i == 48) hipLaunchKernelGGL((index_scores_qs_kernel<48, 4>), grid_qs, dim3(256), 0, st, sp);
+      else if (h_i == 4 && d_i == 64) hipLaunchKernelGGL((index_scores_qs_kernel<64, 4>), grid_qs, dim3(256), 0, st, sp);
+      else if (h_i == 8 && d_i == 16) hipLaunchKernelGGL((index_scores_qs_kernel<16, 8>), grid_qs, dim3(256), 0, st, sp);
+      else if (h_i == 8 && d_i == 32) hipLaunchKernelGGL((index_scores_qs_kernel<32, 8>), grid_qs, dim3(256), 0, st, sp);
+      else qs = false;
+      if (!qs) switch (d_i) {
         case 16: hipLaunchKernelGGL(index_scores_kernel<16>, grid, dim3(256), 0, st, sp); break;
         case 32: hipLaunchKernelGGL(index_scores_kernel<32>, grid, dim3(256), 0, st, sp); break;
         case 48: hipLaunchKernelGGL(index_scores_kernel<48>, grid, dim3(256), 0, st, sp); break;
