@@ -149,6 +149,15 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
   const int qrow = qt0 + col;
   float ka[HALF], kn[HALF];
   load_k(0, ka);
+  // settle the prologue loads here: otherwise the loop's waits, placed for its
+  // first iteration, would also hold every later iteration until the next
+  // tile's prefetch has landed
+#pragma unroll
+  for (int h = 0; h < HI; ++h)
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) asm volatile("" ::"v"(qb[h][i]));
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) asm volatile("" ::"v"(ka[i]));
   for (int kt = 0; kt < n_kt; ++kt) {
     if (kt + 1 < n_kt) load_k(kt + 1, kn);
     f32x16_t score;
