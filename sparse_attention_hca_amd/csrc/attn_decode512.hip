@@ -252,26 +252,34 @@ __global__ __launch_bounds__(256) void decode512_combine(DecodeParams p) {
   const int kvh = hq / p.group, hl = hq % p.group;
   const int hg = hl / HG, col = hl % HG;
   const int64_t part0 = (((int64_t)b * a.h_kv + kvh) * p.n_hg + hg) * p.nsplit;
+  const float* ml = p.ws_ml + (part0 * HG + col) * 2;  // split s at ml[2 * HG * s]
+  const float* po = p.ws_o + part0 * HG * D + (int64_t)col * D + 2 * threadIdx.x;  // split s at po[HG * D * s]
   float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.ws_ml[((part0 + s) * HG + col) * 2]);
-  float Lsum = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float* ml = p.ws_ml + ((part0 + s) * HG + col) * 2;
-    Lsum += ml[1] * (ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - M));
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, ml[2 * HG * s]);
+  // splits four at a time: their loads are issued together
+  float Lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < p.nsplit; s0 += 4) {
+    float m[4], l[4], x[4], y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = s0 + j < p.nsplit ? s0 + j : s0;
+      m[j] = ml[2 * HG * s];
+      l[j] = ml[2 * HG * s + 1];
+      const float2 v = *reinterpret_cast<const float2*>(po + (int64_t)HG * D * s);
+      x[j] = v.x;
+      y[j] = v.y;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float wgt = (s0 + j < p.nsplit && m[j] != -INFINITY) ? exp2f(m[j] - M) : 0.f;
+      Lsum = fmaf(l[j], wgt, Lsum);
+      o0 = fmaf(wgt, x[j], o0);
+      o1 = fmaf(wgt, y[j], o1);
+    }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   uint16_t* op = (uint16_t*)a.o + b * a.so.b + (int64_t)hq * a.so.h;
-  for (int e = threadIdx.x * 2; e < D; e += 512) {
-    float o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float m = p.ws_ml[((part0 + s) * HG + col) * 2];
-      const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
-      const float* src = p.ws_o + ((part0 + s) * HG + col) * D + e;
-      o0 = fmaf(wgt, src[0], o0);
-      o1 = fmaf(wgt, src[1], o1);
-    }
-    *reinterpret_cast<uint32_t*>(op + e) = pack_bf16x2(o0 * inv, o1 * inv);
-  }
+  *reinterpret_cast<uint32_t*>(op + 2 * threadIdx.x) = pack_bf16x2(o0 * inv, o1 * inv);
   if (a.lse && threadIdx.x == 0) a.lse[(int64_t)b * a.h_q + hq] = M * kLn2 + __logf(Lsum);
 }
 
