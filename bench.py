@@ -178,7 +178,24 @@ def bench_decode(torch, hca, synth, cfg, steps, warmup):
     for _ in range(steps):
         tm(f)
     res = {"ms": tm.mean_ms()}
-    del q, kc, vc, kw, vw, o, ws
+    # decode-time cache upkeep: one append per token (ring write), plus the
+    # block compression on the token that closes a block.  These calls are
+    # tiny, so the event-bracketed time is host-bound (argument marshalling
+    # and launch); the kernel-trace profile gives the kernels' own durations.
+    k_ring = torch.zeros((cfg.batch, 2 * cfg.window, cfg.h_kv, cfg.head_dim), dtype=q.dtype, device="cuda:0")
+    v_ring = torch.zeros_like(k_ring)
+    w = torch.full((cfg.h_kv, cfg.block), 1.0 / cfg.block, dtype=torch.float32, device="cuda:0")
+    t_close = cfg.block * cfg.n_blocks - 1
+    t_open = t_close - 1
+    for t, key in ((t_open, "append_call_us"), (t_close, "append_close_call_us")):
+        g = lambda: hca.hca_append_kv(kw[:, :1], vw[:, :1], k_ring, v_ring, t, cfg.block, w, w, kc, vc)
+        for _ in range(warmup):
+            g()
+        ta = Timer(torch)
+        for _ in range(steps):
+            ta(g)
+        res[key] = ta.mean_ms() * 1e3
+    del q, kc, vc, kw, vw, o, ws, k_ring, v_ring
     torch.cuda.empty_cache()
     return res
 
@@ -309,6 +326,7 @@ def main():
         comps["hca_decode_1m"] = {
             "ms": r4["ms"], "gbs": b4 / r4["ms"] / 1e6, "hbm_frac": b4 / r4["ms"] / 1e6 / PEAK_HBM_GBS,
             "tokens_per_s": c4.batch / r4["ms"] * 1e3, "tflops": f4 / r4["ms"] / 1e9,
+            "append_call_us": r4["append_call_us"], "append_close_call_us": r4["append_close_call_us"],
         }
         log(f"[bench] c4 done: {comps['hca_decode_1m']}")
     if "c5" in only:

@@ -87,6 +87,45 @@ hca_status_t hca_compress_kv(hca_dtype_t dt,
                              void* stream);
 
 /*
+ * hca_append_kv -- decode-time upkeep of the HCA caches (mirrorspeed page,
+ * "Hybrid sparse attention" section: every 128 tokens become one cache entry
+ * while the most recent tokens stay uncompressed).  Appends the K/V row of
+ * position t (the same t for every sequence of the batch) to a mirrored ring
+ * of raw rows and, when t closes a block, compresses that block:
+ *     k_ring[b, t mod R, h, :] = k_ring[b, t mod R + R, h, :] = k_new[b, 0, h, :]
+ *     (v_ring likewise), and if (t + 1) % block == 0, with j = (t + 1) / block - 1:
+ *     kc[b, j, h, :] = sum_{i < block} w_k[h, i] * (ring row of position t + 1 - block + i)
+ *     vc[b, j, h, :] likewise with w_v
+ * in fp32, stored in `dt` -- the same values hca_compress_kv gives for block j
+ * of the whole history.  The rows of positions lo .. t (t - lo < R) sit
+ * contiguously at ring rows lo mod R .. lo mod R + (t - lo), so a decode
+ * query at t reads its window straight from the ring: hca_attn_fwd with
+ * k = k_ring + (lo mod R) rows, kv_pos0 = lo, seqlen_kv = t - lo + 1.
+ *   k_new, v_new : [batch, 1, h_kv, head_dim] (read)
+ *   k_ring, v_ring: [batch, 2 * ring, h_kv, head_dim] (two rows written; when a
+ *                   block closes its rows are read back -- positions
+ *                   t + 1 - block .. t - 1 must have been appended before)
+ *   w_k, w_v     : [h_kv, block] fp32 contiguous (read when a block closes)
+ *   kc, vc       : [batch, n_blocks, h_kv, head_dim] (row j written when block j
+ *                   closes; may be NULL otherwise)
+ * Errors: HCA_ERR_INVALID when ring < block, when t closes a block j >=
+ * n_blocks, or when the rings overlap each other, the new rows or kc/vc.
+ * Supported: head_dim in {64, 128, 256, 512}.
+ */
+hca_status_t hca_append_kv(hca_dtype_t dt,
+                           const void* k_new, hca_strides_t sk_new,
+                           const void* v_new, hca_strides_t sv_new,
+                           void* k_ring, hca_strides_t sk_ring,
+                           void* v_ring, hca_strides_t sv_ring,
+                           int ring,
+                           const float* w_k, const float* w_v,
+                           void* kc, hca_strides_t skc,
+                           void* vc, hca_strides_t svc,
+                           int n_blocks, int64_t t,
+                           int batch, int h_kv, int head_dim, int block,
+                           void* stream);
+
+/*
  * Workspace bytes hca_attn_fwd needs for these sizes (0 when none is needed).
  * n_blocks and window are the values that will be passed to hca_attn_fwd.
  */

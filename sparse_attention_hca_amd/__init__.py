@@ -26,7 +26,7 @@ HCA_OK, HCA_ERR_INVALID, HCA_ERR_UNSUPPORTED, HCA_ERR_WORKSPACE, HCA_ERR_HIP = r
 HCA_DTYPE_F32, HCA_DTYPE_BF16 = 0, 1
 
 EXPORTS = (
-    "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_attn_fwd_workspace_size",
+    "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd", "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
 )
 
@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hca_last_error.argtypes = []
     lib.hca_compress_kv.restype = I
     lib.hca_compress_kv.argtypes = [I, P, S, P, S, P, P, P, S, P, S, I, I, I, I, I, P]
+    lib.hca_append_kv.restype = I
+    lib.hca_append_kv.argtypes = [I, P, S, P, S, P, S, P, S, I, P, P, P, S, P, S, I, I64, I, I, I, I, P]
     lib.hca_attn_fwd_workspace_size.restype = SZ
     lib.hca_attn_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.hca_attn_fwd.restype = I
@@ -133,6 +135,27 @@ def hca_compress_kv(k: torch.Tensor, v: torch.Tensor, w_k: torch.Tensor, w_v: to
     _check(lib.hca_compress_kv(_dt(k), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(w_k), _ptr(w_v),
                                _ptr(kc), _strides(kc), _ptr(vc), _strides(vc), B, S, H, d, block, _stream()))
     return kc, vc
+
+
+def hca_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_ring: torch.Tensor, v_ring: torch.Tensor,
+                  t: int, block: int, w_k: Optional[torch.Tensor] = None, w_v: Optional[torch.Tensor] = None,
+                  kc: Optional[torch.Tensor] = None, vc: Optional[torch.Tensor] = None) -> None:
+    """Append the K/V rows of position t ([B, 1, H_kv, d]) to the mirrored rings ([B, 2R, H_kv, d]);
+    when t closes a block, write its compressed row into kc/vc ([B, n_blocks, H_kv, d])."""
+    lib = load_library()
+    _dev(k_new, v_new, k_ring, v_ring)
+    B, _, H, d = k_new.shape
+    ring = k_ring.shape[1] // 2
+    n_blocks = 0 if kc is None else kc.shape[1]
+    if w_k is not None:
+        w_k = w_k.contiguous()
+    if w_v is not None:
+        w_v = w_v.contiguous()
+    _check(lib.hca_append_kv(_dt(k_new), _ptr(k_new), _strides(k_new), _ptr(v_new), _strides(v_new),
+                             _ptr(k_ring), _strides(k_ring), _ptr(v_ring), _strides(v_ring), ring,
+                             _ptr(w_k), _ptr(w_v), _ptr(kc), _strides(kc) if kc is not None else Strides(0, 0, 0),
+                             _ptr(vc), _strides(vc) if vc is not None else Strides(0, 0, 0), n_blocks, t,
+                             B, H, d, block, _stream()))
 
 
 def hca_attn_fwd_workspace_size(batch: int, seqlen_q: int, h_q: int, h_kv: int, head_dim: int,
@@ -217,6 +240,7 @@ def dsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: 
 
 __all__ = [
     "load_library", "HcaError", "Strides", "EXPORTS",
-    "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_attn_fwd_workspace_size", "hca_attn_fwd",
+    "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
+    "hca_attn_fwd",
     "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
 ]

@@ -17,6 +17,7 @@ ARCH = os.environ.get("HCA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = [
     "compress.hip",
+    "append.hip",
     "attn_generic.hip",
     "attn_prefill512.hip",
     "attn_decode512.hip",

@@ -104,6 +104,65 @@ hca_status_t hca_compress_kv(hca_dtype_t dt, const void* k, hca_strides_t sk, co
   return HCA_OK;
 }
 
+hca_status_t hca_append_kv(hca_dtype_t dt, const void* k_new, hca_strides_t skn, const void* v_new,
+                           hca_strides_t svn, void* k_ring, hca_strides_t skr, void* v_ring, hca_strides_t svr,
+                           int ring, const float* w_k, const float* w_v, void* kc, hca_strides_t skc, void* vc,
+                           hca_strides_t svc, int n_blocks, int64_t t, int batch, int h_kv, int head_dim, int block,
+                           void* stream) {
+  if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (batch <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0 || ring <= 0 || n_blocks < 0)
+    return fail(HCA_ERR_INVALID, "sizes must be positive (batch %d h_kv %d head_dim %d block %d ring %d n_blocks %d)",
+                batch, h_kv, head_dim, block, ring, n_blocks);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(HCA_ERR_UNSUPPORTED, "hca_append_kv: head_dim %d not in {64,128,256,512}", head_dim);
+  if (ring < block) return fail(HCA_ERR_INVALID, "hca_append_kv: ring (%d) must hold a whole block (%d)", ring, block);
+  if (t < 0) return fail(HCA_ERR_INVALID, "position must be >= 0");
+  if (t >= kPosLimit) return fail(HCA_ERR_UNSUPPORTED, "positions beyond 2^30 are not supported");
+  const bool closes = (t + 1) % block == 0;
+  const int64_t j = (t + 1) / block - 1;
+  if (closes && j >= n_blocks)
+    return fail(HCA_ERR_INVALID, "hca_append_kv: position %lld closes block %lld but kc/vc hold %d blocks",
+                (long long)t, (long long)j, n_blocks);
+  if (closes && (!w_k || !w_v)) return fail(HCA_ERR_INVALID, "compressor weights are NULL");
+  const size_t es = elem_size(dt);
+  HCA_TRY(check_tensor("k_new", k_new, skn, es));
+  HCA_TRY(check_tensor("v_new", v_new, svn, es));
+  HCA_TRY(check_tensor("k_ring", k_ring, skr, es));
+  HCA_TRY(check_tensor("v_ring", v_ring, svr, es));
+  HCA_TRY(check_tensor("kc", kc, skc, es, !closes));
+  HCA_TRY(check_tensor("vc", vc, svc, es, !closes));
+  {
+    const Range rkn = extent(k_new, skn, batch, 1, h_kv, head_dim, es), rvn = extent(v_new, svn, batch, 1, h_kv, head_dim, es);
+    const Range rkr = extent(k_ring, skr, batch, 2 * (int64_t)ring, h_kv, head_dim, es);
+    const Range rvr = extent(v_ring, svr, batch, 2 * (int64_t)ring, h_kv, head_dim, es);
+    if (overlaps(rkr, rvr) || overlaps(rkr, rkn) || overlaps(rkr, rvn) || overlaps(rvr, rkn) || overlaps(rvr, rvn))
+      return fail(HCA_ERR_INVALID, "hca_append_kv: the rings overlap each other or the new rows");
+    if (closes) {
+      const Range rkc = extent(kc, skc, batch, n_blocks, h_kv, head_dim, es);
+      const Range rvc = extent(vc, svc, batch, n_blocks, h_kv, head_dim, es);
+      if (overlaps(rkc, rvc) || overlaps(rkc, rkr) || overlaps(rkc, rvr) || overlaps(rvc, rkr) || overlaps(rvc, rvr))
+        return fail(HCA_ERR_INVALID, "hca_append_kv: kc/vc overlap each other or the rings");
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int idt = dt == HCA_DTYPE_BF16 ? 1 : 0;
+  hipError_t e = hca::launch_ring_write(idt, k_new, ls(skn), v_new, ls(svn), k_ring, ls(skr), v_ring, ls(svr), ring, t,
+                                        batch, h_kv, head_dim, st);
+  if (e != hipSuccess) return hip_fail(e, "hca_append_kv ring write");
+  if (closes) {
+    // rows t+1-block .. t are contiguous in the mirrored ring from row (t+1-block) mod ring
+    const int64_t start = (t + 1 - block) % ring;
+    const char* kb = (const char*)k_ring + start * skr.seq * (int64_t)es;
+    const char* vb = (const char*)v_ring + start * svr.seq * (int64_t)es;
+    char* kcj = (char*)kc + j * skc.seq * (int64_t)es;
+    char* vcj = (char*)vc + j * svc.seq * (int64_t)es;
+    e = hca::launch_compress(idt, kb, ls(skr), w_k, kcj, ls(skc), vb, ls(svr), w_v, vcj, ls(svc), batch, block, h_kv,
+                             head_dim, block, st);
+    if (e != hipSuccess) return hip_fail(e, "hca_append_kv block compression");
+  }
+  return HCA_OK;
+}
+
 static int n_keys_of(int64_t t, int window, int block) {
   const int64_t lo = t - window + 1 > 0 ? t - window + 1 : 0;
   return (int)(lo / block + (t - lo + 1));

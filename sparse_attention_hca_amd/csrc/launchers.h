@@ -30,6 +30,12 @@ hipError_t launch_compress(int dt, const void* x, LStrides sx, const float* w, v
                            const void* x2, LStrides sx2, const float* w2, void* out2, LStrides so2,
                            int batch, int seqlen, int h, int d, int block, hipStream_t st);
 
+// Writes the K/V row of position t into rows t mod ring and t mod ring + ring
+// of the raw-row rings.
+hipError_t launch_ring_write(int dt, const void* k_new, LStrides skn, const void* v_new, LStrides svn, void* k_ring,
+                             LStrides skr, void* v_ring, LStrides svr, int ring, int64_t t, int batch, int h_kv,
+                             int head_dim, hipStream_t st);
+
 // One workgroup per (query, head): any dtype, head_dim <= 512, keys per query <= kGenericMaxKeys.
 constexpr int kGenericMaxKeys = 16384;
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t st);

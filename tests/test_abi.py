@@ -40,6 +40,30 @@ def _lib():
     return hca.load_library()
 
 
+def test_append_rejects_bad_arguments():
+    lib = _lib()
+    ring_k, ring_v = ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31)
+    kc, vc = ctypes.c_void_p(1 << 32), ctypes.c_void_p(1 << 33)
+
+    def st(**kw):
+        return lib.hca_append_kv(kw.get("dt", 1), kw.get("kn", FAKE), S(0, 512, 512), FAKE, S(0, 512, 512),
+                                 kw.get("kr", ring_k), S(0, 512, 512), ring_v, S(0, 512, 512), kw.get("ring", 128),
+                                 kw.get("wk", FAKE), FAKE, kc, S(0, 512, 512), vc, S(0, 512, 512),
+                                 kw.get("nb", 4), kw.get("t", 127), 1, 1, kw.get("d", 512), kw.get("block", 128),
+                                 None)
+    assert st(dt=5) == hca.HCA_ERR_INVALID
+    assert st(ring=64) == hca.HCA_ERR_INVALID                  # the ring cannot hold a block
+    assert "whole block" in hca.hca_last_error()
+    assert st(t=5 * 128 - 1) == hca.HCA_ERR_INVALID            # closes block 4, kc holds 4
+    assert st(t=-1) == hca.HCA_ERR_INVALID
+    assert st(d=96) == hca.HCA_ERR_UNSUPPORTED
+    assert st(kn=None) == hca.HCA_ERR_INVALID
+    assert st(wk=None) == hca.HCA_ERR_INVALID                  # t = 127 closes block 0
+    assert st(kr=ring_v) == hca.HCA_ERR_INVALID                # the two rings alias
+    assert "overlap" in hca.hca_last_error()
+    assert st(t=1 << 31) == hca.HCA_ERR_UNSUPPORTED
+
+
 def test_compress_rejects_bad_arguments():
     lib = _lib()
     st = lambda **kw: lib.hca_compress_kv(kw.get("dt", 1), kw.get("k", FAKE), kw.get("sk", S(0, 512, 512)),

@@ -263,6 +263,63 @@ def test_decode_equals_prefill_row():
         assert float((ld[..., 0] - lse[..., t]).abs().max()) < 1e-3
 
 
+# ------------------------------------------------------------------ decode-time cache upkeep
+
+APPEND_CASES = [
+    # dtype, d, Hq, Hkv, window, ring
+    ("bf16", 512, 16, 1, 128, 128),    # the decode configuration's shape, ring = window = block
+    ("bf16", 512, 4, 2, 64, 160),      # ring larger than the block, window not a multiple of it
+    ("f32", 128, 2, 2, 100, 128),      # fp32 caches (compressor and generic attention)
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,W,R", APPEND_CASES)
+def test_append_streams_history(dtype, d, Hq, Hkv, W, R):
+    """Positions 0..T-1 appended one at a time: the ring window equals the
+    last rows exactly, every closed block equals hca_compress_kv over the whole
+    history bit for bit (same kernel, same block) and the oracle within the
+    compression tolerance, and decode attention read from the ring matches
+    the oracle at several positions."""
+    T = 3 * 128 + 45
+    cfg = synth.small_prefill("c2" if dtype == "bf16" else "c1", name="append", dtype=dtype, seqlen=T, h_q=Hq,
+                              h_kv=Hkv, head_dim=d, window=W, block=128, batch=2)
+    _say("append", cfg, R)
+    inp = synth.make_prefill(cfg)
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    B, nb = cfg.batch, T // 128
+    k_ring = torch.zeros((B, 2 * R, Hkv, d), dtype=k.dtype, device=k.device)
+    v_ring = torch.zeros_like(k_ring)
+    kc = torch.zeros((B, nb, Hkv, d), dtype=k.dtype, device=k.device)
+    vc = torch.zeros_like(kc)
+    rk = oracle.compress_kv(f64(inp["k"], inp["bf16"]), inp["w"], 128)
+    rv = oracle.compress_kv(f64(inp["v"], inp["bf16"]), inp["w"], 128)
+    checks = {0, 1, 63, 100, 127, 128, 129, 255, 256, 300, T - 1}
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    for t in range(T):
+        hca.hca_append_kv(k[:, t:t + 1], v[:, t:t + 1], k_ring, v_ring, t, 128, w, w, kc, vc)
+        if t not in checks:
+            continue
+        torch.cuda.synchronize()
+        lo = max(0, t - W + 1)
+        s0, n = lo % R, t - lo + 1
+        assert torch.equal(k_ring[:, s0:s0 + n], k[:, lo:t + 1]) and torch.equal(v_ring[:, s0:s0 + n], v[:, lo:t + 1])
+        o, lse = hca.hca_attn_fwd(q[:, t:t + 1], k_ring[:, s0:s0 + n], v_ring[:, s0:s0 + n], kc, vc, window=W,
+                                  block=128, scale=cfg.scale, q_pos0=t, kv_pos0=lo)
+        torch.cuda.synchronize()
+        ro, rlse = oracle.hca_attention(f64(inp["q"][:, t:t + 1], inp["bf16"]), f64(inp["k"][:, :t + 1], inp["bf16"]),
+                                        f64(inp["v"][:, :t + 1], inp["bf16"]), rk, rv, window=W, block=128,
+                                        scale=cfg.scale, q_pos0=t, kv_pos0=0)
+        err = rel_err(host(o), ro)
+        _say(f"  t={t} decode rel err {err:.3e}")
+        assert err < tol
+        assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+    kc_full, vc_full = hca.hca_compress_kv(k, v, w, w, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc_full) and torch.equal(vc, vc_full)
+    assert rel_err(host(kc), rk) < tol and rel_err(host(vc), rv) < tol
+
+
 # ------------------------------------------------------------------ full-size configurations, sampled
 
 def _sample_rows(S, W, n=24, seed=0):
