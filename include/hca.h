@@ -198,6 +198,35 @@ hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float*
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Workspace bytes dsa_index_topk_decode needs (one score row per sequence plus
+ * the two-stage selection's candidates). */
+size_t dsa_index_topk_decode_workspace_size(int batch, int n_keys, int topk);
+
+/*
+ * dsa_index_topk_decode -- the DSA indexer and top-k for one new query per
+ * sequence (mirrorspeed page, "Hybrid sparse attention" section: the indexer
+ * scores the historical positions of each query, so the per-query attention
+ * cost stops growing with the context).  The query of sequence b sits at
+ * position n_keys - 1 and sees keys 0 .. n_keys - 1:
+ *   s(u) = sum_{h < h_i} w_idx[b,0,h] * max(0, <q_idx[b,0,h,:], k_idx[b,u,:]>)
+ * in fp32; idx[b,0,:] receives the min(n_keys, topk) positions with the largest
+ * s (ties: the smaller position wins; -0 counts as +0) in unspecified order,
+ * then -1 padding -- the same set dsa_index_topk gives for row n_keys - 1.
+ * Rows longer than 65536 keys are selected in two exact stages (each 65536-key
+ * segment, then the segments' winners).
+ *   q_idx: [batch, 1, h_i, d_i] fp32 contiguous (read)
+ *   k_idx: [batch, n_keys, d_i] fp32 contiguous (read)
+ *   w_idx: [batch, 1, h_i]      fp32 contiguous (read)
+ *   idx  : [batch, 1, topk]     int32 contiguous (written)
+ * Supported: h_i in {4, 8}, d_i a multiple of 16 and <= 128, topk <= 4096,
+ * n_keys < 2^30.
+ */
+hca_status_t dsa_index_topk_decode(const float* q_idx, const float* k_idx, const float* w_idx,
+                                   int32_t* idx,
+                                   int batch, int n_keys, int h_i, int d_i, int topk,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /*
  * dsa_sparse_attn_fwd -- DSA core attention over the selected positions
  * (mirrorspeed page, "Hybrid sparse attention" section; 256-wide heads per
@@ -222,6 +251,28 @@ hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt,
                                  int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v,
                                  int topk, float scale,
                                  void* stream);
+
+/*
+ * dsa_sparse_attn_decode -- DSA core attention for one query per sequence
+ * over a key history of n_keys rows (mirrorspeed page, "Hybrid sparse
+ * attention" section).  For head h, g = h / (h_q / h_kv):
+ *   o[b,0,h,:] = sum_{u in idx[b,0,:], u >= 0} softmax_u(scale * <q[b,0,h], k[b,u,g]>) * v[b,u,g,:]
+ * with the same conventions as dsa_sparse_attn_fwd (every listed position in
+ * [0, n_keys), else the row is written as NaN).
+ *   q: [batch, 1, h_q, d_qk]; k: [batch, n_keys, h_kv, d_qk]; v: [batch, n_keys, h_kv, d_v];
+ *   idx: [batch, 1, topk] int32 contiguous; o: [batch, 1, h_q, d_v]; lse: [batch, h_q] fp32 or NULL.
+ * Supported: as dsa_sparse_attn_fwd.
+ */
+hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
+                                    const void* q, hca_strides_t sq,
+                                    const void* k, hca_strides_t sk,
+                                    const void* v, hca_strides_t sv,
+                                    const int32_t* idx,
+                                    void* o, hca_strides_t so,
+                                    float* lse,
+                                    int batch, int n_keys, int h_q, int h_kv, int d_qk, int d_v,
+                                    int topk, float scale,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ HCA_DTYPE_F32, HCA_DTYPE_BF16 = 0, 1
 EXPORTS = (
     "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd", "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
+    "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
 )
 
 
@@ -73,6 +74,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, P, SZ, P]
     lib.dsa_sparse_attn_fwd.restype = I
     lib.dsa_sparse_attn_fwd.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
+    lib.dsa_index_topk_decode_workspace_size.restype = SZ
+    lib.dsa_index_topk_decode_workspace_size.argtypes = [I, I, I]
+    lib.dsa_index_topk_decode.restype = I
+    lib.dsa_index_topk_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, SZ, P]
+    lib.dsa_sparse_attn_decode.restype = I
+    lib.dsa_sparse_attn_decode.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
     _lib = lib
     return lib
 
@@ -238,9 +245,60 @@ def dsa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: 
     return o, lse
 
 
+def dsa_index_topk_decode_workspace_size(batch: int, n_keys: int, topk: int) -> int:
+    return load_library().dsa_index_topk_decode_workspace_size(batch, n_keys, topk)
+
+
+def dsa_index_topk_decode(q_idx: torch.Tensor, k_idx: torch.Tensor, w_idx: torch.Tensor, topk: int,
+                          idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                          ) -> torch.Tensor:
+    """Indexer + top-k for one query per sequence (q_idx [B, 1, h_i, d_i], w_idx [B, 1, h_i]) over the
+    keys k_idx [B, n_keys, d_i]; returns idx [B, 1, topk] int32 (-1 padded, unordered)."""
+    lib = load_library()
+    _dev(q_idx, k_idx, w_idx)
+    B, _, hi, di = q_idx.shape
+    n = k_idx.shape[1]
+    for t in (q_idx, k_idx, w_idx):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("indexer inputs must be contiguous float32")
+    if idx is None:
+        idx = torch.empty((B, 1, topk), dtype=torch.int32, device=q_idx.device)
+    if workspace is None:
+        workspace = torch.empty(lib.dsa_index_topk_decode_workspace_size(B, n, topk), dtype=torch.uint8,
+                                device=q_idx.device)
+    _check(lib.dsa_index_topk_decode(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(idx), B, n, hi, di, topk,
+                                     _ptr(workspace), workspace.numel(), _stream()))
+    return idx
+
+
+def dsa_sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                           scale: Optional[float] = None, o: Optional[torch.Tensor] = None, return_lse: bool = True,
+                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of one query per sequence (q [B, 1, Hq, d]) over the positions listed in idx [B, 1, topk]
+    of k, v [B, n_keys, Hkv, d]; returns (o [B, 1, Hq, dv], lse [B, Hq])."""
+    lib = load_library()
+    _dev(q, k, v, idx)
+    B, _, Hq, dqk = q.shape
+    n, Hkv, dv = k.shape[1], k.shape[2], v.shape[3]
+    topk = idx.shape[2]
+    if not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be contiguous int32 [B, 1, topk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if o is None:
+        o = torch.empty((B, 1, Hq, dv), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.dsa_sparse_attn_decode(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                      _ptr(idx), _ptr(o), _strides(o), _ptr(lse), B, n, Hq, Hkv, dqk, dv, topk,
+                                      float(scale), _stream()))
+    return o, lse
+
+
 __all__ = [
     "load_library", "HcaError", "Strides", "EXPORTS",
     "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd",
     "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
+    "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
 ]

@@ -56,7 +56,7 @@ struct SparseParams {
   const int32_t* idx;
   uint16_t* o; LStrides so;
   float* lse;
-  int seqlen, h_q, h_kv, topk, n_hb;
+  int seqlen, n_kv, h_q, h_kv, topk, n_hb;  // seqlen queries; positions < n_kv
   float c;
 };
 
@@ -89,8 +89,8 @@ void sparse_attn256_kernel(SparseParams p) {
     int bad = 0;
     for (int j = tid; j < ntiles * TK; j += 256) {
       int u = j < p.topk ? irow[j] : -1;
-      bad |= (u < -1 || u >= p.seqlen);
-      sidx[j] = (u >= 0 && u < p.seqlen) ? u : -1;
+      bad |= (u < -1 || u >= p.n_kv);
+      sidx[j] = (u >= 0 && u < p.n_kv) ? u : -1;
     }
     if (tid == 0) bad_sh = 0;
     __syncthreads();
@@ -244,7 +244,7 @@ void sparse_attn256_kernel(SparseParams p) {
 
 hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, LStrides sk, const void* v,
                                      LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,
-                                     int seqlen, int h_q, int h_kv, int topk, float scale, hipStream_t st) {
+                                     int seqlen, int n_kv, int h_q, int h_kv, int topk, float scale, hipStream_t st) {
   SparseParams p;
   p.q = (const uint16_t*)q; p.sq = sq;
   p.k = (const uint16_t*)k; p.sk = sk;
@@ -252,7 +252,7 @@ hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, 
   p.idx = idx;
   p.o = (uint16_t*)o; p.so = so;
   p.lse = lse;
-  p.seqlen = seqlen; p.h_q = h_q; p.h_kv = h_kv; p.topk = topk;
+  p.seqlen = seqlen; p.n_kv = n_kv; p.h_q = h_q; p.h_kv = h_kv; p.topk = topk;
   const int group = h_q / h_kv;
   if (group % HPB != 0 || topk > MAX_TOPK) return hipErrorInvalidValue;
   p.n_hb = group / HPB;

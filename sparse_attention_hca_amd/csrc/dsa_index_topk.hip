@@ -207,8 +207,16 @@ __device__ __forceinline__ uint32_t okey(float f) {
 struct SelectParams {
   const float* sc;
   int64_t ld;
-  int32_t* idx;     // [S, topk] of this batch
+  int32_t* idx;     // [S, topk] of this batch (prefill rows) or [rows, topk] (decode rows)
   int r0, topk;
+  // Decode rows (nseg > 0): row r holds keys seg * seg_len .. of sequence
+  // r / nseg (seg = r % nseg; n_total keys in all), scores at sc + (r / nseg) * ld
+  // + seg * seg_len.  Element u stands for position seg * seg_len + u, or for
+  // pos[(r / nseg) * ld + seg * seg_len + u] when pos is given (then ascending
+  // in u).  Prefill rows (nseg == 0): row r is query t = r0 + r over positions
+  // 0 .. t.
+  int nseg, seg_len, n_total;
+  const int32_t* pos;
 };
 
 constexpr int NB = 2048;   // bins of the general radix passes (11 + 11 + 10 bits)
@@ -345,15 +353,30 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
   __shared__ uint32_t wave_cnt[4];
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
-  const int t = p.r0 + row;
-  const int n = t + 1;
   const int k = p.topk;
-  int32_t* out = p.idx + (int64_t)t * k;
+  int n, off = 0;
+  const float* srow;
+  int32_t* out;
+  const int32_t* prow = nullptr;
+  if (p.nseg > 0) {
+    const int b = row / p.nseg;
+    off = (row % p.nseg) * p.seg_len;
+    n = min(p.seg_len, p.n_total - off);
+    srow = p.sc + (int64_t)b * p.ld + off;
+    out = p.idx + (int64_t)row * k;
+    if (p.pos) prow = p.pos + (int64_t)b * p.ld + off;
+  } else {
+    const int t = p.r0 + row;
+    n = t + 1;
+    srow = p.sc + (int64_t)row * p.ld;
+    out = p.idx + (int64_t)t * k;
+  }
+  // position of element u (monotonic in u)
+  auto P = [&](int u) __attribute__((always_inline)) { return prow ? prow[u] : u + off; };
   if (n <= k) {
-    for (int j = tid; j < k; j += 256) out[j] = j < n ? j : -1;
+    for (int j = tid; j < k; j += 256) out[j] = j < n ? P(j) : -1;
     return;
   }
-  const float* srow = p.sc + (int64_t)row * p.ld;
 
   // ---- sampling path: bracket the k-th largest key with two order
   // statistics of a sample of 256 spread groups of 4 adjacent keys, then one
@@ -438,7 +461,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
         // emit: one iteration per flagged element of this thread
         for (uint32_t m = fa; m; m &= m - 1u) {
           const int bit = __builtin_ctz(m);
-          if (oa < (uint32_t)k) out[oa] = ub + 1024 * (bit >> 2) + (bit & 3);
+          if (oa < (uint32_t)k) out[oa] = P(ub + 1024 * (bit >> 2) + (bit & 3));
           ++oa;
         }
         for (uint32_t m = fi; m; m &= m - 1u) {
@@ -448,7 +471,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
           const float x = (bit & 2) ? ((bit & 1) ? h[3] : h[2]) : ((bit & 1) ? h[1] : h[0]);
           if (oi < (uint32_t)CAP) {
             ckey[oi] = okey(x);
-            cpos[oi] = ub + 1024 * (bit >> 2) + (bit & 3);
+            cpos[oi] = P(ub + 1024 * (bit >> 2) + (bit & 3));
           }
           ++oi;
         }
@@ -632,13 +655,13 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       const bool valid = u < n;
       if (valid) key = okey(srow[u]);
       const uint32_t bin = key >> 21;
-      if (valid && bin > B) out[atomicAdd(&sel_info[2], 1u)] = u;
+      if (valid && bin > B) out[atomicAdd(&sel_info[2], 1u)] = P(u);
       uint32_t tot;
       const bool inb = valid && bin == B;
       const uint32_t r = ordered_rank(inb, wave_cnt, tot);
       if (inb) {
         ckey[nc + r] = key;
-        cpos[nc + r] = u;
+        cpos[nc + r] = P(u);
       }
       nc += tot;
     }
@@ -711,12 +734,99 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     uint32_t key = 0;
     const bool valid = u < n;
     if (valid) key = okey(srow[u]);
-    if (valid && key > T) out[atomicAdd(&sel_info[2], 1u)] = u;
+    if (valid && key > T) out[atomicAdd(&sel_info[2], 1u)] = P(u);
     uint32_t tot;
     const bool eq = valid && key == T;
     const uint32_t r = ordered_rank(eq, wave_cnt, tot);
-    if (eq && eq_base + r < need) out[n_above + eq_base + r] = u;
+    if (eq && eq_base + r < need) out[n_above + eq_base + r] = P(u);
     eq_base += tot;
+  }
+}
+
+// ---- decode: one query per sequence over n keys.
+// Scores stream the key rows (HBM-bound: 4 * d_i bytes per key); the query's
+// operands sit in LDS and are read as broadcasts.
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void decode_scores_kernel(const float* qI, const float* kI, const float* w,
+                                                            float* sc, int64_t ld, int n) {
+  __shared__ __attribute__((aligned(16))) float qs[HI * DI];
+  __shared__ float wsh[HI];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < HI * DI; i += 256) qs[i] = qI[(int64_t)b * HI * DI + i];
+  if (tid < HI) wsh[tid] = w[(int64_t)b * HI + tid];
+  __syncthreads();
+  const int u = blockIdx.x * 256 + tid;
+  if (u >= n) return;
+  const float* kr = kI + ((int64_t)b * n + u) * DI;
+  float acc[HI];
+#pragma unroll
+  for (int h = 0; h < HI; ++h) acc[h] = 0.f;
+#pragma unroll
+  for (int c = 0; c < DI; c += 4) {
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + c);
+#pragma unroll
+    for (int h = 0; h < HI; ++h) {
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + h * DI + c);
+      acc[h] = fmaf(kv[0], qv[0], acc[h]);
+      acc[h] = fmaf(kv[1], qv[1], acc[h]);
+      acc[h] = fmaf(kv[2], qv[2], acc[h]);
+      acc[h] = fmaf(kv[3], qv[3], acc[h]);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int h = 0; h < HI; ++h) s = fmaf(wsh[h], fmaxf(acc[h], 0.f), s);
+  sc[(int64_t)b * ld + u] = s;
+}
+
+constexpr int SEG = 65536;  // keys per first-stage row of a decode selection
+
+// The first stage leaves, per (sequence, segment), the segment's selected
+// positions in no particular order.  One workgroup per (sequence, segment)
+// marks them in an LDS bitmap and writes them back in ascending order with
+// their scores, at offset seg * k of the sequence's candidate row: every
+// segment but the last contributes exactly k, so the rows are contiguous.
+__global__ __launch_bounds__(256) void decode_compact_kernel(const int32_t* sel, const float* sc, int64_t ld, int nseg,
+                                                             int n_total, int k, float* cand_sc, int32_t* cand_pos,
+                                                             int64_t ld2) {
+  __shared__ uint32_t bits[SEG / 32];
+  __shared__ uint32_t part[256];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, b = row / nseg, seg = row % nseg;
+  const int off = seg * SEG;
+  for (int i = tid; i < SEG / 32; i += 256) bits[i] = 0;
+  __syncthreads();
+  for (int j = tid; j < k; j += 256) {
+    const int pz = sel[(int64_t)row * k + j];
+    if (pz >= 0) atomicOr(&bits[(pz - off) >> 5], 1u << ((pz - off) & 31));
+  }
+  __syncthreads();
+  // thread tid owns words 8 tid .. 8 tid + 7
+  constexpr int WPT = SEG / 32 / 256;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) cnt += __popc(bits[WPT * tid + i]);
+  part[tid] = cnt;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const uint32_t x = tid >= d ? part[tid - d] : 0u;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  uint32_t o = part[tid] - cnt;
+  const int64_t base = (int64_t)b * ld2 + (int64_t)seg * k;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t m = bits[WPT * tid + i];
+    while (m) {
+      const int pz = off + 32 * (WPT * tid + i) + __builtin_ctz(m);
+      m &= m - 1u;
+      cand_pos[base + o] = pz;
+      cand_sc[base + o] = sc[(int64_t)b * ld + pz];
+      ++o;
+    }
   }
 }
 
@@ -781,7 +891,7 @@ hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* 
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      SelectParams pp;
+      SelectParams pp{};
       pp.sc = (const float*)ws;
       pp.ld = ld;
       pp.idx = idx + (int64_t)b * seqlen * topk;
@@ -793,6 +903,96 @@ hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* 
     }
   }
   return hipSuccess;
+}
+
+size_t dsa_topk_decode_workspace_bytes(int batch, int n_keys, int topk) {
+  const int64_t ld = ((int64_t)n_keys + 127) / 128 * 128;
+  const int64_t nseg = ((int64_t)n_keys + SEG - 1) / SEG;
+  const int64_t ld2 = (nseg * topk + 127) / 128 * 128;
+  size_t bytes = (size_t)batch * ld * sizeof(float);                                // scores
+  if (nseg > 1) {
+    bytes += ((size_t)batch * nseg * topk * sizeof(int32_t) + 255) / 256 * 256;     // first-stage selections
+    bytes += (size_t)batch * ld2 * (sizeof(float) + sizeof(int32_t));                // ordered candidates
+  }
+  return bytes;
+}
+
+hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
+                                        int n_keys, int h_i, int d_i, int topk, void* ws, hipStream_t st) {
+  const int64_t ld = ((int64_t)n_keys + 127) / 128 * 128;
+  const int nseg = (n_keys + SEG - 1) / SEG;
+  const int64_t ld2 = ((int64_t)nseg * topk + 127) / 128 * 128;
+  float* sc = (float*)ws;
+  const dim3 gs((n_keys + 255) / 256, batch);
+#define HCA_DEC_SCORES(DI_, HI_) hipLaunchKernelGGL((decode_scores_kernel<DI_, HI_>), gs, dim3(256), 0, st, qI, kI, w, sc, ld, n_keys)
+  bool ok = true;
+  if (h_i == 4) {
+    switch (d_i) {
+      case 16: HCA_DEC_SCORES(16, 4); break;
+      case 32: HCA_DEC_SCORES(32, 4); break;
+      case 48: HCA_DEC_SCORES(48, 4); break;
+      case 64: HCA_DEC_SCORES(64, 4); break;
+      case 80: HCA_DEC_SCORES(80, 4); break;
+      case 96: HCA_DEC_SCORES(96, 4); break;
+      case 112: HCA_DEC_SCORES(112, 4); break;
+      case 128: HCA_DEC_SCORES(128, 4); break;
+      default: ok = false;
+    }
+  } else if (h_i == 8) {
+    switch (d_i) {
+      case 16: HCA_DEC_SCORES(16, 8); break;
+      case 32: HCA_DEC_SCORES(32, 8); break;
+      case 48: HCA_DEC_SCORES(48, 8); break;
+      case 64: HCA_DEC_SCORES(64, 8); break;
+      case 80: HCA_DEC_SCORES(80, 8); break;
+      case 96: HCA_DEC_SCORES(96, 8); break;
+      case 112: HCA_DEC_SCORES(112, 8); break;
+      case 128: HCA_DEC_SCORES(128, 8); break;
+      default: ok = false;
+    }
+  } else {
+    ok = false;
+  }
+#undef HCA_DEC_SCORES
+  if (!ok) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // first stage: exact top-k of every segment of SEG keys (the whole row when
+  // it fits one segment, written straight to idx)
+  int32_t* sel = nseg > 1 ? (int32_t*)(sc + (size_t)batch * ld) : idx;
+  SelectParams s1{};
+  s1.sc = sc;
+  s1.ld = ld;
+  s1.idx = sel;
+  s1.topk = topk;
+  s1.nseg = nseg;
+  s1.seg_len = SEG;
+  s1.n_total = n_keys;
+  hipLaunchKernelGGL(topk_select_kernel, dim3(batch * nseg), dim3(256), 0, st, s1);
+  e = hipGetLastError();
+  if (e != hipSuccess || nseg == 1) return e;
+  // second stage: the segments' selections, in position order, hold the top-k
+  // of the whole row (each of its members is in its segment's top-k)
+  // the candidate rows start on a 256-byte boundary (16-byte loads)
+  float* cand_sc = (float*)((char*)sel + ((size_t)batch * nseg * topk * sizeof(int32_t) + 255) / 256 * 256);
+  int32_t* cand_pos = (int32_t*)(cand_sc + (size_t)batch * ld2);
+  hipLaunchKernelGGL(decode_compact_kernel, dim3(batch * nseg), dim3(256), 0, st, sel, sc, ld, nseg, n_keys, topk,
+                     cand_sc, cand_pos, ld2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int last = n_keys - (nseg - 1) * SEG;
+  const int n2 = (nseg - 1) * topk + (last < topk ? last : topk);
+  SelectParams s2{};
+  s2.sc = cand_sc;
+  s2.ld = ld2;
+  s2.idx = idx;
+  s2.topk = topk;
+  s2.nseg = 1;
+  s2.seg_len = n2;
+  s2.n_total = n2;
+  s2.pos = cand_pos;
+  hipLaunchKernelGGL(topk_select_kernel, dim3(batch), dim3(256), 0, st, s2);
+  return hipGetLastError();
 }
 
 }  // namespace hca

@@ -302,13 +302,17 @@ hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float*
   return HCA_OK;
 }
 
-hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
-                                 const void* v, hca_strides_t sv, const int32_t* idx, void* o, hca_strides_t so,
-                                 float* lse, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v, int topk,
-                                 float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+// Sparse attention of seqlen_q queries per sequence over n_kv key rows.
+hca_status_t sparse_attn(const char* name, hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k,
+                         hca_strides_t sk, const void* v, hca_strides_t sv, const int32_t* idx, void* o,
+                         hca_strides_t so, float* lse, int batch, int seqlen_q, int n_kv, int h_q, int h_kv, int d_qk,
+                         int d_v, int topk, float scale, void* stream) {
   if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
-  if (batch <= 0 || seqlen <= 0 || h_q <= 0 || h_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
-    return fail(HCA_ERR_INVALID, "dsa_sparse_attn_fwd: sizes must be positive");
+  if (batch <= 0 || seqlen_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
+    return fail(HCA_ERR_INVALID, "%s: sizes must be positive", name);
   if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q must be a multiple of h_kv");
   if (!idx) return fail(HCA_ERR_INVALID, "idx is NULL");
   if (!aligned16(idx)) return fail(HCA_ERR_INVALID, "idx is not 16-byte aligned");
@@ -319,19 +323,74 @@ hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq
   HCA_TRY(check_tensor("o", o, so, es));
   if (lse && ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is not 4-byte aligned");
   if (dt != HCA_DTYPE_BF16 || d_qk != 256 || d_v != 256 || (h_q / h_kv) % 64 || topk > 4096)
-    return fail(HCA_ERR_UNSUPPORTED,
-                "dsa_sparse_attn_fwd: needs bf16, d_qk = d_v = 256, h_q/h_kv a multiple of 64, topk <= 4096");
+    return fail(HCA_ERR_UNSUPPORTED, "%s: needs bf16, d_qk = d_v = 256, h_q/h_kv a multiple of 64, topk <= 4096",
+                name);
   {
-    const Range ro = extent(o, so, batch, seqlen, h_q, d_v, es);
-    if (overlaps(ro, extent(q, sq, batch, seqlen, h_q, d_qk, es)) ||
-        overlaps(ro, extent(k, sk, batch, seqlen, h_kv, d_qk, es)) ||
-        overlaps(ro, extent(v, sv, batch, seqlen, h_kv, d_v, es)) ||
-        overlaps(ro, Range{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)}))
+    const Range ro = extent(o, so, batch, seqlen_q, h_q, d_v, es);
+    if (overlaps(ro, extent(q, sq, batch, seqlen_q, h_q, d_qk, es)) ||
+        overlaps(ro, extent(k, sk, batch, n_kv, h_kv, d_qk, es)) ||
+        overlaps(ro, extent(v, sv, batch, n_kv, h_kv, d_v, es)) ||
+        overlaps(ro, Range{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen_q * topk)}))
       return fail(HCA_ERR_INVALID, "o overlaps an input");
   }
-  hipError_t e = hca::launch_dsa_sparse_attn256(q, ls(sq), k, ls(sk), v, ls(sv), idx, o, ls(so), lse, batch, seqlen,
-                                                h_q, h_kv, topk, scale, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "dsa_sparse_attn_fwd launch");
+  hipError_t e = hca::launch_dsa_sparse_attn256(q, ls(sq), k, ls(sk), v, ls(sv), idx, o, ls(so), lse, batch, seqlen_q,
+                                                n_kv, h_q, h_kv, topk, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return HCA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                                 const void* v, hca_strides_t sv, const int32_t* idx, void* o, hca_strides_t so,
+                                 float* lse, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v, int topk,
+                                 float scale, void* stream) {
+  return sparse_attn("dsa_sparse_attn_fwd", dt, q, sq, k, sk, v, sv, idx, o, so, lse, batch, seqlen, seqlen, h_q,
+                     h_kv, d_qk, d_v, topk, scale, stream);
+}
+
+hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                                    const void* v, hca_strides_t sv, const int32_t* idx, void* o, hca_strides_t so,
+                                    float* lse, int batch, int n_keys, int h_q, int h_kv, int d_qk, int d_v, int topk,
+                                    float scale, void* stream) {
+  return sparse_attn("dsa_sparse_attn_decode", dt, q, sq, k, sk, v, sv, idx, o, so, lse, batch, 1, n_keys, h_q, h_kv,
+                     d_qk, d_v, topk, scale, stream);
+}
+
+size_t dsa_index_topk_decode_workspace_size(int batch, int n_keys, int topk) {
+  if (batch <= 0 || n_keys <= 0 || topk <= 0) return 0;
+  return hca::dsa_topk_decode_workspace_bytes(batch, n_keys, topk);
+}
+
+hca_status_t dsa_index_topk_decode(const float* q_idx, const float* k_idx, const float* w_idx, int32_t* idx, int batch,
+                                   int n_keys, int h_i, int d_i, int topk, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!q_idx || !k_idx || !w_idx || !idx) return fail(HCA_ERR_INVALID, "dsa_index_topk_decode: NULL tensor");
+  if (batch <= 0 || n_keys <= 0 || h_i <= 0 || d_i <= 0 || topk <= 0)
+    return fail(HCA_ERR_INVALID, "dsa_index_topk_decode: sizes must be positive");
+  if ((h_i != 4 && h_i != 8) || d_i % 16 || d_i > 128 || topk > 4096)
+    return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk_decode: needs h_i in {4, 8}, d_i a multiple of 16 <= 128, "
+                                     "topk <= 4096");
+  if (n_keys >= (1 << 30)) return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk_decode: n_keys must be below 2^30");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(idx))
+    return fail(HCA_ERR_INVALID, "dsa_index_topk_decode: tensors must be 16-byte aligned");
+  {
+    const Range ri{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * topk)};
+    const Range rq{(uintptr_t)q_idx, (uintptr_t)(q_idx + (size_t)batch * h_i * d_i)};
+    const Range rk{(uintptr_t)k_idx, (uintptr_t)(k_idx + (size_t)batch * n_keys * d_i)};
+    const Range rw{(uintptr_t)w_idx, (uintptr_t)(w_idx + (size_t)batch * h_i)};
+    if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(ri, rw))
+      return fail(HCA_ERR_INVALID, "dsa_index_topk_decode: idx overlaps an input");
+  }
+  const size_t need = hca::dsa_topk_decode_workspace_bytes(batch, n_keys, topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(HCA_ERR_WORKSPACE, "dsa_index_topk_decode needs a %zu-byte workspace (got %zu)", need,
+                workspace_bytes);
+  if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
+  hipError_t e = hca::launch_dsa_index_topk_decode(q_idx, k_idx, w_idx, idx, batch, n_keys, h_i, d_i, topk, workspace,
+                                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dsa_index_topk_decode launch");
   return HCA_OK;
 }
 

@@ -51,8 +51,14 @@ hipError_t launch_attn_decode512(const AttnArgs& a, void* ws, hipStream_t st);
 size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk);
 hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
                                  int seqlen, int h_i, int d_i, int topk, void* ws, size_t ws_bytes, hipStream_t st);
+// Decode: one query per sequence over n_keys keys ([batch, 1, h_i, d_i] queries,
+// [batch, n_keys, d_i] keys, [batch, 1, topk] output).
+size_t dsa_topk_decode_workspace_bytes(int batch, int n_keys, int topk);
+hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
+                                        int n_keys, int h_i, int d_i, int topk, void* ws, hipStream_t st);
+// Sparse attention of seqlen queries per sequence; selected positions must lie in [0, n_kv).
 hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, LStrides sk, const void* v,
                                      LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,
-                                     int seqlen, int h_q, int h_kv, int topk, float scale, hipStream_t st);
+                                     int seqlen, int n_kv, int h_q, int h_kv, int topk, float scale, hipStream_t st);
 
 }  // namespace hca

@@ -146,6 +146,37 @@ def test_dsa_rejects_bad_arguments():
     assert sp(k=4097) == hca.HCA_ERR_UNSUPPORTED
 
 
+def test_dsa_decode_rejects_bad_arguments():
+    lib = _lib()
+    ws = lib.dsa_index_topk_decode_workspace_size(2, 200000, 2048)
+    # one score row per sequence, 4 segments of first-stage winners, the ordered candidates
+    assert ws >= 2 * 200064 * 4 + 2 * 4 * 2048 * 4 + 2 * 8192 * 8
+    assert lib.dsa_index_topk_decode_workspace_size(2, 5000, 2048) == 2 * 5120 * 4  # one segment: scores only
+    call = lambda **kw: lib.dsa_index_topk_decode(kw.get("q", FAKE), FAKE, FAKE,
+                                                  kw.get("idx", ctypes.c_void_p(1 << 34)), 2, kw.get("n", 200000),
+                                                  kw.get("hi", 4), kw.get("di", 64), kw.get("k", 2048),
+                                                  kw.get("ws", ctypes.c_void_p(1 << 36)), kw.get("wsb", ws), None)
+    assert call(q=None) == hca.HCA_ERR_INVALID
+    assert call(hi=6) == hca.HCA_ERR_UNSUPPORTED
+    assert call(di=72) == hca.HCA_ERR_UNSUPPORTED
+    assert call(k=4097) == hca.HCA_ERR_UNSUPPORTED
+    assert call(n=0) == hca.HCA_ERR_INVALID
+    assert call(n=1 << 30) == hca.HCA_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == hca.HCA_ERR_WORKSPACE
+    assert call(ws=None) == hca.HCA_ERR_WORKSPACE
+    assert call(idx=FAKE) == hca.HCA_ERR_INVALID       # idx aliases the query
+    sp = lambda **kw: lib.dsa_sparse_attn_decode(kw.get("dt", 1), FAKE, S(0, 64 * 256, 256), FAKE, S(0, 256, 256),
+                                                 FAKE, S(0, 256, 256), kw.get("idx", ctypes.c_void_p(1 << 33)),
+                                                 kw.get("o", ctypes.c_void_p(1 << 34)), S(0, 64 * 256, 256), None,
+                                                 1, kw.get("n", 100000), 64, 1, kw.get("d", 256), 256, 16, 0.0625,
+                                                 None)
+    assert sp(idx=None) == hca.HCA_ERR_INVALID
+    assert sp(n=0) == hca.HCA_ERR_INVALID
+    assert sp(d=128) == hca.HCA_ERR_UNSUPPORTED
+    assert sp(o=FAKE) == hca.HCA_ERR_INVALID           # o aliases q
+    assert sp(o=ctypes.c_void_p((1 << 20) + 4096)) == hca.HCA_ERR_INVALID  # o inside the 100000 key rows
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     x = torch.zeros(1, 128, 1, 64, dtype=torch.bfloat16)

@@ -188,3 +188,107 @@ def test_full_size_dsa_sampled():
     _say(f"  sparse attention rel err {err:.3e}")
     assert err < BF16_TOL
     assert np.max(np.abs(host(lse[:, :, rows]) - rlse)) < LSE_TOL
+
+
+# ------------------------------------------------------------------ decode: one query per sequence
+
+def _decode_indexer_inputs(B, n, k, seed, di=64, hi=4, max_attempts=20):
+    """Keys ~ N(0,1); each sequence's query and weights are redrawn until its
+    row is tie-free (the same top-k set for every fp32 evaluation order)."""
+    rng = np.random.default_rng(seed)
+    kI = rng.standard_normal((B, n, di)).astype(np.float32)
+    qI = np.zeros((B, 1, hi, di), dtype=np.float32)
+    w = np.zeros((B, 1, hi), dtype=np.float32)
+    for b in range(B):
+        for _ in range(max_attempts):
+            qI[b, 0] = rng.standard_normal((hi, di)).astype(np.float32)
+            w[b, 0] = rng.standard_normal(hi).astype(np.float32)
+            if oracle.tie_free_row(qI[b, 0], kI[b], w[b, 0], n - 1, k):
+                break
+        else:
+            raise AssertionError("no tie-free draw")
+    return qI, kI, w
+
+
+@pytest.mark.parametrize("B,n,topk", [(2, 1000, 2048), (2, 5000, 512), (3, 70000, 2048), (2, 150001, 2048),
+                                      (1, 131072, 4096)])
+def test_index_topk_decode_exact_sets(B, n, topk):
+    """One query per sequence over n keys, through one segment (n <= 65536) or
+    the two-stage selection (several segments, the last one ragged)."""
+    _say("index_topk_decode", B, n, topk)
+    qI, kI, w = _decode_indexer_inputs(B, n, topk, seed=n + topk)
+    idx = hca.dsa_index_topk_decode(dev_f32(qI), dev_f32(kI), dev_f32(w), topk)
+    got = _sorted_rows(idx.cpu().numpy())
+    for b in range(B):
+        ref = oracle.topk_row(oracle.index_scores_row(qI[b, 0], kI[b], w[b, 0], n - 1), topk)
+        m = min(n, topk)
+        assert got[b, 0, :m].tolist() == np.sort(ref).tolist()
+        assert (got[b, 0, m:] == -1).all()
+
+
+def test_index_topk_decode_heavy_ties_across_segments():
+    """Integer scores with tens of thousands of ties per value over three
+    segments: the winners of every segment and of the merge break ties by
+    position exactly."""
+    n, k = 150001, 2048
+    rng = np.random.default_rng(12)
+    kI = np.zeros((2, n, 64), dtype=np.float32)
+    kI[:, np.arange(n), np.arange(n) % 8] = 1.0
+    qI = rng.integers(0, 2, (2, 1, 4, 64)).astype(np.float32)
+    w = rng.integers(1, 3, (2, 1, 4)).astype(np.float32)
+    idx = hca.dsa_index_topk_decode(dev_f32(qI), dev_f32(kI), dev_f32(w), k)
+    got = _sorted_rows(idx.cpu().numpy())
+    for b in range(2):
+        ref = oracle.topk_row(oracle.index_scores_row(qI[b, 0], kI[b], w[b, 0], n - 1), k)
+        assert got[b, 0].tolist() == np.sort(ref).tolist()
+
+
+def test_index_topk_decode_equals_prefill_last_row():
+    """The decode selection of a query equals the prefill selection of the
+    same query's row (same keys)."""
+    cfg = synth.small_dsa(seqlen=3000, topk=256, batch=2)
+    inp = make_tie_free(cfg)
+    S, k = cfg.seqlen, cfg.topk
+    full = _sorted_rows(hca.dsa_index_topk(dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"]), k).cpu().numpy())
+    for t in (S - 1, 1700):
+        qI = np.ascontiguousarray(inp["qI"][:, t:t + 1])
+        w = np.ascontiguousarray(inp["w"][:, t:t + 1])
+        kI = np.ascontiguousarray(inp["kI"][:, :t + 1])
+        dec = _sorted_rows(hca.dsa_index_topk_decode(dev_f32(qI), dev_f32(kI), dev_f32(w), k).cpu().numpy())
+        assert np.array_equal(dec[:, 0], full[:, t])
+
+
+@pytest.mark.parametrize("n,topk", [(5000, 2048), (70000, 512)])
+def test_sparse_attention_decode_parity(n, topk):
+    """One query per sequence, 64 heads on one KV head, over positions chosen
+    from a history longer than the query sequence (-1 padding included)."""
+    B, Hq, d = 2, 64, 256
+    rng = np.random.default_rng(n)
+    q = synth.bf16_round_bits(rng.standard_normal((B, 1, Hq, d)))
+    k = synth.bf16_round_bits(rng.standard_normal((B, n, 1, d)))
+    v = synth.bf16_round_bits(rng.standard_normal((B, n, 1, d)))
+    idx = np.full((B, 1, topk), -1, dtype=np.int32)
+    for b in range(B):
+        m = topk - 37 * b
+        idx[b, 0, :m] = rng.choice(n, m, replace=False)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o, lse = hca.dsa_sparse_attn_decode(qd, kd, vd, torch.from_numpy(idx).cuda(), scale=1.0 / 16)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.sparse_attention(f64(q, True), f64(k, True), f64(v, True), idx, 1.0 / 16, rows=[0])
+    err = rel_err(host(o), ro)
+    _say(f"sparse decode n={n} rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse[:, :, 0])) < LSE_TOL
+
+
+def test_sparse_attention_decode_rejects_out_of_range_positions():
+    """A position >= n_keys poisons its row with NaN instead of reading past the keys."""
+    B, Hq, d, n, topk = 2, 64, 256, 300, 64
+    q = torch.randn(B, 1, Hq, d, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B, n, 1, d, device="cuda").to(torch.bfloat16)
+    v = torch.randn_like(k)
+    idx = torch.arange(topk, dtype=torch.int32, device="cuda").repeat(B, 1, 1).contiguous()
+    idx[1, 0, 5] = n
+    o, lse = hca.dsa_sparse_attn_decode(q, k, v, idx)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o[0].float()).all() and torch.isnan(o[1].float()).all()
