@@ -229,6 +229,51 @@ def bench_dsa(torch, hca, synth, cfg, steps, warmup):
     return res
 
 
+# DSA decode: one query per sequence over the history length of the HCA decode
+# workload (1,048,704 positions), c5's indexer and attention shapes.
+DSA_DECODE = dict(batch=16, n_keys=1048704, h_i=4, d_i=64, topk=2048, h_q=64, d=256)
+
+
+def bench_dsa_decode(torch, hca, steps, warmup):
+    c = DSA_DECODE
+    B, n = c["batch"], c["n_keys"]
+    t0 = time.time()
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(5)
+    kI = torch.randn((B, n, c["d_i"]), generator=g, device="cuda:0")
+    qI = torch.randn((B, 1, c["h_i"], c["d_i"]), generator=g, device="cuda:0")
+    w = torch.randn((B, 1, c["h_i"]), generator=g, device="cuda:0")
+    k = torch.randn((B, n, 1, c["d"]), generator=g, device="cuda:0").to(torch.bfloat16)
+    v = torch.randn((B, n, 1, c["d"]), generator=g, device="cuda:0").to(torch.bfloat16)
+    q = torch.randn((B, 1, c["h_q"], c["d"]), generator=g, device="cuda:0").to(torch.bfloat16)
+    torch.cuda.synchronize()
+    log(f"[bench] dsa decode: inputs ready in {time.time() - t0:.1f}s")
+    idx = torch.empty((B, 1, c["topk"]), dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(hca.dsa_index_topk_decode_workspace_size(B, n, c["topk"]), dtype=torch.uint8, device="cuda:0")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, c["h_q"]), dtype=torch.float32, device="cuda:0")
+    fi = lambda: hca.dsa_index_topk_decode(qI, kI, w, c["topk"], idx=idx, workspace=ws)
+    fa = lambda: hca.dsa_sparse_attn_decode(q, k, v, idx, scale=1.0 / 16, o=o, lse=lse)
+    for _ in range(warmup):
+        fi()
+        fa()
+    ti, ta = Timer(torch), Timer(torch)
+    for _ in range(steps):
+        ti(fi)
+        ta(fa)
+    ms_i, ms_a = ti.mean_ms(), ta.mean_ms()
+    # indexer: every index key once, the score row written and read back once
+    idx_bytes = B * n * (4 * c["d_i"] + 4 + 4)
+    # attention: the selected K and V rows (bf16) plus q and o
+    attn_bytes = B * c["topk"] * 2 * 2 * c["d"] + 2 * B * c["h_q"] * 2 * c["d"]
+    res = {"index_topk_ms": ms_i, "attn_ms": ms_a, "step_ms": ms_i + ms_a,
+           "index_gbs": idx_bytes / ms_i / 1e6, "index_hbm_frac": idx_bytes / ms_i / 1e6 / PEAK_HBM_GBS,
+           "attn_gbs": attn_bytes / ms_a / 1e6, "tokens_per_s": B / (ms_i + ms_a) * 1e3}
+    del kI, qI, w, k, v, q, idx, ws, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synth, cfg, heads=4):
     """The float64 oracle on a bounded sample of the headline workload: block
     compression of K and V for `heads` heads and attention for every query row
@@ -263,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c3,c4,c5",
+    ap.add_argument("--only", default="c2,c3,c4,c5,c5d",
                     help="comma list of workloads to run (c2 always runs; 'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -341,6 +386,9 @@ def main():
             "attn_tflops": fa / r5["attn_ms"] / 1e9, "attn_mfma_frac": fa / r5["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
         }
         log(f"[bench] c5 done: {comps['dsa_prefill_64k']}")
+    if "c5d" in only:
+        comps["dsa_decode_1m"] = bench_dsa_decode(torch, hca, args.steps, args.warmup)
+        log(f"[bench] c5d done: {comps['dsa_decode_1m']}")
 
     value = c2.seqlen / r2["step_ms"] * 1e3
     achieved = b2 / r2["attn_ms"] / 1e6
