@@ -17,17 +17,21 @@ row at a time, following the ERNIE 5.5 Flash Base pages:
   "1. Hybrid Sparse Attention").
 
 Points the pages leave open are fixed as stated in each module's docstring.
+The gradients (``*_bwd``) are the chain rule through these definitions (the
+pages describe the forward only), pinned against central finite differences.
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (closed forms, special cases reducing to dense
 causal attention computed by torch, brute-force loops and hand-derived golden
 values); none is "parity unpinned".
 """
-from .hca import compress_kv, window_bounds, attend_row, hca_attention, visible_positions
-from .dsa import (index_scores_row, topk_row, index_topk, sparse_attention,
+from .hca import (compress_kv, window_bounds, attend_row, hca_attention, visible_positions,
+                  attend_row_bwd, hca_attention_bwd, compress_kv_bwd)
+from .dsa import (index_scores_row, topk_row, index_topk, sparse_attention, sparse_attention_bwd,
                   score_error_bounds, tie_free_row, tie_free_rows, valid_topk_row)
 
 __all__ = [
     "compress_kv", "window_bounds", "attend_row", "hca_attention", "visible_positions",
+    "attend_row_bwd", "hca_attention_bwd", "compress_kv_bwd", "sparse_attention_bwd",
     "index_scores_row", "topk_row", "index_topk", "sparse_attention",
     "score_error_bounds", "tie_free_row", "tie_free_rows", "valid_topk_row",
 ]

@@ -79,6 +79,42 @@ def sparse_attention(q, k, v, idx, scale: float, rows=None):
     return o, lse
 
 
+def sparse_attention_bwd(q, k, v, idx, scale: float, dout):
+    """Gradients of sparse_attention's output (all rows) given dout = dL/do:
+    (dq, dk, dv) shaped like q, k, v.  The chain rule through the softmax over
+    each query's selected positions (the pages give the forward only): with
+    p = softmax(scale q K_sel^T), ds = p (dout V_sel^T - <dout, o>),
+    dq = scale ds K_sel, dk_sel += scale ds^T q, dv_sel += p^T dout; a position
+    listed by several queries sums their contributions.  Query head h reads KV
+    head h // (Hq / Hkv)."""
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for t in range(S):
+            sel = np.asarray(idx[b, t])
+            sel = sel[sel >= 0]
+            for g in range(Hkv):
+                keys = np.asarray(k[b, sel, g], dtype=np.float64)
+                vals = np.asarray(v[b, sel, g], dtype=np.float64)
+                hs = slice(g * group, (g + 1) * group)
+                logits = scale * (q[b, t, hs] @ keys.T)               # [group, n]
+                p = np.exp(logits - logits.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                o = p @ vals
+                dp = dout[b, t, hs] @ vals.T
+                ds = p * (dp - np.sum(dout[b, t, hs] * o, axis=1, keepdims=True))
+                dq[b, t, hs] = scale * (ds @ keys)
+                np.add.at(dk[b, :, g], sel, scale * (ds.T @ q[b, t, hs]))
+                np.add.at(dv[b, :, g], sel, p.T @ dout[b, t, hs])
+    return dq, dk, dv
+
+
 def score_error_bounds(qI_t, kI, w_t, t: int, margin: float = 2.0):
     """Exact scores s, a bound r on |s_fp32 - s| for any float32 evaluation order, and which
     positions are exact zeros in every float32 evaluation (all index-head dots certainly < 0).

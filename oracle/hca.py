@@ -88,3 +88,79 @@ def hca_attention(q, k, v, kc, vc, *, window: int, block: int, scale: float,
                                        np.asarray(v[b, lo - kv_pos0: t - kv_pos0 + 1, g], dtype=np.float64)])
                 o[b, ri, h], lse[b, h, ri] = attend_row(q[b, i, h], keys, vals, scale)
     return o, lse
+
+
+# ---------------------------------------------------------------- gradients
+#
+# The pages describe the forward only; the gradients below are the chain rule
+# through the definitions above (softmax attention, weighted block sum).  They
+# are pinned against central finite differences of those definitions.
+
+def attend_row_bwd(qv: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float, dout: np.ndarray):
+    """Gradients of attend_row's output row, given the gradient dout of that row,
+    with respect to the query, every key and every value: (dq, dkeys, dvalues).
+
+    p = softmax(scale * keys q); o = p values.  d/dp_x = <dout, v_x>; through the
+    softmax ds_x = p_x (d/dp_x - <dout, o>); then dq = scale sum_x ds_x k_x,
+    dk_x = scale ds_x q, dv_x = p_x dout.
+    """
+    logits = scale * (keys @ qv)
+    p = np.exp(logits - logits.max())
+    p /= p.sum()
+    dp = values @ dout
+    ds = p * (dp - dp @ p)
+    return scale * (ds @ keys), scale * np.outer(ds, qv), np.outer(p, dout)
+
+
+def hca_attention_bwd(q, k, v, kc, vc, dout, *, window: int, block: int, scale: float,
+                      q_pos0: int = 0, kv_pos0: int = 0):
+    """Gradients of hca_attention's output o (all rows) given dout = dL/do.
+
+    Returns (dq, dk, dv, dkc, dvc) shaped like q, k, v, kc, vc: the raw keys and
+    values receive the gradient of the window positions that see them, the
+    compressed entries that of the queries whose blocks they are.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    dkc = np.zeros(kc.shape)
+    dvc = np.zeros(vc.shape)
+    for b in range(B):
+        for i in range(Sq):
+            t = q_pos0 + i
+            lo, n_c = window_bounds(t, window, block)
+            r0, r1 = lo - kv_pos0, t - kv_pos0 + 1
+            for h in range(Hq):
+                g = h // group
+                keys = np.concatenate([np.asarray(kc[b, :n_c, g], dtype=np.float64),
+                                       np.asarray(k[b, r0:r1, g], dtype=np.float64)])
+                vals = np.concatenate([np.asarray(vc[b, :n_c, g], dtype=np.float64),
+                                       np.asarray(v[b, r0:r1, g], dtype=np.float64)])
+                gq, gk, gv = attend_row_bwd(q[b, i, h], keys, vals, scale, dout[b, i, h])
+                dq[b, i, h] = gq
+                dkc[b, :n_c, g] += gk[:n_c]
+                dvc[b, :n_c, g] += gv[:n_c]
+                dk[b, r0:r1, g] += gk[n_c:]
+                dv[b, r0:r1, g] += gv[n_c:]
+    return dq, dk, dv, dkc, dvc
+
+
+def compress_kv_bwd(x: np.ndarray, w: np.ndarray, dout: np.ndarray, block: int):
+    """Gradients of compress_kv given dout = dL/d(out) [B, S // block, H, d]:
+    dx[b, j*block + i, h] = w[h, i] dout[b, j, h] (zero past the last whole
+    block) and dw[h, i] = sum_{b, j} <dout[b, j, h], x[b, j*block + i, h]>."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, H, d = x.shape
+    n = S // block
+    dx = np.zeros(x.shape)
+    dx[:, : n * block] = np.einsum("hi,bnhd->bnihd", w, dout).reshape(B, n * block, H, d)
+    xb = x[:, : n * block].reshape(B, n, block, H, d)
+    dw = np.einsum("bnihd,bnhd->hi", xb, dout)
+    return dx, dw

@@ -70,3 +70,37 @@ def test_non_causal_indexer(monkeypatch):
     real = odsa.index_scores_row
     monkeypatch.setattr(odsa, "index_scores_row", lambda qI_t, kI, w_t, t: real(qI_t, kI, w_t, min(t + 1, kI.shape[0] - 1)))
     _expect_caught([tdsa.test_k_at_least_context_is_dense_causal_mqa, tdsa.test_equal_index_keys_select_first_positions])
+
+
+# ---------------------------------------------------------------- gradients
+
+import test_oracle_grad as tgrad  # noqa: E402
+
+
+def test_softmax_jacobian_missing_mean_term(monkeypatch):
+    def bad(qv, keys, values, scale, dout):
+        logits = scale * (keys @ qv)
+        p = np.exp(logits - logits.max())
+        p /= p.sum()
+        ds = p * (values @ dout)            # drops the <dout, o> term
+        return scale * (ds @ keys), scale * np.outer(ds, qv), np.outer(p, dout)
+    monkeypatch.setattr(ohca, "attend_row_bwd", bad)        # used by hca_attention_bwd
+    monkeypatch.setattr(oracle, "attend_row_bwd", bad)
+    _expect_caught([tgrad.test_attend_row_bwd_matches_finite_differences])
+    _expect_caught([lambda: tgrad.test_hca_attention_bwd_matches_finite_differences(0, 0, 9, 9)])
+
+
+def test_compressed_entries_gradient_dropped_from_raw_keys(monkeypatch):
+    real = ohca.compress_kv_bwd
+    monkeypatch.setattr(oracle, "compress_kv_bwd", lambda x, w, d, b: (0 * real(x, w, d, b)[0], real(x, w, d, b)[1]))
+    _expect_caught([tgrad.test_hca_chain_through_compression_matches_finite_differences])
+
+
+def test_sparse_bwd_value_gradient_transposed(monkeypatch):
+    real = odsa.sparse_attention_bwd
+
+    def bad(q, k, v, idx, scale, dout):
+        dq, dk, dv = real(q, k, v, idx, scale, dout)
+        return dq, dv, dk                    # key and value gradients swapped
+    monkeypatch.setattr(oracle, "sparse_attention_bwd", bad)
+    _expect_caught([tgrad.test_sparse_attention_bwd_matches_finite_differences])
