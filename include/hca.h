@@ -1,7 +1,8 @@
 /*
- * hca.h -- C ABI of libhca.so: the forward path of hybrid sparse attention
- * (HCA heavily compressed attention + DSA top-k sparse attention) for AMD
- * Instinct MI355X (gfx950).
+ * hca.h -- C ABI of libhca.so: hybrid sparse attention (HCA heavily
+ * compressed attention + DSA top-k sparse attention) for AMD Instinct MI355X
+ * (gfx950): the forward path, decode-time cache upkeep, and the backward of
+ * both attentions and of the block compressor.
  *
  * The method is the one described on the ERNIE 5.5 Flash Base pages:
  *   - mirrorspeed page, section "Hybrid sparse attention, 1/7 full context
@@ -273,6 +274,126 @@ hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
                                     int batch, int n_keys, int h_q, int h_kv, int d_qk, int d_v,
                                     int topk, float scale,
                                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward.  The pages describe the forward only (mirrorspeed page, "Hybrid
+ * sparse attention" section; training reaches 128K-token contexts).  The
+ * gradients below are the chain rule through the forward definitions above:
+ * with p the softmax weights recomputed from the forward's lse and
+ * D = <dO, O> per (query, head),
+ *   ds_x = p_x (<dO, value_x> - D),  dq = scale * sum_x ds_x key_x,
+ *   dkey_x += scale * ds_x q,        dvalue_x += p_x dO.
+ * All gradients are fp32 (their strides follow the same 16-byte rule, i.e.
+ * multiples of 4 elements) and are overwritten, except where a call says it
+ * accumulates.  Sums run in a fixed order without atomics, except the DSA
+ * key/value gradients (see dsa_sparse_attn_bwd).
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes hca_attn_bwd needs (D per query and head). */
+size_t hca_attn_bwd_workspace_size(int batch, int seqlen_q, int h_q);
+
+/*
+ * hca_attn_bwd -- gradients of hca_attn_fwd's output o with respect to q, the
+ * raw K/V and the compressed entries, given dout = dL/do and the forward's o
+ * and lse (same keys per query as hca_attn_fwd: compressed entries j < n_c
+ * plus the raw window [lo, t]).
+ *   q, k, v, kc, vc, o, dout: as in hca_attn_fwd, dtype dt (read)
+ *   lse : [batch, h_q, seqlen_q] fp32 contiguous from hca_attn_fwd (read)
+ *   dq  : [batch, seqlen_q, h_q, head_dim] fp32 (written)
+ *   dk, dv  : [batch, seqlen_kv, h_kv, head_dim] fp32 (written; rows no query
+ *             sees get zeros)
+ *   dkc, dvc: [batch, n_blocks, h_kv, head_dim] fp32 (written; may be NULL
+ *             when n_blocks == 0)
+ * To reach the raw K/V through the compressor, follow with
+ * hca_compress_kv_bwd, which adds its share into dk/dv.
+ * Errors: as hca_attn_fwd; HCA_ERR_INVALID when a gradient overlaps an input
+ * or another gradient; HCA_ERR_WORKSPACE for a missing or short workspace.
+ * Supported: fp32 and bf16, head_dim <= 512 (multiple of 4), at most 16384
+ * keys per query.
+ */
+hca_status_t hca_attn_bwd(hca_dtype_t dt,
+                          const void* q, hca_strides_t sq,
+                          const void* k, hca_strides_t sk,
+                          const void* v, hca_strides_t sv,
+                          const void* kc, hca_strides_t skc,
+                          const void* vc, hca_strides_t svc,
+                          const void* o, hca_strides_t so,
+                          const float* lse,
+                          const void* dout, hca_strides_t sdout,
+                          float* dq, hca_strides_t sdq,
+                          float* dk, hca_strides_t sdk,
+                          float* dv, hca_strides_t sdv,
+                          float* dkc, hca_strides_t sdkc,
+                          float* dvc, hca_strides_t sdvc,
+                          int batch, int seqlen_q, int64_t q_pos0,
+                          int seqlen_kv, int64_t kv_pos0, int n_blocks,
+                          int h_q, int h_kv, int head_dim, int block, int window, float scale,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * hca_compress_kv_bwd -- backward of hca_compress_kv given dkc, dvc = dL/dkc,
+ * dL/dvc (fp32):
+ *   dk[b, j*block + i, h, :] += w_k[h, i] * dkc[b, j, h, :]   (v likewise; rows
+ *                                                              past the last whole block untouched)
+ *   dw_k[h, i] = sum_{b, j} <dkc[b, j, h, :], k[b, j*block + i, h, :]>  (dw_v likewise)
+ *   k, v   : [batch, seqlen, h_kv, head_dim] dtype dt (read)
+ *   dkc, dvc: [batch, seqlen/block, h_kv, head_dim] fp32 (read)
+ *   w_k, w_v: [h_kv, block] fp32 contiguous (read)
+ *   dk, dv : [batch, seqlen, h_kv, head_dim] fp32 (ACCUMULATED: pass the raw
+ *            gradients from hca_attn_bwd, or zeros)
+ *   dw_k, dw_v: [h_kv, block] fp32 contiguous (written)
+ * Errors: HCA_ERR_INVALID for null pointers, bad sizes or overlapping gradients.
+ * Supported: fp32 and bf16, head_dim a multiple of 4.
+ */
+hca_status_t hca_compress_kv_bwd(hca_dtype_t dt,
+                                 const void* k, hca_strides_t sk,
+                                 const void* v, hca_strides_t sv,
+                                 const float* dkc, hca_strides_t sdkc,
+                                 const float* dvc, hca_strides_t sdvc,
+                                 const float* w_k, const float* w_v,
+                                 float* dk, hca_strides_t sdk,
+                                 float* dv, hca_strides_t sdv,
+                                 float* dw_k, float* dw_v,
+                                 int batch, int seqlen, int h_kv, int head_dim, int block,
+                                 void* stream);
+
+/* Workspace bytes dsa_sparse_attn_bwd needs (D, and an inverted index of idx). */
+size_t dsa_sparse_attn_bwd_workspace_size(int batch, int seqlen, int h_q, int topk);
+
+/*
+ * dsa_sparse_attn_bwd -- gradients of dsa_sparse_attn_fwd's output with
+ * respect to q, k and v, given dout, the forward's o and lse, and the same
+ * idx.  Every occurrence of a position in a query's list counts (a position
+ * listed twice receives both contributions); entries outside [0, seqlen),
+ * -1 included, are skipped.
+ *   q, k, v, o, dout, idx: as in dsa_sparse_attn_fwd, dtype dt (read)
+ *   lse : [batch, h_q, seqlen] fp32 contiguous from the forward (read)
+ *   dq  : [batch, seqlen, h_q, d_qk] fp32 (written)
+ *   dk  : [batch, seqlen, h_kv, d_qk] fp32, dv: [batch, seqlen, h_kv, d_v] fp32
+ *         (written; positions no query lists get zeros)
+ * dk and dv sum over the queries that list a position in an order set by
+ * atomic slot claims, so they are reproducible up to fp32 rounding only.
+ * Errors: HCA_ERR_INVALID for bad pointers, sizes or overlaps;
+ * HCA_ERR_WORKSPACE for a missing or short workspace.
+ * Supported: fp32 and bf16, d_qk and d_v <= 512 (multiples of 4), any
+ * h_q / h_kv, topk <= 4096.
+ */
+hca_status_t dsa_sparse_attn_bwd(hca_dtype_t dt,
+                                 const void* q, hca_strides_t sq,
+                                 const void* k, hca_strides_t sk,
+                                 const void* v, hca_strides_t sv,
+                                 const int32_t* idx,
+                                 const void* o, hca_strides_t so,
+                                 const float* lse,
+                                 const void* dout, hca_strides_t sdout,
+                                 float* dq, hca_strides_t sdq,
+                                 float* dk, hca_strides_t sdk,
+                                 float* dv, hca_strides_t sdv,
+                                 int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v,
+                                 int topk, float scale,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

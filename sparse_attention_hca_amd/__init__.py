@@ -1,4 +1,4 @@
-"""Python binding of libhca.so: HCA / DSA forward attention for MI355X (gfx950).
+"""Python binding of libhca.so: HCA / DSA attention (forward, decode upkeep, backward) for MI355X (gfx950).
 
 Each function here has the name of the C entry point it wraps and only
 marshals arguments: it reads device pointers, strides and sizes from torch
@@ -29,6 +29,8 @@ EXPORTS = (
     "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd", "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
+    "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "dsa_sparse_attn_bwd_workspace_size",
+    "dsa_sparse_attn_bwd",
 )
 
 
@@ -80,6 +82,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_index_topk_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, SZ, P]
     lib.dsa_sparse_attn_decode.restype = I
     lib.dsa_sparse_attn_decode.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
+    lib.hca_attn_bwd_workspace_size.restype = SZ
+    lib.hca_attn_bwd_workspace_size.argtypes = [I, I, I]
+    lib.hca_attn_bwd.restype = I
+    lib.hca_attn_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P, S, P, S, P, S,
+                                 I, I, I64, I, I64, I, I, I, I, I, I, F, P, SZ, P]
+    lib.hca_compress_kv_bwd.restype = I
+    lib.hca_compress_kv_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, P, P, S, P, S, P, P, I, I, I, I, I, P]
+    lib.dsa_sparse_attn_bwd_workspace_size.restype = SZ
+    lib.dsa_sparse_attn_bwd_workspace_size.argtypes = [I, I, I, I]
+    lib.dsa_sparse_attn_bwd.restype = I
+    lib.dsa_sparse_attn_bwd.argtypes = [I, P, S, P, S, P, S, P, P, S, P, P, S, P, S, P, S, P, S,
+                                        I, I, I, I, I, I, I, F, P, SZ, P]
     _lib = lib
     return lib
 
@@ -295,10 +309,110 @@ def dsa_sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, id
     return o, lse
 
 
+def hca_attn_bwd_workspace_size(batch: int, seqlen_q: int, h_q: int) -> int:
+    return load_library().hca_attn_bwd_workspace_size(batch, seqlen_q, h_q)
+
+
+def hca_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional[torch.Tensor],
+                 vc: Optional[torch.Tensor], o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, *, window: int,
+                 block: int, scale: Optional[float] = None, q_pos0: int = 0, kv_pos0: int = 0,
+                 workspace: Optional[torch.Tensor] = None):
+    """Gradients of hca_attn_fwd's output given dout, the forward's o and lse:
+    returns fp32 (dq, dk, dv, dkc, dvc) shaped like q, k, v, kc, vc (dkc/dvc None without entries)."""
+    lib = load_library()
+    _dev(q, k, v, kc, vc, o, lse, dout)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    nb = 0 if kc is None else kc.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dkc = torch.empty(kc.shape, **f32) if nb else None
+    dvc = torch.empty(vc.shape, **f32) if nb else None
+    if workspace is None:
+        workspace = torch.empty(lib.hca_attn_bwd_workspace_size(B, Sq, Hq), dtype=torch.uint8, device=q.device)
+    zs = Strides(0, 0, 0)
+    st = lambda t: zs if t is None else _strides(t)
+    _check(lib.hca_attn_bwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                            _ptr(kc), st(kc), _ptr(vc), st(vc), _ptr(o), _strides(o), _ptr(lse), _ptr(dout),
+                            _strides(dout), _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                            _ptr(dkc), st(dkc), _ptr(dvc), st(dvc), B, Sq, q_pos0, Skv, kv_pos0, nb, Hq, Hkv, d,
+                            block, window, float(scale), _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, dkc, dvc
+
+
+def hca_compress_kv_bwd(k: torch.Tensor, v: torch.Tensor, dkc: torch.Tensor, dvc: torch.Tensor, w_k: torch.Tensor,
+                        w_v: torch.Tensor, block: int, dk: Optional[torch.Tensor] = None,
+                        dv: Optional[torch.Tensor] = None):
+    """Backward of hca_compress_kv: adds w * dkc (w * dvc) into the fp32 dk (dv) over the whole blocks
+    (zeros are allocated when dk/dv are not given) and returns (dk, dv, dw_k, dw_v)."""
+    lib = load_library()
+    _dev(k, v, dkc, dvc, w_k, w_v, dk, dv)
+    B, S, H, d = k.shape
+    f32 = dict(dtype=torch.float32, device=k.device)
+    if dk is None:
+        dk = torch.zeros(k.shape, **f32)
+    if dv is None:
+        dv = torch.zeros(v.shape, **f32)
+    for t in (dkc, dvc, dk, dv):
+        if t.dtype != torch.float32:
+            raise ValueError("gradients must be float32")
+    w_k = w_k.contiguous()
+    w_v = w_v.contiguous()
+    dw_k = torch.empty((H, block), **f32)
+    dw_v = torch.empty((H, block), **f32)
+    _check(lib.hca_compress_kv_bwd(_dt(k), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(dkc), _strides(dkc),
+                                   _ptr(dvc), _strides(dvc), _ptr(w_k), _ptr(w_v), _ptr(dk), _strides(dk), _ptr(dv),
+                                   _strides(dv), _ptr(dw_k), _ptr(dw_v), B, S, H, d, block, _stream()))
+    return dk, dv, dw_k, dw_v
+
+
+def dsa_sparse_attn_bwd_workspace_size(batch: int, seqlen: int, h_q: int, topk: int) -> int:
+    return load_library().dsa_sparse_attn_bwd_workspace_size(batch, seqlen, h_q, topk)
+
+
+def dsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, o: torch.Tensor,
+                        lse: torch.Tensor, dout: torch.Tensor, scale: Optional[float] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Gradients of dsa_sparse_attn_fwd's output given dout, the forward's o and lse and the same idx:
+    returns fp32 (dq, dk, dv) shaped like q, k, v."""
+    lib = load_library()
+    _dev(q, k, v, idx, o, lse, dout)
+    B, S, Hq, dqk = q.shape
+    Hkv, dv_ = k.shape[2], v.shape[3]
+    topk = idx.shape[2]
+    if not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be contiguous int32 [B, S, topk]")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    if workspace is None:
+        workspace = torch.empty(lib.dsa_sparse_attn_bwd_workspace_size(B, S, Hq, topk), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib.dsa_sparse_attn_bwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                   _ptr(idx), _ptr(o), _strides(o), _ptr(lse), _ptr(dout), _strides(dout),
+                                   _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                                   B, S, Hq, Hkv, dqk, dv_, topk, float(scale), _ptr(workspace), workspace.numel(),
+                                   _stream()))
+    return dq, dk, dv
+
+
 __all__ = [
     "load_library", "HcaError", "Strides", "EXPORTS",
     "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd",
     "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
+    "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd",
+    "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
 ]

@@ -23,6 +23,7 @@ SOURCES = [
     "attn_decode512.hip",
     "dsa_index_topk.hip",
     "dsa_attn256.hip",
+    "attn_bwd.hip",
     "hca_abi.cpp",
 ]
 

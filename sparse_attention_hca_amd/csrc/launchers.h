@@ -47,6 +47,34 @@ hipError_t launch_attn_prefill512(const AttnArgs& a, hipStream_t st);
 size_t decode512_workspace_bytes(int batch, int h_q, int h_kv, int n_keys);
 hipError_t launch_attn_decode512(const AttnArgs& a, void* ws, hipStream_t st);
 
+// Backward (fp32 gradients).  One struct for the HCA and DSA attention
+// backward; the DSA fields (idx, inverted index) are unused by HCA.
+struct BwdArgs {
+  const void *q, *k, *v, *kc, *vc, *o, *dout;
+  LStrides sq, sk, sv, skc, svc, so, sdo;
+  const float* lse;  // [batch, h_q, seqlen_q] natural log, from the forward
+  float* delta;      // workspace: <dO, O> per (query, head)
+  float *dq, *dk, *dv, *dkc, *dvc;
+  LStrides sdq, sdk, sdv, sdkc, sdvc;
+  int batch, seqlen_q, seqlen_kv, n_blocks, h_q, h_kv, d, d_v, block, window, topk;
+  int64_t q_pos0, kv_pos0;
+  float scale;
+  const int32_t* idx;       // DSA selections [batch, seqlen_q, topk]
+  const int32_t* inv_off;   // inverted index: offsets [batch, seqlen_kv + 1]
+  int32_t* inv_list;        //                 query lists [batch, inv_ld]
+  int64_t inv_ld;
+};
+constexpr int kBwdMaxKeys = 16384;  // keys per query of the dq kernel (LDS row of ds)
+size_t hca_bwd_workspace_bytes(int batch, int seqlen_q, int h_q);
+hipError_t launch_hca_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
+size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk);
+hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
+// dk/dv (fp32, accumulated) += the compressor's backward of dkc/dvc; dw_k/dw_v written.
+hipError_t launch_compress_bwd(int dt, const void* k, LStrides sk, const void* v, LStrides sv, const float* dkc,
+                               LStrides sdkc, const float* dvc, LStrides sdvc, const float* wk, const float* wv,
+                               float* dk, LStrides sdk, float* dv, LStrides sdv, float* dwk, float* dwv, int batch,
+                               int seqlen, int h, int d, int block, hipStream_t st);
+
 // DSA
 size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk);
 hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,

@@ -12,6 +12,13 @@ bfloat16 with round-to-nearest-even when the workload is bf16):
   and w can be redrawn from the sub-stream (seed, b, t, attempt) so that a
   caller can replace rows whose top-k boundary is too close to call.
 
+* Free-standing tensors (gradients flowing into a backward call, inputs of
+  other shapes): ``make_normal(shape, seed, std, bf16)``, one generator per
+  call.
+* Index lists for sparse attention: ``make_index_lists`` draws, per row t, a
+  random set of distinct positions <= t (a random permutation's prefix),
+  optionally repeats some entries of the row, and pads with -1.
+
 Large arrays are drawn in chunks; a Generator's normal stream does not depend
 on how the draw is split, so chunking does not change any value.
 """
@@ -106,3 +113,29 @@ def redraw_dsa_rows(inp: dict, rows, attempt: int) -> None:
         inp["qI"][b, t] = r.standard_normal((cfg.h_i, cfg.d_i), dtype=np.float32)
         inp["w"][b, t] = r.standard_normal(cfg.h_i, dtype=np.float32)
         inp["redraws"][b, t] = attempt
+
+
+def make_normal(shape, seed: int, std: float = 1.0, bf16: bool = False) -> np.ndarray:
+    """N(0, std^2) float32 draws of the given shape (bf16 bit patterns when bf16)."""
+    return _normal(np.random.default_rng(seed), tuple(shape), std, bf16)
+
+
+def make_index_lists(batch: int, seqlen: int, topk: int, seed: int, n_valid=None, dup_per_row: int = 0
+                     ) -> np.ndarray:
+    """int32 [batch, seqlen, topk]: row t lists min(t + 1, n_valid(t), topk) distinct positions in [0, t]
+    in random order (n_valid: an int, or None for topk), then, when dup_per_row > 0, that many of its
+    entries are overwritten with copies of other entries of the same row (rows with at least two
+    entries), and the rest of the row is -1."""
+    rng = np.random.default_rng(seed)
+    out = np.full((batch, seqlen, topk), -1, dtype=np.int32)
+    cap = topk if n_valid is None else min(int(n_valid), topk)
+    for b in range(batch):
+        for t in range(seqlen):
+            n = min(t + 1, cap)
+            row = rng.permutation(t + 1)[:n].astype(np.int32)
+            if dup_per_row and n >= 2:
+                for _ in range(dup_per_row):
+                    src, dst = rng.choice(n, 2, replace=False)
+                    row[dst] = row[src]
+            out[b, t, :n] = row
+    return out

@@ -183,3 +183,80 @@ def test_binding_fails_loudly_without_gpu_tensors():
     w = torch.zeros(1, 128)
     with pytest.raises(ValueError):
         hca.hca_compress_kv(x, x, w, w, 128)
+
+
+def test_hca_bwd_rejects_bad_arguments():
+    lib = _lib()
+    need = lib.hca_attn_bwd_workspace_size(1, 300, 4)
+    assert need >= 300 * 4 * 4
+    assert lib.hca_attn_bwd_workspace_size(0, 300, 4) == 0
+    g = [ctypes.c_void_p((1 << 34) + (i << 28)) for i in range(5)]   # distinct, non-overlapping gradient buffers
+    sf = S(0, 128 * 4, 128)
+
+    def call(**kw):
+        return lib.hca_attn_bwd(kw.get("dt", 0), kw.get("q", FAKE), sf, FAKE, sf, FAKE, sf, FAKE, S(0, 128, 128),
+                                FAKE, S(0, 128, 128), FAKE, sf, kw.get("lse", ctypes.c_void_p(1 << 33)), FAKE, sf,
+                                kw.get("dq", g[0]), sf, kw.get("dk", g[1]), sf, g[2], sf, g[3], S(0, 128, 128), g[4],
+                                S(0, 128, 128), 1, kw.get("sq", 300), 0, kw.get("skv", 300), kw.get("kvp", 0),
+                                kw.get("nb", 4), 4, kw.get("hkv", 4), kw.get("d", 128), 64, kw.get("window", 64),
+                                0.1, kw.get("ws", ctypes.c_void_p(1 << 40)), kw.get("wsb", need), None)
+    assert call(dt=3) == hca.HCA_ERR_INVALID
+    assert call(hkv=3) == hca.HCA_ERR_INVALID
+    assert call(window=0) == hca.HCA_ERR_INVALID
+    assert call(q=None) == hca.HCA_ERR_INVALID
+    assert call(lse=None) == hca.HCA_ERR_INVALID
+    assert call(d=516) == hca.HCA_ERR_UNSUPPORTED
+    assert call(kvp=10) == hca.HCA_ERR_INVALID              # raw K/V start after query 0's window
+    assert call(nb=2) == hca.HCA_ERR_INVALID                # last query (t = 299) needs floor(236 / 64) = 3 entries
+    assert "compressed" in hca.hca_last_error()
+    assert call(dq=FAKE) == hca.HCA_ERR_INVALID             # gradient aliases an input
+    assert "overlap" in hca.hca_last_error()
+    assert call(dk=g[0]) == hca.HCA_ERR_INVALID             # two gradients alias
+    assert call(wsb=need - 1) == hca.HCA_ERR_WORKSPACE
+    assert call(ws=None) == hca.HCA_ERR_WORKSPACE
+    assert call(window=20000, sq=20000, skv=20000) == hca.HCA_ERR_UNSUPPORTED   # > 16384 keys per query
+
+
+def test_compress_bwd_rejects_bad_arguments():
+    lib = _lib()
+    sf = S(0, 512, 512)
+
+    def call(**kw):
+        return lib.hca_compress_kv_bwd(kw.get("dt", 1), kw.get("k", FAKE), S(0, 512, 512), FAKE, S(0, 512, 512),
+                                       ctypes.c_void_p(1 << 30), sf, ctypes.c_void_p(1 << 31), sf,
+                                       kw.get("wk", FAKE), FAKE, kw.get("dk", ctypes.c_void_p(1 << 34)), sf,
+                                       ctypes.c_void_p(1 << 35), sf, kw.get("dwk", ctypes.c_void_p(1 << 36)),
+                                       ctypes.c_void_p(1 << 37), 1, 256, 1, kw.get("d", 512), kw.get("block", 128),
+                                       None)
+    assert call(dt=4) == hca.HCA_ERR_INVALID
+    assert call(k=None) == hca.HCA_ERR_INVALID
+    assert call(wk=None) == hca.HCA_ERR_INVALID
+    assert call(dwk=None) == hca.HCA_ERR_INVALID
+    assert call(block=0) == hca.HCA_ERR_INVALID
+    assert call(d=510) == hca.HCA_ERR_UNSUPPORTED
+    assert call(dk=ctypes.c_void_p(1 << 35)) == hca.HCA_ERR_INVALID    # dk aliases dv
+    assert call(dk=ctypes.c_void_p(1 << 30)) == hca.HCA_ERR_INVALID    # dk aliases dkc
+
+
+def test_dsa_bwd_rejects_bad_arguments():
+    lib = _lib()
+    need = lib.dsa_sparse_attn_bwd_workspace_size(1, 100, 8, 16)
+    assert need >= 100 * 8 * 4 + 100 * 16 * 4
+    sq = S(0, 8 * 64, 64)
+    skv = S(0, 2 * 64, 64)
+
+    def call(**kw):
+        return lib.dsa_sparse_attn_bwd(kw.get("dt", 0), FAKE, sq, FAKE, skv, FAKE, skv,
+                                       kw.get("idx", ctypes.c_void_p(1 << 33)), FAKE, sq, ctypes.c_void_p(1 << 32),
+                                       FAKE, sq, kw.get("dq", ctypes.c_void_p(1 << 34)), sq,
+                                       kw.get("dk", ctypes.c_void_p(1 << 35)), skv, ctypes.c_void_p(1 << 36), skv,
+                                       1, 100, 8, kw.get("hkv", 2), kw.get("d", 64), 64, kw.get("k", 16), 0.125,
+                                       kw.get("ws", ctypes.c_void_p(1 << 40)), kw.get("wsb", need), None)
+    assert call(dt=2) == hca.HCA_ERR_INVALID
+    assert call(hkv=3) == hca.HCA_ERR_INVALID
+    assert call(idx=None) == hca.HCA_ERR_INVALID
+    assert call(d=1024) == hca.HCA_ERR_UNSUPPORTED
+    assert call(k=4097) == hca.HCA_ERR_UNSUPPORTED
+    assert call(dq=FAKE) == hca.HCA_ERR_INVALID
+    assert call(dk=ctypes.c_void_p(1 << 34)) == hca.HCA_ERR_INVALID
+    assert call(wsb=need - 1) == hca.HCA_ERR_WORKSPACE

@@ -1,0 +1,255 @@
+"""GPU parity of the backward path -- HCA attention, the block compressor and
+DSA sparse attention -- against the float64 oracle gradients on the same seeded
+inputs, called through the C-ABI.
+
+fp32 cases feed the kernels the oracle's own forward (o, lse rounded to fp32),
+so they test the backward arithmetic alone at the fp32 tolerance.  bf16 cases
+chain the library's forward and backward and compare with the oracle's
+gradients of the exact (fp64) forward at the bf16 tolerance."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import BF16_TOL, F32_TOL, dev_bf16, dev_f32, f64, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+hca = pytest.importorskip("sparse_attention_hca_amd")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, bf16):
+    return dev_bf16(x) if bf16 else dev_f32(x)
+
+
+def _softmax_w(h, block, seed):
+    z = synth.make_normal((h, block), seed).astype(np.float64)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def _check(name, got, ref, tol):
+    err = rel_err(host(got), ref)
+    _say(f"  {name}: rel err {err:.2e} (tol {tol:.0e})")
+    assert err < tol, name
+
+
+# ------------------------------------------------------------------ HCA attention
+
+@pytest.mark.parametrize("B,Sq,Skv,q_pos0,kv_pos0,Hq,Hkv,d,block,window,nb", [
+    (2, 300, 300, 0, 0, 4, 2, 64, 64, 48, 4),         # prefill, GQA, ragged tail, block > window
+    (1, 130, 190, 400, 340, 2, 1, 128, 32, 61, 15),   # a chunk mid-sequence, raw K/V starting before it
+    (1, 1, 40, 999, 960, 8, 8, 256, 128, 40, 7),      # one decode query
+    (1, 70, 70, 0, 0, 2, 2, 512, 16, 200, 0),         # window covers everything: no compressed entry
+])
+def test_hca_attn_bwd_f32(B, Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, d, block, window, nb):
+    _say("hca bwd f32", B, Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, d, block, window, nb)
+    q = synth.make_normal((B, Sq, Hq, d), 11)
+    k = synth.make_normal((B, Skv, Hkv, d), 12)
+    v = synth.make_normal((B, Skv, Hkv, d), 13)
+    kc = synth.make_normal((B, nb, Hkv, d), 14)
+    vc = synth.make_normal((B, nb, Hkv, d), 15)
+    dout = synth.make_normal((B, Sq, Hq, d), 16)
+    scale = float(1.0 / np.sqrt(d))
+    kw = dict(window=window, block=block, scale=scale, q_pos0=q_pos0, kv_pos0=kv_pos0)
+    args64 = [x.astype(np.float64) for x in (q, k, v, kc, vc)]
+    o, lse = oracle.hca_attention(*args64, **kw)
+    ref = oracle.hca_attention_bwd(*args64, dout.astype(np.float64), **kw)
+    dkc_dev = dev_f32(kc) if nb else None
+    dvc_dev = dev_f32(vc) if nb else None
+    got = hca.hca_attn_bwd(dev_f32(q), dev_f32(k), dev_f32(v), dkc_dev, dvc_dev, dev_f32(o), dev_f32(lse),
+                           dev_f32(dout), **kw)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv", "dkc", "dvc"), got, ref):
+        if r.size == 0:
+            assert g is None
+            continue
+        _check(name, g, r, F32_TOL)
+
+
+def test_hca_attn_bwd_unseen_rows_are_zero_and_strided_views_work():
+    """Raw rows past the last query and compressed entries no query reaches
+    get zero gradients; inputs and gradients may be head-strided views."""
+    B, S, H, d, block, window, nb = 1, 200, 2, 64, 32, 40, 8
+    q = synth.make_normal((B, S, H, d), 21)
+    kv = synth.make_normal((B, S + 30, 2 * H, d), 22)       # K and V interleaved per head, 30 extra rows
+    kc = synth.make_normal((B, nb, H, d), 23)
+    dout = synth.make_normal((B, S, H, d), 24)
+    k, v = kv[:, :, :H], kv[:, :, H:]
+    kw = dict(window=window, block=block, scale=0.125)
+    o, lse = oracle.hca_attention(q, k, v, kc, kc, **kw)
+    ref = oracle.hca_attention_bwd(q, k, v, kc, kc, dout, **kw)
+    kv_dev = dev_f32(kv)
+    got = hca.hca_attn_bwd(dev_f32(q), kv_dev[:, :, :H], kv_dev[:, :, H:], dev_f32(kc), dev_f32(kc), dev_f32(o),
+                           dev_f32(lse), dev_f32(dout), **kw)
+    torch.cuda.synchronize()
+    dq, dk, dv, dkc, dvc = (host(x) for x in got)
+    assert (dk[:, S:] == 0).all() and (dv[:, S:] == 0).all()
+    # last query t = 199: lo = 160 -> entries 0..4 seen; 5..7 never
+    assert (dkc[:, 5:] == 0).all() and (dvc[:, 5:] == 0).all()
+    for name, g, r in zip(("dq", "dk", "dv", "dkc", "dvc"), (dq, dk, dv, dkc, dvc), ref):
+        err = rel_err(g, r)
+        _say(f"  {name}: {err:.2e}")
+        assert err < F32_TOL, name
+
+
+@pytest.mark.parametrize("S,H,d,block,window", [(600, 2, 512, 128, 128), (333, 3, 256, 64, 100)])
+def test_hca_training_step_bf16_chain(S, H, d, block, window):
+    """bf16 forward (compression + attention) then backward (attention, then the
+    compressor into the raw K/V gradients and the weights) against the oracle's
+    gradients of the whole chain."""
+    _say("hca chain bf16", S, H, d, block, window)
+    B = 1
+    q = synth.make_normal((B, S, H, d), 31, bf16=True)
+    k = synth.make_normal((B, S, H, d), 32, bf16=True)
+    v = synth.make_normal((B, S, H, d), 33, bf16=True)
+    dout = synth.make_normal((B, S, H, d), 34, bf16=True)
+    wk, wv = _softmax_w(H, block, 35), _softmax_w(H, block, 36)
+    scale = float(1.0 / np.sqrt(d))
+    kw = dict(window=window, block=block, scale=scale)
+    # library: forward then backward
+    qd, kd, vd, gd = (dev_bf16(x) for x in (q, k, v, dout))
+    wkd, wvd = dev_f32(wk), dev_f32(wv)
+    kcd, vcd = hca.hca_compress_kv(kd, vd, wkd, wvd, block)
+    o, lse = hca.hca_attn_fwd(qd, kd, vd, kcd, vcd, **kw)
+    dq, dk, dv, dkc, dvc = hca.hca_attn_bwd(qd, kd, vd, kcd, vcd, o, lse, gd, **kw)
+    dk, dv, dwk, dwv = hca.hca_compress_kv_bwd(kd, vd, dkc, dvc, wkd, wvd, block, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    # oracle
+    q64, k64, v64, g64 = (f64(x, True) for x in (q, k, v, dout))
+    kc64, vc64 = oracle.compress_kv(k64, wk, block), oracle.compress_kv(v64, wv, block)
+    rq, rk, rv, rkc, rvc = oracle.hca_attention_bwd(q64, k64, v64, kc64, vc64, g64, **kw)
+    ck, rwk = oracle.compress_kv_bwd(k64, wk, rkc, block)
+    cv, rwv = oracle.compress_kv_bwd(v64, wv, rvc, block)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk + ck), ("dv", dv, rv + cv), ("dkc", dkc, rkc),
+                       ("dvc", dvc, rvc), ("dw_k", dwk, rwk), ("dw_v", dwv, rwv)):
+        _check(name, g, r, BF16_TOL)
+
+
+# ------------------------------------------------------------------ compressor
+
+@pytest.mark.parametrize("dtype,S,H,d,block", [("f32", 100, 2, 64, 7), ("bf16", 1000, 3, 512, 128),
+                                               ("f32", 256, 1, 128, 1), ("bf16", 50, 2, 256, 64)])
+def test_compress_kv_bwd(dtype, S, H, d, block):
+    """dk/dv accumulate onto what they held; rows past the last whole block keep it."""
+    _say("compress bwd", dtype, S, H, d, block)
+    bf = dtype == "bf16"
+    B, nb = 2, S // block
+    k = synth.make_normal((B, S, H, d), 41, bf16=bf)
+    v = synth.make_normal((B, S, H, d), 42, bf16=bf)
+    dkc = synth.make_normal((B, nb, H, d), 43)
+    dvc = synth.make_normal((B, nb, H, d), 44)
+    base_k = synth.make_normal((B, S, H, d), 45)
+    base_v = synth.make_normal((B, S, H, d), 46)
+    wk, wv = _softmax_w(H, block, 47), _softmax_w(H, block, 48)
+    dk, dv, dwk, dwv = hca.hca_compress_kv_bwd(_dev(k, bf), _dev(v, bf), dev_f32(dkc), dev_f32(dvc), dev_f32(wk),
+                                               dev_f32(wv), block, dk=dev_f32(base_k), dv=dev_f32(base_v))
+    torch.cuda.synchronize()
+    rk, rwk = oracle.compress_kv_bwd(f64(k, bf), wk, dkc, block)
+    rv, rwv = oracle.compress_kv_bwd(f64(v, bf), wv, dvc, block)
+    hk, hv = host(dk), host(dv)
+    assert (hk[:, nb * block:] == base_k[:, nb * block:]).all()
+    for name, g, r in (("dk", hk, rk + base_k), ("dv", hv, rv + base_v), ("dw_k", host(dwk), rwk),
+                       ("dw_v", host(dwv), rwv)):
+        err = rel_err(g, r)
+        _say(f"  {name}: {err:.2e}")
+        assert err < F32_TOL, name      # fp32 arithmetic on exact (bf16-representable) inputs
+
+
+# ------------------------------------------------------------------ DSA sparse attention
+
+def _oracle_dsa_fwd(q, k, v, idx, scale):
+    """Oracle forward per KV head (the oracle's sparse_attention reads one KV head)."""
+    B, S, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    group = Hq // Hkv
+    o = np.zeros((B, S, Hq, v.shape[3]))
+    lse = np.zeros((B, Hq, S))
+    for g in range(Hkv):
+        hs = slice(g * group, (g + 1) * group)
+        og, lg = oracle.sparse_attention(q[:, :, hs], k[:, :, g:g + 1], v[:, :, g:g + 1], idx, scale)
+        o[:, :, hs], lse[:, hs] = og, lg
+    return o, lse
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,dqk,dv,topk,n_valid,dup", [
+    (2, 200, 4, 2, 64, 32, 24, 20, 0),       # GQA, -1 padding after 20 entries, d_v != d_qk
+    (1, 150, 6, 1, 256, 256, 40, None, 3),   # duplicates in every row with >= 2 entries
+    (1, 97, 2, 2, 128, 64, 128, None, 0),    # topk > S: every row lists its whole causal prefix
+])
+def test_dsa_sparse_attn_bwd_f32(B, S, Hq, Hkv, dqk, dv, topk, n_valid, dup):
+    _say("dsa bwd f32", B, S, Hq, Hkv, dqk, dv, topk, n_valid, dup)
+    q = synth.make_normal((B, S, Hq, dqk), 51).astype(np.float64)
+    k = synth.make_normal((B, S, Hkv, dqk), 52).astype(np.float64)
+    v = synth.make_normal((B, S, Hkv, dv), 53).astype(np.float64)
+    dout = synth.make_normal((B, S, Hq, dv), 54).astype(np.float64)
+    idx = synth.make_index_lists(B, S, topk, seed=55, n_valid=n_valid, dup_per_row=dup)
+    scale = float(1.0 / np.sqrt(dqk))
+    o, lse = _oracle_dsa_fwd(q, k, v, idx, scale)
+    rq, rk, rv = oracle.sparse_attention_bwd(q, k, v, idx, scale, dout)
+    got = hca.dsa_sparse_attn_bwd(dev_f32(q), dev_f32(k), dev_f32(v), torch.from_numpy(idx).cuda(), dev_f32(o),
+                                  dev_f32(lse), dev_f32(dout), scale=scale)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), got, (rq, rk, rv)):
+        _check(name, g, r, F32_TOL)
+
+
+def test_dsa_bwd_skips_empty_and_out_of_range_entries():
+    """A row whose list holds no valid entry (forward: o = 0, lse = -inf) gets
+    dq = 0 and adds nothing to dk/dv, whatever its dout; entries at or past
+    seqlen are skipped.  The expected values are the oracle's with that row's
+    dout set to zero (every gradient is linear in dout)."""
+    B, S, Hq, d, topk = 1, 80, 4, 64, 16
+    q = synth.make_normal((B, S, Hq, d), 61).astype(np.float64)
+    k = synth.make_normal((B, S, 1, d), 62).astype(np.float64)
+    v = synth.make_normal((B, S, 1, d), 63).astype(np.float64)
+    dout = synth.make_normal((B, S, Hq, d), 64).astype(np.float64)
+    idx = synth.make_index_lists(B, S, topk, seed=65)
+    scale = 0.125
+    o, lse = _oracle_dsa_fwd(q, k, v, idx, scale)
+    dz = dout.copy()
+    dz[0, 30] = 0.0
+    rq, rk, rv = oracle.sparse_attention_bwd(q, k, v, idx, scale, dz)
+    bad = idx.copy()
+    bad[0, 30] = -1                      # empty row
+    o[0, 30], lse[0, :, 30] = 0.0, -np.inf
+    bad[0, 5, 10] = S + 7                # row 5 lists 6 valid entries then -1s: one padding slot out of range
+    got = hca.dsa_sparse_attn_bwd(dev_f32(q), dev_f32(k), dev_f32(v), torch.from_numpy(bad).cuda(), dev_f32(o),
+                                  dev_f32(lse), dev_f32(dout), scale=scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = (host(x) for x in got)
+    assert (dq[0, 30] == 0).all()
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        err = rel_err(g, r)
+        _say(f"  {name}: {err:.2e}")
+        assert err < F32_TOL, name
+
+
+@pytest.mark.parametrize("S,topk", [(256, 64), (300, 256)])
+def test_dsa_training_step_bf16_chain(S, topk):
+    """bf16 DSA forward (64 query heads on one KV head, d 256) then backward,
+    against the oracle's gradients."""
+    _say("dsa chain bf16", S, topk)
+    B, Hq, d = 1, 64, 256
+    q = synth.make_normal((B, S, Hq, d), 71, bf16=True)
+    k = synth.make_normal((B, S, 1, d), 72, bf16=True)
+    v = synth.make_normal((B, S, 1, d), 73, bf16=True)
+    dout = synth.make_normal((B, S, Hq, d), 74, bf16=True)
+    idx = synth.make_index_lists(B, S, topk, seed=75)
+    scale = float(1.0 / np.sqrt(d))
+    qd, kd, vd, gd = (dev_bf16(x) for x in (q, k, v, dout))
+    idd = torch.from_numpy(idx).cuda()
+    o, lse = hca.dsa_sparse_attn_fwd(qd, kd, vd, idd, scale=scale)
+    dq, dk, dv = hca.dsa_sparse_attn_bwd(qd, kd, vd, idd, o, lse, gd, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.sparse_attention_bwd(f64(q, True), f64(k, True), f64(v, True), idx, scale, f64(dout, True))
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check(name, g, r, BF16_TOL)

@@ -38,3 +38,18 @@ def test_dsa_row_redraw_is_local():
     c = synth.make_dsa(cfg)
     synth.redraw_dsa_rows(c, [(0, 10), (0, 33)], attempt=1)
     np.testing.assert_array_equal(b["qI"], c["qI"])
+
+
+def test_index_lists_are_causal_distinct_and_padded():
+    idx = synth.make_index_lists(2, 50, 8, seed=4, n_valid=6)
+    assert idx.shape == (2, 50, 8) and idx.dtype == np.int32
+    for b in range(2):
+        for t in range(50):
+            row = idx[b, t]
+            n = min(t + 1, 6)
+            assert (row[n:] == -1).all()
+            assert len(set(row[:n].tolist())) == n and row[:n].min() >= 0 and row[:n].max() <= t
+    dup = synth.make_index_lists(1, 40, 8, seed=4, dup_per_row=2)
+    assert any(len(set(dup[0, t][dup[0, t] >= 0].tolist())) < min(t + 1, 8) for t in range(40))
+    assert (dup[dup >= 0] <= np.arange(40)[None, :, None].repeat(8, 2)[dup >= 0]).all()
+    np.testing.assert_array_equal(synth.make_index_lists(2, 50, 8, seed=4, n_valid=6), idx)
