@@ -289,8 +289,15 @@ hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
  * key/value gradients (see dsa_sparse_attn_bwd).
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes hca_attn_bwd needs (D per query and head). */
-size_t hca_attn_bwd_workspace_size(int batch, int seqlen_q, int h_q);
+/*
+ * Workspace bytes hca_attn_bwd needs for these arguments (the values that will
+ * be passed to it; 0 for invalid sizes): D per query and head and, on the
+ * bf16 / head_dim 512 path, fp32 partial gradients of the compressed entries
+ * (one 64-entry x 512 block per chunk of at most max(32, seqlen_q / 1024)
+ * query tiles of 32 that see the block).
+ */
+size_t hca_attn_bwd_workspace_size(hca_dtype_t dt, int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q,
+                                   int h_kv, int head_dim, int block, int window);
 
 /*
  * hca_attn_bwd -- gradients of hca_attn_fwd's output o with respect to q, the
@@ -308,8 +315,11 @@ size_t hca_attn_bwd_workspace_size(int batch, int seqlen_q, int h_q);
  * hca_compress_kv_bwd, which adds its share into dk/dv.
  * Errors: as hca_attn_fwd; HCA_ERR_INVALID when a gradient overlaps an input
  * or another gradient; HCA_ERR_WORKSPACE for a missing or short workspace.
- * Supported: fp32 and bf16, head_dim <= 512 (multiple of 4), at most 16384
- * keys per query.
+ * Kernels: bf16 with head_dim 512 runs two MFMA kernels (query-tile major
+ * for dq and D, key-tile major for dk/dv/dkc/dvc) and a fixed-order sum of the
+ * compressed-entry partials; other shapes run one-row-per-workgroup kernels.
+ * Supported: fp32 and bf16, head_dim <= 512 (multiple of 4); outside the MFMA
+ * path at most 16384 keys per query.
  */
 hca_status_t hca_attn_bwd(hca_dtype_t dt,
                           const void* q, hca_strides_t sq,

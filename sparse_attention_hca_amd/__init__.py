@@ -83,7 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_sparse_attn_decode.restype = I
     lib.dsa_sparse_attn_decode.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
     lib.hca_attn_bwd_workspace_size.restype = SZ
-    lib.hca_attn_bwd_workspace_size.argtypes = [I, I, I]
+    lib.hca_attn_bwd_workspace_size.argtypes = [I, I, I, I64, I, I, I, I, I, I]
     lib.hca_attn_bwd.restype = I
     lib.hca_attn_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P, S, P, S, P, S,
                                  I, I, I64, I, I64, I, I, I, I, I, I, F, P, SZ, P]
@@ -309,8 +309,11 @@ def dsa_sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, id
     return o, lse
 
 
-def hca_attn_bwd_workspace_size(batch: int, seqlen_q: int, h_q: int) -> int:
-    return load_library().hca_attn_bwd_workspace_size(batch, seqlen_q, h_q)
+def hca_attn_bwd_workspace_size(dtype: torch.dtype, batch: int, seqlen_q: int, q_pos0: int, n_blocks: int, h_q: int,
+                                h_kv: int, head_dim: int, block: int, window: int) -> int:
+    dt = HCA_DTYPE_BF16 if dtype == torch.bfloat16 else HCA_DTYPE_F32
+    return load_library().hca_attn_bwd_workspace_size(dt, batch, seqlen_q, q_pos0, n_blocks, h_q, h_kv, head_dim,
+                                                      block, window)
 
 
 def hca_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional[torch.Tensor],
@@ -335,7 +338,8 @@ def hca_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional
     dkc = torch.empty(kc.shape, **f32) if nb else None
     dvc = torch.empty(vc.shape, **f32) if nb else None
     if workspace is None:
-        workspace = torch.empty(lib.hca_attn_bwd_workspace_size(B, Sq, Hq), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(lib.hca_attn_bwd_workspace_size(_dt(q), B, Sq, q_pos0, nb, Hq, Hkv, d, block, window),
+                                dtype=torch.uint8, device=q.device)
     zs = Strides(0, 0, 0)
     st = lambda t: zs if t is None else _strides(t)
     _check(lib.hca_attn_bwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),

@@ -24,6 +24,7 @@ SOURCES = [
     "dsa_index_topk.hip",
     "dsa_attn256.hip",
     "attn_bwd.hip",
+    "attn_bwd512.hip",
     "hca_abi.cpp",
 ]
 

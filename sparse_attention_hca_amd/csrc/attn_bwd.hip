@@ -394,17 +394,27 @@ hipError_t run_dsa_bwd(const BwdArgs& a, int32_t* cnt, int32_t* cur, hipStream_t
 
 }  // namespace
 
-size_t hca_bwd_workspace_bytes(int batch, int seqlen_q, int h_q) {
+static size_t delta_bytes(int batch, int seqlen_q, int h_q) {
   return ((size_t)batch * h_q * seqlen_q * sizeof(float) + 255) / 256 * 256;
 }
 
+bool hca_bwd_uses_mfma(int dt, int head_dim) { return dt == 1 && head_dim == 512; }
+
+size_t hca_bwd_workspace_bytes(int dt, int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q, int h_kv,
+                               int head_dim, int block, int window) {
+  if (hca_bwd_uses_mfma(dt, head_dim))
+    return hca_bwd512_workspace_bytes(batch, seqlen_q, q_pos0, n_blocks, h_q, h_kv, block, window);
+  return delta_bytes(batch, seqlen_q, h_q);
+}
+
 hipError_t launch_hca_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st) {
+  if (hca_bwd_uses_mfma(dt, a.d)) return launch_hca_attn_bwd512(a, ws, st);
   a.delta = (float*)ws;
   return dt == 1 ? run_hca_bwd<uint16_t>(a, st) : run_hca_bwd<float>(a, st);
 }
 
 size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk) {
-  size_t bytes = hca_bwd_workspace_bytes(batch, seqlen, h_q);                      // delta
+  size_t bytes = delta_bytes(batch, seqlen, h_q);                                  // delta
   bytes += ((size_t)batch * (seqlen + 1) * sizeof(int32_t) + 255) / 256 * 256;      // counts -> offsets
   bytes += ((size_t)batch * seqlen * sizeof(int32_t) + 255) / 256 * 256;            // cursors
   bytes += (size_t)batch * seqlen * topk * sizeof(int32_t);                          // lists
@@ -414,7 +424,7 @@ size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk) {
 hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st) {
   char* p = (char*)ws;
   a.delta = (float*)p;
-  p += hca_bwd_workspace_bytes(a.batch, a.seqlen_q, a.h_q);
+  p += delta_bytes(a.batch, a.seqlen_q, a.h_q);
   int32_t* cnt = (int32_t*)p;
   p += ((size_t)a.batch * (a.seqlen_kv + 1) * sizeof(int32_t) + 255) / 256 * 256;
   int32_t* cur = (int32_t*)p;

@@ -37,6 +37,7 @@
 //     compressed cache.  Within a head, the longest query tiles go first.
 #include "device_common.h"
 #include "launchers.h"
+#include "mfma_asm.h"
 
 namespace hca {
 namespace {
@@ -53,51 +54,12 @@ constexpr int VST = BN * VROW;      // V stage bytes
 constexpr int STAGE = KST + VST;
 constexpr float kGuard = 64.f;  // log2 headroom of the fixed softmax reference
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 struct PrefillParams {
   AttnArgs a;
   int n_qt;   // query tiles per (batch, head)
   int total;  // batch * h_q * n_qt
   float c;    // scale * log2(e)
 };
-
-// 16-byte LDS DMA of one wave: lane l copies 16 bytes from g (per lane) to LDS
-// byte address lds + 16 l (lds travels in M0).  Written as asm so that the
-// compiler does not track it as an LDS store (it would wait for it before
-// unrelated LDS reads); the explicit vmcnt wait and barrier of each tile order
-// DMA and reads.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-
-// The two products are written as inline asm so that S^T accumulates in VGPRs
-// (the softmax reads it) while O^T accumulates in AGPRs: O^T takes all 256
-// AGPRs, and the compiler would otherwise put every MFMA accumulator in AGPRs
-// and spill.  The compiler does not see these as MFMAs, so the wait states
-// the ISA requires around them are explicit: after the last S^T step (its
-// result is read by VALU), before the first O^T step of a tile (P^T was just
-// written by VALU), before an MFMA that reads a VALU-written operand and
-// before O^T is read back.  Back-to-back MFMAs on the same accumulator need
-// none.
-__device__ __forceinline__ void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_s(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_s_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 15" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_o(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void zero_o(f32x16& acc, const bf16x8& z) {
-  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=&a"(acc) : "v"(z));
-}
-__device__ __forceinline__ void mfma_o_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void prefill512_kernel(PrefillParams p) {

@@ -302,9 +302,13 @@ hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float*
   return HCA_OK;
 }
 
-size_t hca_attn_bwd_workspace_size(int batch, int seqlen_q, int h_q) {
-  if (batch <= 0 || seqlen_q <= 0 || h_q <= 0) return 0;
-  return hca::hca_bwd_workspace_bytes(batch, seqlen_q, h_q);
+size_t hca_attn_bwd_workspace_size(hca_dtype_t dt, int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q,
+                                   int h_kv, int head_dim, int block, int window) {
+  if ((dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) || batch <= 0 || seqlen_q <= 0 || h_q <= 0 || h_kv <= 0 ||
+      head_dim <= 0 || n_blocks < 0 || block < 1 || window < 1 || q_pos0 < 0 || q_pos0 + seqlen_q > kPosLimit)
+    return 0;
+  return hca::hca_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen_q, q_pos0, n_blocks, h_q, h_kv,
+                                      head_dim, block, window);
 }
 
 hca_status_t hca_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
@@ -345,7 +349,8 @@ hca_status_t hca_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
   if (lo0 < kv_pos0 || t1 >= kv_pos0 + seqlen_kv)
     return fail(HCA_ERR_INVALID, "hca_attn_bwd: raw K/V must cover every query's window");
   if (lo1 / block > n_blocks) return fail(HCA_ERR_INVALID, "hca_attn_bwd: the last query needs more compressed entries");
-  if (n_keys_of(t1, window, block) > hca::kBwdMaxKeys)
+  const bool mfma = hca::hca_bwd_uses_mfma(dt == HCA_DTYPE_BF16 ? 1 : 0, head_dim);
+  if (!mfma && n_keys_of(t1, window, block) > hca::kBwdMaxKeys)
     return fail(HCA_ERR_UNSUPPORTED, "hca_attn_bwd: at most %d keys per query", hca::kBwdMaxKeys);
   {
     const Range outs[5] = {extent(dq, sdq, batch, seqlen_q, h_q, head_dim, 4),
@@ -367,7 +372,8 @@ hca_status_t hca_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
         if (overlaps(outs[x], outs[y])) return fail(HCA_ERR_INVALID, "hca_attn_bwd: gradients overlap each other");
     }
   }
-  const size_t need = hca::hca_bwd_workspace_bytes(batch, seqlen_q, h_q);
+  const size_t need = hca::hca_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen_q, q_pos0, n_blocks,
+                                                   h_q, h_kv, head_dim, block, window);
   if (!workspace || workspace_bytes < need)
     return fail(HCA_ERR_WORKSPACE, "hca_attn_bwd needs a %zu-byte workspace (got %zu)", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");

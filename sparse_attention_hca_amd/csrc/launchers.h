@@ -64,9 +64,15 @@ struct BwdArgs {
   int32_t* inv_list;        //                 query lists [batch, inv_ld]
   int64_t inv_ld;
 };
-constexpr int kBwdMaxKeys = 16384;  // keys per query of the dq kernel (LDS row of ds)
-size_t hca_bwd_workspace_bytes(int batch, int seqlen_q, int h_q);
+constexpr int kBwdMaxKeys = 16384;  // keys per query of the generic dq kernel (LDS row of ds)
+// bf16 with head_dim 512 runs the MFMA kernels (no key limit); everything else the generic ones.
+bool hca_bwd_uses_mfma(int dt, int head_dim);
+size_t hca_bwd_workspace_bytes(int dt, int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q, int h_kv,
+                               int head_dim, int block, int window);
 hipError_t launch_hca_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
+size_t hca_bwd512_workspace_bytes(int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q, int h_kv,
+                                  int block, int window);
+hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st);
 size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk);
 hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
 // dk/dv (fp32, accumulated) += the compressor's backward of dkc/dvc; dw_k/dw_v written.

@@ -187,9 +187,13 @@ def test_binding_fails_loudly_without_gpu_tensors():
 
 def test_hca_bwd_rejects_bad_arguments():
     lib = _lib()
-    need = lib.hca_attn_bwd_workspace_size(1, 300, 4)
+    need = lib.hca_attn_bwd_workspace_size(0, 1, 300, 0, 4, 4, 4, 128, 64, 64)
     assert need >= 300 * 4 * 4
-    assert lib.hca_attn_bwd_workspace_size(0, 300, 4) == 0
+    assert lib.hca_attn_bwd_workspace_size(0, 0, 300, 0, 4, 4, 4, 128, 64, 64) == 0
+    # bf16 / head_dim 512: D plus the compressed-entry partials; 32K queries, 256 entries, window 128:
+    # entry tiles of 64 start at positions 255, 8447, 16639, 24831 -> 32 + 24 + 16 + 8 chunks of 32 query tiles
+    big = lib.hca_attn_bwd_workspace_size(1, 1, 32768, 0, 256, 16, 16, 512, 128, 128)
+    assert big == 32768 * 16 * 4 + 2 * 16 * (32 + 24 + 16 + 8) * 64 * 512 * 4
     g = [ctypes.c_void_p((1 << 34) + (i << 28)) for i in range(5)]   # distinct, non-overlapping gradient buffers
     sf = S(0, 128 * 4, 128)
 

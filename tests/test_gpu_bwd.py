@@ -134,6 +134,40 @@ def test_hca_training_step_bf16_chain(S, H, d, block, window):
         _check(name, g, r, BF16_TOL)
 
 
+@pytest.mark.parametrize("Sq,Skv,q_pos0,kv_pos0,Hq,Hkv,block,window,nb", [
+    (3000, 3000, 0, 0, 2, 1, 16, 40, 187),       # GQA; compressed tiles cut into several chunks of queries
+    (1100, 1100, 0, 0, 1, 1, 128, 128, 7),       # the c2 block / window at a small length, ragged tiles
+    (130, 190, 400, 340, 2, 2, 32, 61, 15),      # a chunk mid-sequence, raw K/V starting before it
+    (1, 40, 999, 960, 4, 1, 128, 40, 7),         # one decode query
+    (70, 70, 0, 0, 2, 2, 16, 200, 0),            # window covers everything: no compressed entry
+])
+def test_hca_attn_bwd_bf16_512(Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window, nb):
+    """The MFMA path (bf16, head_dim 512): the library's forward, then its
+    backward, against the oracle's gradients on the same bf16 inputs."""
+    _say("hca bwd bf16 d512", Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window, nb)
+    B, d = 1, 512
+    q = synth.make_normal((B, Sq, Hq, d), 81, bf16=True)
+    k = synth.make_normal((B, Skv, Hkv, d), 82, bf16=True)
+    v = synth.make_normal((B, Skv, Hkv, d), 83, bf16=True)
+    kc = synth.make_normal((B, nb, Hkv, d), 84, bf16=True)
+    vc = synth.make_normal((B, nb, Hkv, d), 85, bf16=True)
+    dout = synth.make_normal((B, Sq, Hq, d), 86, bf16=True)
+    scale = float(1.0 / np.sqrt(d))
+    kw = dict(window=window, block=block, scale=scale, q_pos0=q_pos0, kv_pos0=kv_pos0)
+    qd, kd, vd, gd = (dev_bf16(x) for x in (q, k, v, dout))
+    kcd = dev_bf16(kc) if nb else None
+    vcd = dev_bf16(vc) if nb else None
+    o, lse = hca.hca_attn_fwd(qd, kd, vd, kcd, vcd, **kw)
+    got = hca.hca_attn_bwd(qd, kd, vd, kcd, vcd, o, lse, gd, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.hca_attention_bwd(*(f64(x, True) for x in (q, k, v, kc, vc, dout)), **kw)
+    for name, g, r in zip(("dq", "dk", "dv", "dkc", "dvc"), got, ref):
+        if r.size == 0:
+            assert g is None
+            continue
+        _check(name, g, r, BF16_TOL)
+
+
 # ------------------------------------------------------------------ compressor
 
 @pytest.mark.parametrize("dtype,S,H,d,block", [("f32", 100, 2, 64, 7), ("bf16", 1000, 3, 512, 128),
