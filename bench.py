@@ -6,7 +6,9 @@ block 128, window 128): block compression of K and V followed by attention.
 are timed in the same run and reported under `components`:
   * HCA prefill at 131072 tokens (window 256): compression, attention, both;
   * HCA decode: 64 sequences x 1 query over 8192 compressed entries + 128 raw;
-  * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention.
+  * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention;
+  * HCA training backward at 32768 tokens: attention backward (dq, dk, dv,
+    dkc, dvc) and the compressor backward (raw-row gradients, weights).
 
 Inputs are seeded synthetic draws (the library's own generators) already
 resident in HBM when timing starts.  Kernel times come from HIP events on the
@@ -274,6 +276,62 @@ def bench_dsa_decode(torch, hca, steps, warmup):
     return res
 
 
+def backward_work(cfg):
+    """(FLOPs, algorithmic bytes) of the HCA attention backward: 10*d FLOPs per
+    visible (query head, key) pair (S, dP, dQ, dK, dV); reads Q, K, V, O, dO
+    (bf16), the compressed cache and the LSE once, writes dQ, dK, dV, dKc, dVc
+    (fp32) once."""
+    flops, _ = prefill_work(cfg)
+    flops *= 10.0 / 4.0
+    e = 2
+    qo = cfg.batch * cfg.seqlen * cfg.h_q * cfg.head_dim
+    kv = cfg.batch * cfg.seqlen * cfg.h_kv * cfg.head_dim
+    cache = cfg.batch * cfg.n_blocks * cfg.h_kv * cfg.head_dim
+    reads = e * (3 * qo + 2 * kv + 2 * cache) + 4 * cfg.batch * cfg.h_q * cfg.seqlen
+    writes = 4 * (qo + 2 * kv + 2 * cache)
+    return flops, reads + writes
+
+
+def bench_backward(torch, hca, synth, cfg, steps, warmup):
+    """Forward once (compression + attention), then the timed backward:
+    hca_attn_bwd followed by hca_compress_kv_bwd (into the same dk/dv)."""
+    import numpy as np
+    t0 = time.time()
+    inp = synth.make_prefill(cfg)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp["q"], inp["k"], inp["v"]
+    w = torch.from_numpy(inp["w"]).to("cuda:0")
+    dout = dev(synth.make_normal((cfg.batch, cfg.seqlen, cfg.h_q, cfg.head_dim), cfg.seed + 1, cfg.std, bf16=True))
+    log(f"[bench] backward: inputs ready in {time.time() - t0:.1f}s")
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
+    ws = torch.empty(hca.hca_attn_bwd_workspace_size(torch.bfloat16, cfg.batch, cfg.seqlen, 0, cfg.n_blocks, cfg.h_q,
+                                                     cfg.h_kv, cfg.head_dim, cfg.block, cfg.window),
+                     dtype=torch.uint8, device="cuda:0")
+    grads = {}
+
+    def fa():
+        grads["g"] = hca.hca_attn_bwd(q, k, v, kc, vc, o, lse, dout, window=cfg.window, block=cfg.block,
+                                      scale=cfg.scale, workspace=ws)
+
+    def fc():
+        dq, dk, dv, dkc, dvc = grads["g"]
+        hca.hca_compress_kv_bwd(k, v, dkc, dvc, w, w, cfg.block, dk=dk, dv=dv)
+
+    for _ in range(warmup):
+        fa()
+        fc()
+    ta, tc = Timer(torch), Timer(torch)
+    for _ in range(steps):
+        ta(fa)
+        tc(fc)
+    res = {"attn_bwd_ms": ta.mean_ms(), "compress_bwd_ms": tc.mean_ms()}
+    del q, k, v, o, lse, dout, kc, vc, ws, grads
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synth, cfg, heads=4):
     """The float64 oracle on a bounded sample of the headline workload: block
     compression of K and V for `heads` heads and attention for every query row
@@ -308,7 +366,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c3,c4,c5,c5d",
+    ap.add_argument("--only", default="c2,c3,c4,c5,c5d,bwd",
                     help="comma list of workloads to run (c2 always runs; 'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -389,6 +447,20 @@ def main():
     if "c5d" in only:
         comps["dsa_decode_1m"] = bench_dsa_decode(torch, hca, args.steps, args.warmup)
         log(f"[bench] c5d done: {comps['dsa_decode_1m']}")
+
+    if "bwd" in only:
+        rb = bench_backward(torch, hca, synth, c2, max(3, args.steps // 2), 2)
+        fb, bb = backward_work(c2)
+        comps["hca_backward_32k"] = {
+            "attn_bwd_ms": rb["attn_bwd_ms"], "compress_bwd_ms": rb["compress_bwd_ms"],
+            "tokens_per_s": c2.seqlen / (rb["attn_bwd_ms"] + rb["compress_bwd_ms"]) * 1e3,
+            "attn_bwd_tflops": fb / rb["attn_bwd_ms"] / 1e9,
+            "attn_bwd_mfma_frac": fb / rb["attn_bwd_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+            "attn_bwd_gbs": bb / rb["attn_bwd_ms"] / 1e6,
+            "attn_bwd_hbm_frac": bb / rb["attn_bwd_ms"] / 1e6 / PEAK_HBM_GBS,
+            "algorithmic_bytes": bb, "flops": fb,
+        }
+        log(f"[bench] bwd done: {comps['hca_backward_32k']}")
 
     value = c2.seqlen / r2["step_ms"] * 1e3
     achieved = b2 / r2["attn_ms"] / 1e6

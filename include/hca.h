@@ -354,7 +354,7 @@ hca_status_t hca_attn_bwd(hca_dtype_t dt,
  *            gradients from hca_attn_bwd, or zeros)
  *   dw_k, dw_v: [h_kv, block] fp32 contiguous (written)
  * Errors: HCA_ERR_INVALID for null pointers, bad sizes or overlapping gradients.
- * Supported: fp32 and bf16, head_dim a multiple of 4.
+ * Supported: fp32 and bf16, head_dim a multiple of 4, at most 512.
  */
 hca_status_t hca_compress_kv_bwd(hca_dtype_t dt,
                                  const void* k, hca_strides_t sk,

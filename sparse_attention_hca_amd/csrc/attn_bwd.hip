@@ -320,25 +320,48 @@ struct CompBwdArgs {
   int batch, nb, h, d, block;
 };
 
+// One workgroup per (compressed block, head): each thread keeps 4 dims of the
+// block's dkc and dvc rows and updates those dims of every other source row
+// (two rows in flight per step, 128 threads per row, d <= 512).
 __global__ __launch_bounds__(NT) void comp_bwd_dx_kernel(CompBwdArgs c) {
-  const int64_t total = (int64_t)c.batch * c.nb * c.block * c.h * c.d;
-  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < total; e += (int64_t)gridDim.x * NT) {
-    const int dd = (int)(e % c.d);
-    const int64_t r = e / c.d;
-    const int h = (int)(r % c.h);
-    const int64_t rs = r / c.h;  // b * (nb * block) + row
-    const int row = (int)(rs % ((int64_t)c.nb * c.block));
-    const int b = (int)(rs / ((int64_t)c.nb * c.block));
-    const int j = row / c.block, i = row % c.block;
-    c.dk[b * c.sdk.b + (int64_t)row * c.sdk.s + (int64_t)h * c.sdk.h + dd] +=
-        c.wk[h * c.block + i] * c.dkc[b * c.sdkc.b + (int64_t)j * c.sdkc.s + (int64_t)h * c.sdkc.h + dd];
-    c.dv[b * c.sdv.b + (int64_t)row * c.sdv.s + (int64_t)h * c.sdv.h + dd] +=
-        c.wv[h * c.block + i] * c.dvc[b * c.sdvc.b + (int64_t)j * c.sdvc.s + (int64_t)h * c.sdvc.h + dd];
+  const int bj = blockIdx.x, h = blockIdx.y;
+  const int b = bj / c.nb, j = bj % c.nb;
+  const int half = threadIdx.x >> 7, e = 4 * (threadIdx.x & 127);
+  if (e >= c.d) return;
+  const f32x4 gk = *reinterpret_cast<const f32x4*>(c.dkc + b * c.sdkc.b + (int64_t)j * c.sdkc.s + (int64_t)h * c.sdkc.h + e);
+  const f32x4 gv = *reinterpret_cast<const f32x4*>(c.dvc + b * c.sdvc.b + (int64_t)j * c.sdvc.s + (int64_t)h * c.sdvc.h + e);
+  float* dk0 = c.dk + b * c.sdk.b + (int64_t)j * c.block * c.sdk.s + (int64_t)h * c.sdk.h + e;
+  float* dv0 = c.dv + b * c.sdv.b + (int64_t)j * c.block * c.sdv.s + (int64_t)h * c.sdv.h + e;
+  for (int i = half; i < c.block; i += 2) {
+    const float wk = c.wk[h * c.block + i], wv = c.wv[h * c.block + i];
+    f32x4* pk = reinterpret_cast<f32x4*>(dk0 + (int64_t)i * c.sdk.s);
+    f32x4* pv = reinterpret_cast<f32x4*>(dv0 + (int64_t)i * c.sdv.s);
+    f32x4 xk = *pk, xv = *pv;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      xk[t] = fmaf(wk, gk[t], xk[t]);
+      xv[t] = fmaf(wv, gv[t], xv[t]);
+    }
+    *pk = xk;
+    *pv = xv;
   }
 }
 
-// dw[h, i] = sum_{b, j, dims} dxc[b, j, h, :] * x[b, j*block + i, h, :]: one
-// workgroup per (row-in-block i, head h, K or V).
+template <typename T>
+__device__ __forceinline__ f32x4 ld4f(const T* p);
+template <>
+__device__ __forceinline__ f32x4 ld4f<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+template <>
+__device__ __forceinline__ f32x4 ld4f<uint16_t>(const uint16_t* p) {
+  const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+               __uint_as_float(u[1] & 0xffff0000u)};
+}
+
+// dw[h, i] = sum_{b, j} <dxc[b, j, h, :], x[b, j*block + i, h, :]>: one
+// workgroup per (row-in-block i, head h, K or V); threads hold 4 dims and
+// walk the (b, j) rows (128 threads per row, two rows in flight), then one
+// block reduction.
 template <typename T>
 __global__ __launch_bounds__(NT) void comp_bwd_dw_kernel(CompBwdArgs c) {
   __shared__ float part[NT / 64];
@@ -347,14 +370,17 @@ __global__ __launch_bounds__(NT) void comp_bwd_dw_kernel(CompBwdArgs c) {
   const LStrides sx = which ? c.sv : c.sk;
   const float* dxc = which ? c.dvc : c.dkc;
   const LStrides sd = which ? c.sdvc : c.sdkc;
+  const int half = threadIdx.x >> 7, e = 4 * (threadIdx.x & 127);
   float acc = 0.f;
-  const int64_t n = (int64_t)c.batch * c.nb * c.d;
-  for (int64_t e = threadIdx.x; e < n; e += NT) {
-    const int dd = (int)(e % c.d);
-    const int64_t bj = e / c.d;
-    const int j = (int)(bj % c.nb), b = (int)(bj / c.nb);
-    acc = fmaf(dxc[b * sd.b + (int64_t)j * sd.s + (int64_t)h * sd.h + dd],
-               ldf(x, b * sx.b + ((int64_t)j * c.block + i) * sx.s + (int64_t)h * sx.h + dd), acc);
+  if (e < c.d) {
+    for (int b = 0; b < c.batch; ++b)
+#pragma unroll 4
+      for (int j = half; j < c.nb; j += 2) {
+        const f32x4 g = *reinterpret_cast<const f32x4*>(dxc + b * sd.b + (int64_t)j * sd.s + (int64_t)h * sd.h + e);
+        const f32x4 xv = ld4f<T>(x + b * sx.b + ((int64_t)j * c.block + i) * sx.s + (int64_t)h * sx.h + e);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc = fmaf(g[t], xv[t], acc);
+      }
   }
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
@@ -445,11 +471,8 @@ hipError_t launch_compress_bwd(int dt, const void* k, LStrides sk, const void* v
   c.dk = dk; c.dv = dv; c.sdk = sdk; c.sdv = sdv;
   c.dwk = dwk; c.dwv = dwv;
   c.batch = batch; c.nb = seqlen / block; c.h = h; c.d = d; c.block = block;
-  if (c.nb > 0) {
-    const int64_t total = (int64_t)batch * c.nb * block * h * d;
-    const int64_t nblk = (total + NT - 1) / NT;
-    hipLaunchKernelGGL(comp_bwd_dx_kernel, dim3((unsigned)(nblk < 65536 ? nblk : 65536)), dim3(NT), 0, st, c);
-  }
+  if (c.nb > 0)
+    hipLaunchKernelGGL(comp_bwd_dx_kernel, dim3((unsigned)(batch * c.nb), h), dim3(NT), 0, st, c);
   if (dt == 1)
     hipLaunchKernelGGL(comp_bwd_dw_kernel<uint16_t>, dim3(block, h, 2), dim3(NT), 0, st, c);
   else

@@ -76,8 +76,10 @@ __device__ __forceinline__ void pack_b(const float* v, bf16x8* out) {
 
 // First product of a tile: acc = A B over d = 512 (32 k-steps), A rows read
 // from LDS at `ab` (lane offset included, +32 bytes per step), B from
-// registers.  Reads run four steps ahead.
-__device__ __forceinline__ void product_d(f32x16& acc, const unsigned char* ab, const bf16x8* bf) {
+// registers.  Reads run four steps ahead.  hook(ks) runs before step ks (the
+// callers issue the next tile's DMA there, so its issue overlaps the MFMAs).
+template <typename Hook>
+__device__ __forceinline__ void product_d(f32x16& acc, const unsigned char* ab, const bf16x8* bf, Hook hook) {
   auto ld = [&](int ks) __attribute__((always_inline)) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + 32 * ks));
   };
@@ -88,6 +90,7 @@ __device__ __forceinline__ void product_d(f32x16& acc, const unsigned char* ab, 
   for (int ks = 0; ks < 32; ++ks) {
     const bf16x8 x = q[ks & 3];
     if (ks + 4 < 32) q[ks & 3] = ld(ks + 4);
+    hook(ks);
     if (ks == 0) mfma_s_first(acc, x, bf[ks]);
     else if (ks == 31) mfma_s_last(acc, x, bf[ks]);
     else mfma_s(acc, x, bf[ks]);
@@ -193,25 +196,32 @@ void bwd512_dq_kernel(DqParams p) {
   const uint16_t* vb = (const uint16_t*)a.v + b * a.sv.b + (int64_t)g * a.sv.h;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
 
-  // DMA of tile tt into stage st: wave w copies K and V rows 8w .. 8w+7.
-  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
-    const uint16_t *kbase, *vbase;
-    int64_t ks_, vs_;
-    int row0, row_max;
+  // DMA of tile tt into stage st: wave w copies K and V rows 8w .. 8w+7, one
+  // row per call of dma_row(i), i < 16 (K rows first).
+  const uint16_t* d_kbase = kcb;
+  const uint16_t* d_vbase = vcb;
+  int64_t d_ks = 0, d_vs = 0;
+  int d_row0 = 0, d_rmax = 0;
+  uint32_t d_kl = 0;
+  auto dma_setup = [&](int tt, int st) __attribute__((always_inline)) {
     if (tt < n_ct) {
-      kbase = kcb; vbase = vcb; ks_ = a.skc.s; vs_ = a.svc.s; row0 = tt * BT; row_max = nc_max - 1;
+      d_kbase = kcb; d_vbase = vcb; d_ks = a.skc.s; d_vs = a.svc.s; d_row0 = tt * BT; d_rmax = nc_max - 1;
     } else {
-      kbase = kb; vbase = vb; ks_ = a.sk.s; vs_ = a.sv.s;
-      row0 = lo_first + (tt - n_ct) * BT - kvp0; row_max = t_last - kvp0;
+      d_kbase = kb; d_vbase = vb; d_ks = a.sk.s; d_vs = a.sv.s;
+      d_row0 = lo_first + (tt - n_ct) * BT - kvp0; d_rmax = t_last - kvp0;
     }
-    const uint32_t kl = lds0 + st * DQ_STAGE, vl = kl + TILE2;
+    d_kl = lds0 + st * DQ_STAGE;
+  };
+  auto dma_row = [&](int i) __attribute__((always_inline)) {
+    const int r = 8 * w + (i & 7);
+    const int64_t row = min(d_row0 + r, d_rmax);
+    if (i < 8) dma16(d_kbase + row * d_ks + 8 * lane, d_kl + r * ROW2);
+    else dma16(d_vbase + row * d_vs + 8 * lane, d_kl + TILE2 + r * ROW1);
+  };
+  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
+    dma_setup(tt, st);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * w + i;
-      const int64_t row = min(row0 + r, row_max);
-      dma16(kbase + row * ks_ + 8 * lane, kl + r * ROW2);
-      dma16(vbase + row * vs_ + 8 * lane, vl + r * ROW1);
-    }
+    for (int i = 0; i < 16; ++i) dma_row(i);
   };
 
   unsigned char* xb = smem + 2 * DQ_STAGE + pair * DQ_XB;
@@ -224,7 +234,9 @@ void bwd512_dq_kernel(DqParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) zero_o(dq[i], zero8);
 
-  auto compute = [&](int tt, int st) __attribute__((always_inline)) {
+  // compute(tt): tile tt; the next tile's DMA rows are issued inside the
+  // first product (or up front when this pair has nothing to do)
+  auto compute = [&](int tt, int st, bool next) __attribute__((always_inline)) {
     const bool comp = tt < n_ct;
     const int j0 = tt * BT;
     const int p0 = lo_first + (tt - n_ct) * BT;
@@ -232,8 +244,15 @@ void bwd512_dq_kernel(DqParams p) {
     const unsigned char* sb = smem + st * DQ_STAGE;
     f32x16 s;
     bf16x8 dsf[2];
+    if (next) dma_setup(tt + 1, st ^ 1);
+    if (!active && next) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dma_row(i);
+    }
     if (active) {
-      product_d(s, sb + a_off, xf);  // S^T (even) or dP^T (odd): keys x queries
+      product_d(s, sb + a_off, xf, [&](int ks) __attribute__((always_inline)) {
+        if (next && (ks & 1)) dma_row(ks >> 1);
+      });  // S^T (even) or dP^T (odd): keys x queries
       // even wave: P = exp2(S c - lse2) over the visible keys [klo, klo + kn)
       // of this lane's query (masked logits become -inf, so P = 0); then each
       // wave hands its 32x32 fp32 block to the other
@@ -288,8 +307,7 @@ void bwd512_dq_kernel(DqParams p) {
   issue(0, 0);
   for (int tt = 0; tt < ntiles; ++tt) {
     barrier_dma();
-    if (tt + 1 < ntiles) issue(tt + 1, (tt + 1) & 1);
-    compute(tt, tt & 1);
+    compute(tt, tt & 1, tt + 1 < ntiles);
   }
 
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
@@ -314,55 +332,77 @@ struct DkvParams {
   BwdArgs a;
   int n_rt;     // raw key tiles of 64 per (batch, KV head)
   int n_ci;     // compressed chunk items per (batch, KV head)
-  int lc;       // query tiles (of 32) per compressed chunk
-  int total_c;  // batch * h_kv * n_ci
-  int total;    // total_c + batch * h_kv * n_rt
+  int lc;       // query tiles (of 32) per chunk; chunk m covers query tiles [lc m, lc (m + 1))
+  int total;    // batch * h_kv * (n_ci + n_rt)
   float c;      // scale * log2(e)
   float* part;  // compressed partials [batch*h_kv*n_ci][64][512] for dK, then the same for dV
 };
 
-// Query tiles (of 32) that a compressed tile ct (entries 64ct ..) needs, as
-// chunks of lc tiles; also the first query tile.
-__device__ __forceinline__ int comp_chunks(const BwdArgs& a, int ct, int lc, int* qt_first) {
-  const int64_t t_star = (int64_t)a.block * (64 * ct + 1) + a.window - 1;  // first position that sees entry 64ct
-  const int64_t i_first = t_star - a.q_pos0 > 0 ? t_star - a.q_pos0 : 0;
-  if (i_first > a.seqlen_q - 1) return 0;
-  *qt_first = (int)(i_first / BT);
-  const int nq = (a.seqlen_q - 1) / BT - *qt_first + 1;
-  return (nq + lc - 1) / lc;
+// First query tile (of 32) that sees compressed tile ct (entries 64ct ..), or
+// -1 when no query does.  Non-decreasing in ct.
+__device__ __host__ __forceinline__ int comp_first_qt(int64_t block, int64_t window, int64_t q_pos0, int seqlen_q,
+                                                      int ct) {
+  const int64_t t_star = block * (64 * ct + 1) + window - 1;  // first position that sees entry 64ct
+  const int64_t i_first = t_star - q_pos0 > 0 ? t_star - q_pos0 : 0;
+  return i_first > seqlen_q - 1 ? -1 : (int)(i_first / BT);
+}
+
+// Compressed work items of one (batch, KV head), chunk-major: for m = m0 ..
+// m_last, every compressed tile ct that some query of chunk m sees (a prefix
+// 0 .. A(m) - 1 of the tiles, since first_qt grows with ct).  Items of the
+// same m read the same query tiles, so running them side by side shares L2.
+struct CompPlan {
+  int n_ct;    // compressed tiles seen by any query
+  int m_last;  // last chunk
+  int lc;
+};
+__device__ __host__ __forceinline__ int comp_tiles_active(const CompPlan& cp, int m, int64_t block, int64_t window,
+                                                          int64_t q_pos0, int seqlen_q) {
+  int n = 0;
+  while (n < cp.n_ct && comp_first_qt(block, window, q_pos0, seqlen_q, n) / cp.lc <= m) ++n;
+  return n;
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd512_dkv_kernel(DkvParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[KV_SMEM];
   const BwdArgs& a = p.a;
-  const int item = blockIdx.x;  // compressed chunks (longest) first, then raw tiles
-  if (item >= p.total) return;
+  // items of one (batch, KV head) are contiguous and each XCD takes a
+  // contiguous range of items; within a (batch, KV head): compressed chunks
+  // (chunk-major), then raw tiles in key order
+  const int item = xcd_remap(blockIdx.x, p.total);
+  if (item < 0) return;
   const int group = a.h_q / a.h_kv;
   const int W = a.window, blk = a.block;
   const int qp0 = (int)a.q_pos0, kvp0 = (int)a.kv_pos0;
+  const int per_bg = p.n_ci + p.n_rt;
+  const int bg = item / per_bg;
+  const int local = item % per_bg;
+  const int qt_end = (a.seqlen_q - 1) / BT;
 
   bool comp;
-  int bg, row0, qt_lo, qt_hi, pidx = 0;
-  if (item < p.total_c) {
+  int row0, qt_lo, qt_hi, pidx = 0;
+  if (local < p.n_ci) {
     comp = true;
-    bg = item / p.n_ci;
-    int c = item % p.n_ci;
-    pidx = item;
-    int ct = 0, qf = 0;
-    for (;; ++ct) {
-      const int n = comp_chunks(a, ct, p.lc, &qf);
-      if (c < n) break;
+    pidx = bg * p.n_ci + local;
+    CompPlan cp;
+    cp.lc = p.lc;
+    cp.n_ct = 0;
+    while (64 * cp.n_ct < a.n_blocks && comp_first_qt(blk, W, a.q_pos0, a.seqlen_q, cp.n_ct) >= 0) ++cp.n_ct;
+    int m = comp_first_qt(blk, W, a.q_pos0, a.seqlen_q, 0) / p.lc;
+    int c = local, n;
+    while (c >= (n = comp_tiles_active(cp, m, blk, W, a.q_pos0, a.seqlen_q))) {
       c -= n;
+      ++m;
     }
+    const int ct = c;
     row0 = 64 * ct;  // entries
-    qt_lo = qf + c * p.lc;
-    qt_hi = min(qt_lo + p.lc - 1, (a.seqlen_q - 1) / BT);
+    qt_lo = max(comp_first_qt(blk, W, a.q_pos0, a.seqlen_q, ct), p.lc * m);
+    qt_hi = min(p.lc * (m + 1) - 1, qt_end);
   } else {
     comp = false;
-    const int r = item - p.total_c;
-    bg = r / p.n_rt;
-    row0 = KV_BN * (r % p.n_rt);  // raw rows
+    const int r = local - p.n_ci;
+    row0 = KV_BN * r;  // raw rows
     const int px0 = kvp0 + row0, px1 = kvp0 + min(row0 + KV_BN, a.seqlen_kv) - 1;
     const int i_lo = max(0, px0 - qp0), i_hi = min(a.seqlen_q - 1, px1 + W - 1 - qp0);
     qt_lo = i_lo / BT;
@@ -416,25 +456,39 @@ void bwd512_dkv_kernel(DkvParams p) {
   }
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem;
-  // DMA of tile tt (head g*group + tt / nq, query tile qt_lo + tt % nq) into stage st
-  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
+  // DMA of tile tt (head g*group + tt / nq, query tile qt_lo + tt % nq) into
+  // stage st: wave w copies Q and dO rows 8w .. 8w+7, one row per call of
+  // dma_row(i), i < 16; wave 0 also the tile's lse and D (dma_stats).
+  const uint16_t* d_qb = nullptr;
+  const uint16_t* d_ob = nullptr;
+  int d_qi0 = 0;
+  int64_t d_sbase = 0;
+  uint32_t d_ql = 0;
+  auto dma_setup = [&](int tt, int st) __attribute__((always_inline)) {
     const int h = g * group + tt / nq;
-    const int qi0 = BT * (qt_lo + tt % nq);
-    const uint16_t* qb = (const uint16_t*)a.q + b * a.sq.b + (int64_t)h * a.sq.h;
-    const uint16_t* ob = (const uint16_t*)a.dout + b * a.sdo.b + (int64_t)h * a.sdo.h;
-    const uint32_t ql = lds0 + st * KV_STAGE, ol = ql + TILE2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * w + i;
-      const int64_t row = min(qi0 + r, a.seqlen_q - 1);
-      dma16(qb + row * a.sq.s + 8 * lane, ql + r * ROW2);
-      dma16(ob + row * a.sdo.s + 8 * lane, ol + r * ROW2);
-    }
+    d_qi0 = BT * (qt_lo + tt % nq);
+    d_qb = (const uint16_t*)a.q + b * a.sq.b + (int64_t)h * a.sq.h;
+    d_ob = (const uint16_t*)a.dout + b * a.sdo.b + (int64_t)h * a.sdo.h;
+    d_sbase = ((int64_t)b * a.h_q + h) * a.seqlen_q;
+    d_ql = lds0 + st * KV_STAGE;
+  };
+  auto dma_row = [&](int i) __attribute__((always_inline)) {
+    const int r = 8 * w + (i & 7);
+    const int64_t row = min(d_qi0 + r, a.seqlen_q - 1);
+    if (i < 8) dma16(d_qb + row * a.sq.s + 8 * lane, d_ql + r * ROW2);
+    else dma16(d_ob + row * a.sdo.s + 8 * lane, d_ql + TILE2 + r * ROW2);
+  };
+  auto dma_stats = [&]() __attribute__((always_inline)) {
     if (w == 0) {
-      const int64_t base = ((int64_t)b * a.h_q + h) * a.seqlen_q;
-      const int qi = min(qi0 + (lane & 31), a.seqlen_q - 1);
-      dma4(lane < 32 ? (const void*)(a.lse + base + qi) : (const void*)(a.delta + base + qi), ql + 2 * TILE2);
+      const int qi = min(d_qi0 + (lane & 31), a.seqlen_q - 1);
+      dma4(lane < 32 ? (const void*)(a.lse + d_sbase + qi) : (const void*)(a.delta + d_sbase + qi), d_ql + 2 * TILE2);
     }
+  };
+  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
+    dma_setup(tt, st);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dma_row(i);
+    dma_stats();
   };
 
   unsigned char* xb = smem + 2 * KV_STAGE + pair * KV_XB;
@@ -447,7 +501,7 @@ void bwd512_dkv_kernel(DkvParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) zero_o(acc[i], zero8);
 
-  auto compute = [&](int tt, int st) __attribute__((always_inline)) {
+  auto compute = [&](int tt, int st, bool next) __attribute__((always_inline)) {
     const int qi0 = BT * (qt_lo + tt % nq);
     const int ta = qp0 + qi0, tb = qp0 + min(qi0 + BT, a.seqlen_q) - 1;  // the tile's query positions
     bool active;
@@ -460,8 +514,18 @@ void bwd512_dkv_kernel(DkvParams p) {
     const float* s_lse = (const float*)(sb + 2 * TILE2);
     f32x16 s;
     float pr[16];
+    if (next) {
+      dma_setup(tt + 1, st ^ 1);
+      dma_stats();
+    }
+    if (!active && next) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dma_row(i);
+    }
     if (active) {
-      product_d(s, sb + a_off, xf);  // S = Q K^T (even) or dP = dO V^T (odd): queries x keys
+      product_d(s, sb + a_off, xf, [&](int ks) __attribute__((always_inline)) {
+        if (next && (ks & 1)) dma_row(ks >> 1);
+      });  // S = Q K^T (even) or dP = dO V^T (odd): queries x keys
       if (role == 0) {
         // masked logits become -inf, so P = 0
 #pragma unroll
@@ -521,15 +585,14 @@ void bwd512_dkv_kernel(DkvParams p) {
     issue(0, 0);
     for (int tt = 0; tt < ntiles; ++tt) {
       barrier_dma();
-      if (tt + 1 < ntiles) issue(tt + 1, (tt + 1) & 1);
-      compute(tt, tt & 1);
+      compute(tt, tt & 1, tt + 1 < ntiles);
     }
   }
 
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
   float* dst;
   if (comp) {
-    dst = p.part + (size_t)role * p.total_c * KV_BN * D + ((size_t)pidx * KV_BN + 32 * pair + col) * D;
+    dst = p.part + (size_t)role * a.batch * a.h_kv * p.n_ci * KV_BN * D + ((size_t)pidx * KV_BN + 32 * pair + col) * D;
   } else {
     if (!kvalid) return;
     dst = role == 0 ? a.dk + b * a.sdk.b + (int64_t)kr * a.sdk.s + (int64_t)g * a.sdk.h
@@ -545,51 +608,56 @@ void bwd512_dkv_kernel(DkvParams p) {
           f32x4{acc[i][4 * q4] * sc, acc[i][4 * q4 + 1] * sc, acc[i][4 * q4 + 2] * sc, acc[i][4 * q4 + 3] * sc};
 }
 
-// dkc/dvc[b, j, g, :] = sum over the chunks of j's tile of the partials, in
-// chunk order.  One workgroup of 128 threads (4 dims each) per (entry, head, batch).
+// Compressed plan of one (batch, KV head) from the host or the device.
+__device__ __host__ __forceinline__ CompPlan comp_plan(int64_t block, int64_t window, int64_t q_pos0, int seqlen_q,
+                                                       int n_blocks, int lc) {
+  CompPlan cp;
+  cp.lc = lc;
+  cp.n_ct = 0;
+  while (64 * cp.n_ct < n_blocks && comp_first_qt(block, window, q_pos0, seqlen_q, cp.n_ct) >= 0) ++cp.n_ct;
+  cp.m_last = ((seqlen_q - 1) / BT) / lc;
+  return cp;
+}
+
+// dkc/dvc[b, j, g, :] = sum over the chunks m (in order) of the partials of
+// j's tile.  One workgroup of 128 threads (4 dims each) per (entry, head, batch).
 __global__ __launch_bounds__(128) void bwd512_reduce_kernel(DkvParams p) {
   const BwdArgs& a = p.a;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int ct = j / KV_BN;
-  int first = 0, n = 0, qf = 0;
-  for (int c = 0; c <= ct; ++c) {
-    const int k = comp_chunks(a, c, p.lc, &qf);
-    if (c < ct) first += k;
-    else n = k;
-  }
+  const CompPlan cp = comp_plan(a.block, a.window, a.q_pos0, a.seqlen_q, a.n_blocks, p.lc);
   const int e = 4 * threadIdx.x;
-  const size_t base = ((size_t)(b * a.h_kv + g) * p.n_ci + first) * KV_BN + (j % KV_BN);
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-  const size_t vofs = (size_t)p.total_c * KV_BN * D;
-  for (int c = 0; c < n; ++c) {
-    const float* pk = p.part + (base + (size_t)c * KV_BN) * D + e;
-    sk += *reinterpret_cast<const f32x4*>(pk);
-    sv += *reinterpret_cast<const f32x4*>(pk + vofs);
+  if (ct < cp.n_ct) {
+    const size_t vofs = (size_t)a.batch * a.h_kv * p.n_ci * KV_BN * D;
+    const size_t base = (size_t)(b * a.h_kv + g) * p.n_ci;
+    int prefix = 0;
+    for (int m = comp_first_qt(a.block, a.window, a.q_pos0, a.seqlen_q, 0) / p.lc; m <= cp.m_last; ++m) {
+      const int n = comp_tiles_active(cp, m, a.block, a.window, a.q_pos0, a.seqlen_q);
+      if (ct < n) {
+        const float* pk = p.part + ((base + prefix + ct) * KV_BN + (j % KV_BN)) * D + e;
+        sk += *reinterpret_cast<const f32x4*>(pk);
+        sv += *reinterpret_cast<const f32x4*>(pk + vofs);
+      }
+      prefix += n;
+    }
   }
   *reinterpret_cast<f32x4*>(a.dkc + b * a.sdkc.b + (int64_t)j * a.sdkc.s + (int64_t)g * a.sdkc.h + e) = sk;
   *reinterpret_cast<f32x4*>(a.dvc + b * a.sdvc.b + (int64_t)j * a.sdvc.s + (int64_t)g * a.sdvc.h + e) = sv;
 }
 
-// Query tiles of 32 per compressed chunk: at least 32, and at most 32 chunks
-// per compressed tile.
+// Query tiles of 32 per chunk: at least 32, and at most 32 chunks.
 int chunk_len(int seqlen_q) {
   const int n_qt = (seqlen_q + BT - 1) / BT;
   return max(32, (n_qt + 31) / 32);
 }
 
-int host_comp_chunks(int64_t block, int64_t window, int64_t q_pos0, int seqlen_q, int ct, int lc) {
-  const int64_t t_star = block * (64 * ct + 1) + window - 1;
-  const int64_t i_first = t_star - q_pos0 > 0 ? t_star - q_pos0 : 0;
-  if (i_first > seqlen_q - 1) return 0;
-  const int nq = (seqlen_q - 1) / BT - (int)(i_first / BT) + 1;
-  return (nq + lc - 1) / lc;
-}
-
 // Compressed chunk items per (batch, KV head).
 int n_chunk_items(int seqlen_q, int64_t q_pos0, int n_blocks, int block, int window) {
   const int lc = chunk_len(seqlen_q);
+  const CompPlan cp = comp_plan(block, window, q_pos0, seqlen_q, n_blocks, lc);
   int n = 0;
-  for (int ct = 0; 64 * ct < n_blocks; ++ct) n += host_comp_chunks(block, window, q_pos0, seqlen_q, ct, lc);
+  for (int ct = 0; ct < cp.n_ct; ++ct) n += cp.m_last - comp_first_qt(block, window, q_pos0, seqlen_q, ct) / lc + 1;
   return n;
 }
 
@@ -616,11 +684,10 @@ hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st) {
   kp.n_rt = (a.seqlen_kv + KV_BN - 1) / KV_BN;
   kp.lc = chunk_len(a.seqlen_q);
   kp.n_ci = n_chunk_items(a.seqlen_q, a.q_pos0, a.n_blocks, a.block, a.window);
-  kp.total_c = a.batch * a.h_kv * kp.n_ci;
-  kp.total = kp.total_c + a.batch * a.h_kv * kp.n_rt;
+  kp.total = a.batch * a.h_kv * (kp.n_ci + kp.n_rt);
   kp.c = dp.c;
   kp.part = (float*)((char*)ws + ((size_t)a.batch * a.h_q * a.seqlen_q * sizeof(float) + 255) / 256 * 256);
-  hipLaunchKernelGGL(bwd512_dkv_kernel, dim3(kp.total), dim3(256), 0, st, kp);
+  hipLaunchKernelGGL(bwd512_dkv_kernel, dim3(((kp.total + 7) / 8) * 8), dim3(256), 0, st, kp);
   if (a.n_blocks > 0)
     hipLaunchKernelGGL(bwd512_reduce_kernel, dim3(a.n_blocks, a.h_kv, a.batch), dim3(128), 0, st, kp);
   return hipGetLastError();

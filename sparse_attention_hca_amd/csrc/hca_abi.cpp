@@ -399,7 +399,8 @@ hca_status_t hca_compress_kv_bwd(hca_dtype_t dt, const void* k, hca_strides_t sk
   if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
   if (batch <= 0 || seqlen <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0)
     return fail(HCA_ERR_INVALID, "hca_compress_kv_bwd: sizes must be positive");
-  if (head_dim % 4) return fail(HCA_ERR_UNSUPPORTED, "hca_compress_kv_bwd: head_dim must be a multiple of 4");
+  if (head_dim % 4 || head_dim > 512)
+    return fail(HCA_ERR_UNSUPPORTED, "hca_compress_kv_bwd: head_dim must be a multiple of 4, at most 512");
   if (!w_k || !w_v || !dw_k || !dw_v) return fail(HCA_ERR_INVALID, "hca_compress_kv_bwd: weights or their gradients are NULL");
   const size_t es = elem_size(dt);
   const int nb = seqlen / block;

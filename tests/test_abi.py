@@ -238,6 +238,7 @@ def test_compress_bwd_rejects_bad_arguments():
     assert call(dwk=None) == hca.HCA_ERR_INVALID
     assert call(block=0) == hca.HCA_ERR_INVALID
     assert call(d=510) == hca.HCA_ERR_UNSUPPORTED
+    assert call(d=516) == hca.HCA_ERR_UNSUPPORTED
     assert call(dk=ctypes.c_void_p(1 << 35)) == hca.HCA_ERR_INVALID    # dk aliases dv
     assert call(dk=ctypes.c_void_p(1 << 30)) == hca.HCA_ERR_INVALID    # dk aliases dkc
 
