@@ -368,6 +368,47 @@ hca_status_t hca_compress_kv_bwd(hca_dtype_t dt,
                                  int batch, int seqlen, int h_kv, int head_dim, int block,
                                  void* stream);
 
+/*
+ * hca_attn_compress_bwd -- the backward of a whole HCA layer's attention for a
+ * sequence processed from position 0: hca_compress_kv (K, V -> kc, vc with
+ * w_k, w_v) followed by hca_attn_fwd (queries 0 .. seqlen-1 over kc, vc and the
+ * raw window).  Gives the same values as hca_attn_bwd followed by
+ * hca_compress_kv_bwd, in one call:
+ *   dq, dkc, dvc as hca_attn_bwd;
+ *   dk[b, r, g, :] = (window part of hca_attn_bwd) + w_k[g, r % block] * dkc[b, r / block, g, :]
+ *                    for rows r < n_blocks * block (window part only beyond), dv likewise;
+ *   dw_k[g, i] = sum_{b, j} <dkc[b, j, g, :], k[b, j*block + i, g, :]>, dw_v likewise.
+ *   q, o, dout: [batch, seqlen, h_q, head_dim]; k, v: [batch, seqlen, h_kv, head_dim]
+ *   kc, vc: [batch, n_blocks, h_kv, head_dim], the compression of k, v (read)
+ *   w_k, w_v, dw_k, dw_v: [h_kv, block] fp32 contiguous
+ *   dq, dk, dv, dkc, dvc: fp32, overwritten.
+ * On the bf16 / head_dim 512 path the compressor's share is added inside the
+ * key-tile kernel, saving a read-modify-write pass over dk and dv.
+ * Workspace: hca_attn_bwd_workspace_size with q_pos0 = 0 and seqlen_q = seqlen.
+ * Errors: as hca_attn_bwd, and HCA_ERR_INVALID when a weight pointer is NULL,
+ * n_blocks * block > seqlen, or the weight gradients overlap other outputs.
+ */
+hca_status_t hca_attn_compress_bwd(hca_dtype_t dt,
+                                   const void* q, hca_strides_t sq,
+                                   const void* k, hca_strides_t sk,
+                                   const void* v, hca_strides_t sv,
+                                   const void* kc, hca_strides_t skc,
+                                   const void* vc, hca_strides_t svc,
+                                   const void* o, hca_strides_t so,
+                                   const float* lse,
+                                   const void* dout, hca_strides_t sdout,
+                                   const float* w_k, const float* w_v,
+                                   float* dq, hca_strides_t sdq,
+                                   float* dk, hca_strides_t sdk,
+                                   float* dv, hca_strides_t sdv,
+                                   float* dkc, hca_strides_t sdkc,
+                                   float* dvc, hca_strides_t sdvc,
+                                   float* dw_k, float* dw_v,
+                                   int batch, int seqlen, int n_blocks,
+                                   int h_q, int h_kv, int head_dim, int block, int window, float scale,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Workspace bytes dsa_sparse_attn_bwd needs (D, and an inverted index of idx). */
 size_t dsa_sparse_attn_bwd_workspace_size(int batch, int seqlen, int h_q, int topk);
 

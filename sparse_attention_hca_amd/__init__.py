@@ -29,8 +29,8 @@ EXPORTS = (
     "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd", "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
-    "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "dsa_sparse_attn_bwd_workspace_size",
-    "dsa_sparse_attn_bwd",
+    "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
+    "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
 )
 
 
@@ -87,6 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hca_attn_bwd.restype = I
     lib.hca_attn_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P, S, P, S, P, S,
                                  I, I, I64, I, I64, I, I, I, I, I, I, F, P, SZ, P]
+    lib.hca_attn_compress_bwd.restype = I
+    lib.hca_attn_compress_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P, P, S, P, P, P, S, P, S, P, S,
+                                          P, S, P, S, P, P, I, I, I, I, I, I, I, I, F, P, SZ, P]
     lib.hca_compress_kv_bwd.restype = I
     lib.hca_compress_kv_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, P, P, S, P, S, P, P, I, I, I, I, I, P]
     lib.dsa_sparse_attn_bwd_workspace_size.restype = SZ
@@ -376,6 +379,45 @@ def hca_compress_kv_bwd(k: torch.Tensor, v: torch.Tensor, dkc: torch.Tensor, dvc
     return dk, dv, dw_k, dw_v
 
 
+def hca_attn_compress_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional[torch.Tensor],
+                          vc: Optional[torch.Tensor], o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                          w_k: torch.Tensor, w_v: torch.Tensor, *, window: int, block: int,
+                          scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward of compression + attention for a sequence from position 0: returns fp32
+    (dq, dk, dv, dkc, dvc, dw_k, dw_v); dk/dv include the compressor's share."""
+    lib = load_library()
+    _dev(q, k, v, kc, vc, o, lse, dout, w_k, w_v)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nb = 0 if kc is None else kc.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, S]")
+    w_k = w_k.contiguous()
+    w_v = w_v.contiguous()
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dkc = torch.empty(kc.shape, **f32) if nb else None
+    dvc = torch.empty(vc.shape, **f32) if nb else None
+    dw_k = torch.empty((Hkv, block), **f32)
+    dw_v = torch.empty((Hkv, block), **f32)
+    if workspace is None:
+        workspace = torch.empty(lib.hca_attn_bwd_workspace_size(_dt(q), B, S, 0, nb, Hq, Hkv, d, block, window),
+                                dtype=torch.uint8, device=q.device)
+    zs = Strides(0, 0, 0)
+    st = lambda t: zs if t is None else _strides(t)
+    _check(lib.hca_attn_compress_bwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                     _ptr(kc), st(kc), _ptr(vc), st(vc), _ptr(o), _strides(o), _ptr(lse), _ptr(dout),
+                                     _strides(dout), _ptr(w_k), _ptr(w_v), _ptr(dq), _strides(dq), _ptr(dk),
+                                     _strides(dk), _ptr(dv), _strides(dv), _ptr(dkc), st(dkc), _ptr(dvc), st(dvc),
+                                     _ptr(dw_k), _ptr(dw_v), B, S, nb, Hq, Hkv, d, block, window, float(scale),
+                                     _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, dkc, dvc, dw_k, dw_v
+
+
 def dsa_sparse_attn_bwd_workspace_size(batch: int, seqlen: int, h_q: int, topk: int) -> int:
     return load_library().dsa_sparse_attn_bwd_workspace_size(batch, seqlen, h_q, topk)
 
@@ -417,6 +459,6 @@ __all__ = [
     "hca_attn_fwd",
     "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
-    "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd",
+    "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
 ]

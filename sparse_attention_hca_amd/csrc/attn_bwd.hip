@@ -460,10 +460,24 @@ hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st) {
   return dt == 1 ? run_dsa_bwd<uint16_t>(a, cnt, cur, st) : run_dsa_bwd<float>(a, cnt, cur, st);
 }
 
+hipError_t launch_hca_attn_compress_bwd(int dt, BwdArgs a, const float* wk, const float* wv, float* dwk, float* dwv,
+                                        void* ws, hipStream_t st) {
+  hipError_t e;
+  if (hca_bwd_uses_mfma(dt, a.d))
+    e = launch_hca_attn_bwd512(a, ws, st, wk, wv);
+  else
+    e = launch_hca_attn_bwd(dt, a, ws, st);
+  if (e != hipSuccess) return e;
+  // the weight gradient, plus (generic path) the raw-row update
+  return launch_compress_bwd(dt, a.k, a.sk, a.v, a.sv, a.dkc, a.sdkc, a.dvc, a.sdvc, wk, wv, a.dk, a.sdk, a.dv, a.sdv,
+                             dwk, dwv, a.batch, a.n_blocks * a.block, a.h_kv, a.d, a.block, st,
+                             !hca_bwd_uses_mfma(dt, a.d));
+}
+
 hipError_t launch_compress_bwd(int dt, const void* k, LStrides sk, const void* v, LStrides sv, const float* dkc,
                                LStrides sdkc, const float* dvc, LStrides sdvc, const float* wk, const float* wv,
                                float* dk, LStrides sdk, float* dv, LStrides sdv, float* dwk, float* dwv, int batch,
-                               int seqlen, int h, int d, int block, hipStream_t st) {
+                               int seqlen, int h, int d, int block, hipStream_t st, bool dx) {
   CompBwdArgs c;
   c.k = k; c.v = v; c.sk = sk; c.sv = sv;
   c.dkc = dkc; c.dvc = dvc; c.sdkc = sdkc; c.sdvc = sdvc;
@@ -471,7 +485,7 @@ hipError_t launch_compress_bwd(int dt, const void* k, LStrides sk, const void* v
   c.dk = dk; c.dv = dv; c.sdk = sdk; c.sdv = sdv;
   c.dwk = dwk; c.dwv = dwv;
   c.batch = batch; c.nb = seqlen / block; c.h = h; c.d = d; c.block = block;
-  if (c.nb > 0)
+  if (c.nb > 0 && dx)
     hipLaunchKernelGGL(comp_bwd_dx_kernel, dim3((unsigned)(batch * c.nb), h), dim3(NT), 0, st, c);
   if (dt == 1)
     hipLaunchKernelGGL(comp_bwd_dw_kernel<uint16_t>, dim3(block, h, 2), dim3(NT), 0, st, c);

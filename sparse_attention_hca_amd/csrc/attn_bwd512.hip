@@ -333,9 +333,14 @@ struct DkvParams {
   int n_rt;     // raw key tiles of 64 per (batch, KV head)
   int n_ci;     // compressed chunk items per (batch, KV head)
   int lc;       // query tiles (of 32) per chunk; chunk m covers query tiles [lc m, lc (m + 1))
-  int total;    // batch * h_kv * (n_ci + n_rt)
+  int mode;     // items launched: 0 all, 1 compressed chunks only, 2 raw tiles only
+  int total;    // batch * h_kv * (items per (batch, KV head) of this mode)
   float c;      // scale * log2(e)
   float* part;  // compressed partials [batch*h_kv*n_ci][64][512] for dK, then the same for dV
+  // when set (mode 2, after the reduce): raw row r of a whole block also gets
+  // the compressor's share w[g, r % block] * dkc[r / block] (resp. dvc)
+  const float* fw_k;
+  const float* fw_v;
 };
 
 // First query tile (of 32) that sees compressed tile ct (entries 64ct ..), or
@@ -375,9 +380,9 @@ void bwd512_dkv_kernel(DkvParams p) {
   const int group = a.h_q / a.h_kv;
   const int W = a.window, blk = a.block;
   const int qp0 = (int)a.q_pos0, kvp0 = (int)a.kv_pos0;
-  const int per_bg = p.n_ci + p.n_rt;
+  const int per_bg = p.mode == 0 ? p.n_ci + p.n_rt : p.mode == 1 ? p.n_ci : p.n_rt;
   const int bg = item / per_bg;
-  const int local = item % per_bg;
+  const int local = item % per_bg + (p.mode == 2 ? p.n_ci : 0);
   const int qt_end = (a.seqlen_q - 1) / BT;
 
   bool comp;
@@ -600,6 +605,23 @@ void bwd512_dkv_kernel(DkvParams p) {
   }
   dst += 4 * hf;
   const float sc = role == 0 ? a.scale : 1.f;
+  if (!comp && p.fw_k && kr < a.n_blocks * blk) {
+    // fused compressor backward: + w[g, r % block] * d(compressed row r / block)
+    const float wgt = (role == 0 ? p.fw_k : p.fw_v)[g * blk + kr % blk];
+    const float* cr = role == 0 ? a.dkc + b * a.sdkc.b + (int64_t)(kr / blk) * a.sdkc.s + (int64_t)g * a.sdkc.h
+                                : a.dvc + b * a.sdvc.b + (int64_t)(kr / blk) * a.sdvc.s + (int64_t)g * a.sdvc.h;
+    cr += 4 * hf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(cr + 32 * i + 8 * q4);
+        *reinterpret_cast<f32x4*>(dst + 32 * i + 8 * q4) =
+            f32x4{fmaf(acc[i][4 * q4], sc, wgt * cv[0]), fmaf(acc[i][4 * q4 + 1], sc, wgt * cv[1]),
+                  fmaf(acc[i][4 * q4 + 2], sc, wgt * cv[2]), fmaf(acc[i][4 * q4 + 3], sc, wgt * cv[3])};
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -670,7 +692,7 @@ size_t hca_bwd512_workspace_bytes(int batch, int seqlen_q, int64_t q_pos0, int n
   return delta + 2 * (size_t)batch * h_kv * n_ci * KV_BN * D * sizeof(float);
 }
 
-hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st) {
+hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st, const float* fw_k, const float* fw_v) {
   a.delta = (float*)ws;
   DqParams dp;
   dp.a = a;
@@ -684,12 +706,33 @@ hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st) {
   kp.n_rt = (a.seqlen_kv + KV_BN - 1) / KV_BN;
   kp.lc = chunk_len(a.seqlen_q);
   kp.n_ci = n_chunk_items(a.seqlen_q, a.q_pos0, a.n_blocks, a.block, a.window);
-  kp.total = a.batch * a.h_kv * (kp.n_ci + kp.n_rt);
   kp.c = dp.c;
   kp.part = (float*)((char*)ws + ((size_t)a.batch * a.h_q * a.seqlen_q * sizeof(float) + 255) / 256 * 256);
-  hipLaunchKernelGGL(bwd512_dkv_kernel, dim3(((kp.total + 7) / 8) * 8), dim3(256), 0, st, kp);
+  kp.fw_k = nullptr;
+  kp.fw_v = nullptr;
+  const int bgs = a.batch * a.h_kv;
+  if (!fw_k) {
+    kp.mode = 0;
+    kp.total = bgs * (kp.n_ci + kp.n_rt);
+    hipLaunchKernelGGL(bwd512_dkv_kernel, dim3(((kp.total + 7) / 8) * 8), dim3(256), 0, st, kp);
+    if (a.n_blocks > 0)
+      hipLaunchKernelGGL(bwd512_reduce_kernel, dim3(a.n_blocks, a.h_kv, a.batch), dim3(128), 0, st, kp);
+    return hipGetLastError();
+  }
+  // fused compressor backward: compressed entries first, their sums, then the
+  // raw rows (which add the compressor's share of their block)
+  if (kp.n_ci > 0) {
+    kp.mode = 1;
+    kp.total = bgs * kp.n_ci;
+    hipLaunchKernelGGL(bwd512_dkv_kernel, dim3(((kp.total + 7) / 8) * 8), dim3(256), 0, st, kp);
+  }
   if (a.n_blocks > 0)
     hipLaunchKernelGGL(bwd512_reduce_kernel, dim3(a.n_blocks, a.h_kv, a.batch), dim3(128), 0, st, kp);
+  kp.mode = 2;
+  kp.total = bgs * kp.n_rt;
+  kp.fw_k = fw_k;
+  kp.fw_v = fw_v;
+  hipLaunchKernelGGL(bwd512_dkv_kernel, dim3(((kp.total + 7) / 8) * 8), dim3(256), 0, st, kp);
   return hipGetLastError();
 }
 

@@ -68,6 +68,95 @@ constexpr int64_t kPosLimit = (int64_t)1 << 30;
 
 }  // namespace
 
+// Keys seen by the query at position t: compressed entries, then the raw window.
+static int n_keys_of(int64_t t, int window, int block) {
+  const int64_t lo = t - window + 1 > 0 ? t - window + 1 : 0;
+  return (int)(lo / block + (t - lo + 1));
+}
+
+static hca_status_t attn_bwd_impl(const char* fn, hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                          const void* v, hca_strides_t sv, const void* kc, hca_strides_t skc, const void* vc,
+                          hca_strides_t svc, const void* o, hca_strides_t so, const float* lse, const void* dout,
+                          hca_strides_t sdo, float* dq, hca_strides_t sdq, float* dk, hca_strides_t sdk, float* dv,
+                          hca_strides_t sdv, float* dkc, hca_strides_t sdkc, float* dvc, hca_strides_t sdvc,
+                          int batch, int seqlen_q, int64_t q_pos0, int seqlen_kv, int64_t kv_pos0, int n_blocks,
+                          int h_q, int h_kv, int head_dim, int block, int window, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream, const float* w_k, const float* w_v, float* dw_k,
+                          float* dw_v) {
+  if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_kv <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || n_blocks < 0)
+    return fail(HCA_ERR_INVALID, "%s: sizes must be positive", fn);
+  if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q (%d) must be a multiple of h_kv (%d)", h_q, h_kv);
+  if (window < 1 || block < 1) return fail(HCA_ERR_INVALID, "window and block must be >= 1");
+  if (q_pos0 < 0 || kv_pos0 < 0) return fail(HCA_ERR_INVALID, "positions must be >= 0");
+  if (q_pos0 + seqlen_q > kPosLimit || kv_pos0 + seqlen_kv > kPosLimit)
+    return fail(HCA_ERR_UNSUPPORTED, "positions beyond 2^30 are not supported");
+  if (head_dim > 512 || head_dim % 4) return fail(HCA_ERR_UNSUPPORTED, "%s: head_dim must be <= 512, a multiple of 4", fn);
+  if (!(scale == scale)) return fail(HCA_ERR_INVALID, "scale is NaN");
+  if (!lse || ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is NULL or not 4-byte aligned");
+  const size_t es = elem_size(dt);
+  HCA_TRY(check_tensor("q", q, sq, es));
+  HCA_TRY(check_tensor("k", k, sk, es));
+  HCA_TRY(check_tensor("v", v, sv, es));
+  HCA_TRY(check_tensor("kc", kc, skc, es, n_blocks == 0));
+  HCA_TRY(check_tensor("vc", vc, svc, es, n_blocks == 0));
+  HCA_TRY(check_tensor("o", o, so, es));
+  HCA_TRY(check_tensor("dout", dout, sdo, es));
+  HCA_TRY(check_tensor("dq", dq, sdq, 4));
+  HCA_TRY(check_tensor("dk", dk, sdk, 4));
+  HCA_TRY(check_tensor("dv", dv, sdv, 4));
+  HCA_TRY(check_tensor("dkc", dkc, sdkc, 4, n_blocks == 0));
+  HCA_TRY(check_tensor("dvc", dvc, sdvc, 4, n_blocks == 0));
+  const int64_t t0 = q_pos0, t1 = q_pos0 + seqlen_q - 1;
+  const int64_t lo0 = t0 - window + 1 > 0 ? t0 - window + 1 : 0;
+  const int64_t lo1 = t1 - window + 1 > 0 ? t1 - window + 1 : 0;
+  if (lo0 < kv_pos0 || t1 >= kv_pos0 + seqlen_kv)
+    return fail(HCA_ERR_INVALID, "%s: raw K/V must cover every query's window", fn);
+  if (lo1 / block > n_blocks) return fail(HCA_ERR_INVALID, "%s: the last query needs more compressed entries", fn);
+  const bool mfma = hca::hca_bwd_uses_mfma(dt == HCA_DTYPE_BF16 ? 1 : 0, head_dim);
+  if (!mfma && n_keys_of(t1, window, block) > hca::kBwdMaxKeys)
+    return fail(HCA_ERR_UNSUPPORTED, "%s: at most %d keys per query", fn, hca::kBwdMaxKeys);
+  {
+    const Range outs[5] = {extent(dq, sdq, batch, seqlen_q, h_q, head_dim, 4),
+                           extent(dk, sdk, batch, seqlen_kv, h_kv, head_dim, 4),
+                           extent(dv, sdv, batch, seqlen_kv, h_kv, head_dim, 4),
+                           n_blocks ? extent(dkc, sdkc, batch, n_blocks, h_kv, head_dim, 4) : Range{0, 0},
+                           n_blocks ? extent(dvc, sdvc, batch, n_blocks, h_kv, head_dim, 4) : Range{0, 0}};
+    const Range ins[7] = {extent(q, sq, batch, seqlen_q, h_q, head_dim, es),
+                          extent(k, sk, batch, seqlen_kv, h_kv, head_dim, es),
+                          extent(v, sv, batch, seqlen_kv, h_kv, head_dim, es),
+                          n_blocks ? extent(kc, skc, batch, n_blocks, h_kv, head_dim, es) : Range{0, 0},
+                          n_blocks ? extent(vc, svc, batch, n_blocks, h_kv, head_dim, es) : Range{0, 0},
+                          extent(o, so, batch, seqlen_q, h_q, head_dim, es),
+                          extent(dout, sdo, batch, seqlen_q, h_q, head_dim, es)};
+    for (int x = 0; x < 5; ++x) {
+      for (int y = 0; y < 7; ++y)
+        if (overlaps(outs[x], ins[y])) return fail(HCA_ERR_INVALID, "%s: a gradient overlaps an input", fn);
+      for (int y = x + 1; y < 5; ++y)
+        if (overlaps(outs[x], outs[y])) return fail(HCA_ERR_INVALID, "%s: gradients overlap each other", fn);
+    }
+  }
+  const size_t need = hca::hca_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen_q, q_pos0, n_blocks,
+                                                   h_q, h_kv, head_dim, block, window);
+  if (!workspace || workspace_bytes < need)
+    return fail(HCA_ERR_WORKSPACE, "%s needs a %zu-byte workspace (got %zu)", fn, need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
+  hca::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.kc = kc; a.vc = vc; a.o = o; a.dout = dout;
+  a.sq = ls(sq); a.sk = ls(sk); a.sv = ls(sv); a.skc = ls(skc); a.svc = ls(svc); a.so = ls(so); a.sdo = ls(sdo);
+  a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dkc = dkc; a.dvc = dvc;
+  a.sdq = ls(sdq); a.sdk = ls(sdk); a.sdv = ls(sdv); a.sdkc = ls(sdkc); a.sdvc = ls(sdvc);
+  a.batch = batch; a.seqlen_q = seqlen_q; a.seqlen_kv = seqlen_kv; a.n_blocks = n_blocks;
+  a.h_q = h_q; a.h_kv = h_kv; a.d = head_dim; a.d_v = head_dim; a.block = block; a.window = window;
+  a.q_pos0 = q_pos0; a.kv_pos0 = kv_pos0; a.scale = scale;
+  hipError_t e = w_k ? hca::launch_hca_attn_compress_bwd(dt == HCA_DTYPE_BF16 ? 1 : 0, a, w_k, w_v, dw_k, dw_v,
+                                                        workspace, (hipStream_t)stream)
+                     : hca::launch_hca_attn_bwd(dt == HCA_DTYPE_BF16 ? 1 : 0, a, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return HCA_OK;
+}
+
 extern "C" {
 
 int hca_abi_version(void) { return 1; }
@@ -163,10 +252,6 @@ hca_status_t hca_append_kv(hca_dtype_t dt, const void* k_new, hca_strides_t skn,
   return HCA_OK;
 }
 
-static int n_keys_of(int64_t t, int window, int block) {
-  const int64_t lo = t - window + 1 > 0 ? t - window + 1 : 0;
-  return (int)(lo / block + (t - lo + 1));
-}
 
 size_t hca_attn_fwd_workspace_size(int batch, int seqlen_q, int h_q, int h_kv, int head_dim, int n_blocks,
                                    int window) {
@@ -319,76 +404,46 @@ hca_status_t hca_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
                           int batch, int seqlen_q, int64_t q_pos0, int seqlen_kv, int64_t kv_pos0, int n_blocks,
                           int h_q, int h_kv, int head_dim, int block, int window, float scale, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
-  if (batch <= 0 || seqlen_q <= 0 || seqlen_kv <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || n_blocks < 0)
-    return fail(HCA_ERR_INVALID, "hca_attn_bwd: sizes must be positive");
-  if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q (%d) must be a multiple of h_kv (%d)", h_q, h_kv);
-  if (window < 1 || block < 1) return fail(HCA_ERR_INVALID, "window and block must be >= 1");
-  if (q_pos0 < 0 || kv_pos0 < 0) return fail(HCA_ERR_INVALID, "positions must be >= 0");
-  if (q_pos0 + seqlen_q > kPosLimit || kv_pos0 + seqlen_kv > kPosLimit)
-    return fail(HCA_ERR_UNSUPPORTED, "positions beyond 2^30 are not supported");
-  if (head_dim > 512 || head_dim % 4) return fail(HCA_ERR_UNSUPPORTED, "hca_attn_bwd: head_dim must be <= 512, a multiple of 4");
-  if (!(scale == scale)) return fail(HCA_ERR_INVALID, "scale is NaN");
-  if (!lse || ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is NULL or not 4-byte aligned");
-  const size_t es = elem_size(dt);
-  HCA_TRY(check_tensor("q", q, sq, es));
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("kc", kc, skc, es, n_blocks == 0));
-  HCA_TRY(check_tensor("vc", vc, svc, es, n_blocks == 0));
-  HCA_TRY(check_tensor("o", o, so, es));
-  HCA_TRY(check_tensor("dout", dout, sdo, es));
-  HCA_TRY(check_tensor("dq", dq, sdq, 4));
-  HCA_TRY(check_tensor("dk", dk, sdk, 4));
-  HCA_TRY(check_tensor("dv", dv, sdv, 4));
-  HCA_TRY(check_tensor("dkc", dkc, sdkc, 4, n_blocks == 0));
-  HCA_TRY(check_tensor("dvc", dvc, sdvc, 4, n_blocks == 0));
-  const int64_t t0 = q_pos0, t1 = q_pos0 + seqlen_q - 1;
-  const int64_t lo0 = t0 - window + 1 > 0 ? t0 - window + 1 : 0;
-  const int64_t lo1 = t1 - window + 1 > 0 ? t1 - window + 1 : 0;
-  if (lo0 < kv_pos0 || t1 >= kv_pos0 + seqlen_kv)
-    return fail(HCA_ERR_INVALID, "hca_attn_bwd: raw K/V must cover every query's window");
-  if (lo1 / block > n_blocks) return fail(HCA_ERR_INVALID, "hca_attn_bwd: the last query needs more compressed entries");
-  const bool mfma = hca::hca_bwd_uses_mfma(dt == HCA_DTYPE_BF16 ? 1 : 0, head_dim);
-  if (!mfma && n_keys_of(t1, window, block) > hca::kBwdMaxKeys)
-    return fail(HCA_ERR_UNSUPPORTED, "hca_attn_bwd: at most %d keys per query", hca::kBwdMaxKeys);
+  return attn_bwd_impl("hca_attn_bwd", dt, q, sq, k, sk, v, sv, kc, skc, vc, svc, o, so, lse, dout, sdo, dq, sdq, dk,
+                       sdk, dv, sdv, dkc, sdkc, dvc, sdvc, batch, seqlen_q, q_pos0, seqlen_kv, kv_pos0, n_blocks, h_q,
+                       h_kv, head_dim, block, window, scale, workspace, workspace_bytes, stream, nullptr, nullptr,
+                       nullptr, nullptr);
+}
+
+hca_status_t hca_attn_compress_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                                   const void* v, hca_strides_t sv, const void* kc, hca_strides_t skc, const void* vc,
+                                   hca_strides_t svc, const void* o, hca_strides_t so, const float* lse,
+                                   const void* dout, hca_strides_t sdo, const float* w_k, const float* w_v, float* dq,
+                                   hca_strides_t sdq, float* dk, hca_strides_t sdk, float* dv, hca_strides_t sdv,
+                                   float* dkc, hca_strides_t sdkc, float* dvc, hca_strides_t sdvc, float* dw_k,
+                                   float* dw_v, int batch, int seqlen, int n_blocks, int h_q, int h_kv, int head_dim,
+                                   int block, int window, float scale, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!w_k || !w_v || !dw_k || !dw_v)
+    return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: weights or their gradients are NULL");
+  if (((uintptr_t)w_k | (uintptr_t)w_v | (uintptr_t)dw_k | (uintptr_t)dw_v) & 3u)
+    return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: weights must be 4-byte aligned");
+  if (block >= 1 && n_blocks >= 0 && (int64_t)n_blocks * block > seqlen)
+    return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: n_blocks * block exceeds seqlen");
   {
-    const Range outs[5] = {extent(dq, sdq, batch, seqlen_q, h_q, head_dim, 4),
-                           extent(dk, sdk, batch, seqlen_kv, h_kv, head_dim, 4),
-                           extent(dv, sdv, batch, seqlen_kv, h_kv, head_dim, 4),
-                           n_blocks ? extent(dkc, sdkc, batch, n_blocks, h_kv, head_dim, 4) : Range{0, 0},
-                           n_blocks ? extent(dvc, sdvc, batch, n_blocks, h_kv, head_dim, 4) : Range{0, 0}};
-    const Range ins[7] = {extent(q, sq, batch, seqlen_q, h_q, head_dim, es),
-                          extent(k, sk, batch, seqlen_kv, h_kv, head_dim, es),
-                          extent(v, sv, batch, seqlen_kv, h_kv, head_dim, es),
-                          n_blocks ? extent(kc, skc, batch, n_blocks, h_kv, head_dim, es) : Range{0, 0},
-                          n_blocks ? extent(vc, svc, batch, n_blocks, h_kv, head_dim, es) : Range{0, 0},
-                          extent(o, so, batch, seqlen_q, h_q, head_dim, es),
-                          extent(dout, sdo, batch, seqlen_q, h_q, head_dim, es)};
-    for (int x = 0; x < 5; ++x) {
-      for (int y = 0; y < 7; ++y)
-        if (overlaps(outs[x], ins[y])) return fail(HCA_ERR_INVALID, "hca_attn_bwd: a gradient overlaps an input");
-      for (int y = x + 1; y < 5; ++y)
-        if (overlaps(outs[x], outs[y])) return fail(HCA_ERR_INVALID, "hca_attn_bwd: gradients overlap each other");
+    const Range rw[4] = {Range{(uintptr_t)w_k, (uintptr_t)(w_k + (size_t)h_kv * block)},
+                         Range{(uintptr_t)w_v, (uintptr_t)(w_v + (size_t)h_kv * block)},
+                         Range{(uintptr_t)dw_k, (uintptr_t)(dw_k + (size_t)h_kv * block)},
+                         Range{(uintptr_t)dw_v, (uintptr_t)(dw_v + (size_t)h_kv * block)}};
+    if (overlaps(rw[2], rw[3]) || overlaps(rw[0], rw[2]) || overlaps(rw[0], rw[3]) || overlaps(rw[1], rw[2]) ||
+        overlaps(rw[1], rw[3]))
+      return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: weight gradients overlap");
+    if (batch > 0 && seqlen > 0 && h_q > 0 && h_kv > 0 && head_dim > 0) {
+      const Range outs[3] = {extent(dq, sdq, batch, seqlen, h_q, head_dim, 4), extent(dk, sdk, batch, seqlen, h_kv, head_dim, 4),
+                             extent(dv, sdv, batch, seqlen, h_kv, head_dim, 4)};
+      for (int x = 0; x < 3; ++x)
+        for (int y = 2; y < 4; ++y)
+          if (overlaps(outs[x], rw[y])) return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: gradients overlap");
     }
   }
-  const size_t need = hca::hca_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen_q, q_pos0, n_blocks,
-                                                   h_q, h_kv, head_dim, block, window);
-  if (!workspace || workspace_bytes < need)
-    return fail(HCA_ERR_WORKSPACE, "hca_attn_bwd needs a %zu-byte workspace (got %zu)", need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
-  hca::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.kc = kc; a.vc = vc; a.o = o; a.dout = dout;
-  a.sq = ls(sq); a.sk = ls(sk); a.sv = ls(sv); a.skc = ls(skc); a.svc = ls(svc); a.so = ls(so); a.sdo = ls(sdo);
-  a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dkc = dkc; a.dvc = dvc;
-  a.sdq = ls(sdq); a.sdk = ls(sdk); a.sdv = ls(sdv); a.sdkc = ls(sdkc); a.sdvc = ls(sdvc);
-  a.batch = batch; a.seqlen_q = seqlen_q; a.seqlen_kv = seqlen_kv; a.n_blocks = n_blocks;
-  a.h_q = h_q; a.h_kv = h_kv; a.d = head_dim; a.d_v = head_dim; a.block = block; a.window = window;
-  a.q_pos0 = q_pos0; a.kv_pos0 = kv_pos0; a.scale = scale;
-  hipError_t e = hca::launch_hca_attn_bwd(dt == HCA_DTYPE_BF16 ? 1 : 0, a, workspace, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "hca_attn_bwd launch");
-  return HCA_OK;
+  return attn_bwd_impl("hca_attn_compress_bwd", dt, q, sq, k, sk, v, sv, kc, skc, vc, svc, o, so, lse, dout, sdo, dq,
+                       sdq, dk, sdk, dv, sdv, dkc, sdkc, dvc, sdvc, batch, seqlen, 0, seqlen, 0, n_blocks, h_q, h_kv,
+                       head_dim, block, window, scale, workspace, workspace_bytes, stream, w_k, w_v, dw_k, dw_v);
 }
 
 hca_status_t hca_compress_kv_bwd(hca_dtype_t dt, const void* k, hca_strides_t sk, const void* v, hca_strides_t sv,

@@ -70,16 +70,23 @@ bool hca_bwd_uses_mfma(int dt, int head_dim);
 size_t hca_bwd_workspace_bytes(int dt, int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q, int h_kv,
                                int head_dim, int block, int window);
 hipError_t launch_hca_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
+// Attention backward followed by the compressor backward (raw rows of whole
+// blocks get w * dkc added; dw written), for kv_pos0 = 0 and kc = compression
+// of the given raw rows.
+hipError_t launch_hca_attn_compress_bwd(int dt, BwdArgs a, const float* wk, const float* wv, float* dwk, float* dwv,
+                                        void* ws, hipStream_t st);
 size_t hca_bwd512_workspace_bytes(int batch, int seqlen_q, int64_t q_pos0, int n_blocks, int h_q, int h_kv,
                                   int block, int window);
-hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st);
+// fw_k/fw_v non-null: fused compressor backward into the raw-row gradients.
+hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st, const float* fw_k = nullptr,
+                                  const float* fw_v = nullptr);
 size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk);
 hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
 // dk/dv (fp32, accumulated) += the compressor's backward of dkc/dvc; dw_k/dw_v written.
 hipError_t launch_compress_bwd(int dt, const void* k, LStrides sk, const void* v, LStrides sv, const float* dkc,
                                LStrides sdkc, const float* dvc, LStrides sdvc, const float* wk, const float* wv,
                                float* dk, LStrides sdk, float* dv, LStrides sdv, float* dwk, float* dwv, int batch,
-                               int seqlen, int h, int d, int block, hipStream_t st);
+                               int seqlen, int h, int d, int block, hipStream_t st, bool dx = true);
 
 // DSA
 size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk);

@@ -265,3 +265,24 @@ def test_dsa_bwd_rejects_bad_arguments():
     assert call(dq=FAKE) == hca.HCA_ERR_INVALID
     assert call(dk=ctypes.c_void_p(1 << 34)) == hca.HCA_ERR_INVALID
     assert call(wsb=need - 1) == hca.HCA_ERR_WORKSPACE
+
+
+def test_attn_compress_bwd_rejects_bad_arguments():
+    lib = _lib()
+    need = lib.hca_attn_bwd_workspace_size(1, 1, 256, 0, 2, 2, 2, 512, 128, 128)
+    sq = S(0, 2 * 512, 512)
+    sc = S(0, 2 * 512, 512)
+    g = [ctypes.c_void_p((1 << 34) + (i << 28)) for i in range(7)]
+
+    def call(**kw):
+        return lib.hca_attn_compress_bwd(1, FAKE, sq, FAKE, sq, FAKE, sq, FAKE, sc, FAKE, sc, FAKE, sq,
+                                         ctypes.c_void_p(1 << 33), FAKE, sq, kw.get("wk", FAKE), FAKE, g[0], sq,
+                                         g[1], sq, g[2], sq, g[3], sc, g[4], sc, kw.get("dwk", g[5]), g[6], 1,
+                                         kw.get("s", 256), kw.get("nb", 2), 2, 2, 512, 128, 128, 0.04,
+                                         ctypes.c_void_p(1 << 40), need, None)
+    assert call(wk=None) == hca.HCA_ERR_INVALID
+    assert call(dwk=None) == hca.HCA_ERR_INVALID
+    assert call(nb=3) == hca.HCA_ERR_INVALID          # 3 blocks of 128 > 256 rows
+    assert "n_blocks" in hca.hca_last_error()
+    assert call(dwk=g[0]) == hca.HCA_ERR_INVALID      # dw_k inside dq
+    assert call(s=0) == hca.HCA_ERR_INVALID

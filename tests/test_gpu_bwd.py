@@ -168,6 +168,49 @@ def test_hca_attn_bwd_bf16_512(Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window,
         _check(name, g, r, BF16_TOL)
 
 
+@pytest.mark.parametrize("dtype,S,H,d,block,window", [("bf16", 1100, 2, 512, 128, 128), ("bf16", 700, 1, 512, 64, 100),
+                                                      ("f32", 300, 2, 64, 32, 40)])
+def test_hca_attn_compress_bwd(dtype, S, H, d, block, window):
+    """The fused layer backward (compressor share added inside the key-tile
+    kernel on the MFMA path) against the oracle's chain, and against the
+    two-call path (hca_attn_bwd then hca_compress_kv_bwd).  S is not a whole
+    number of blocks, so the rows past the last block take the window part
+    only."""
+    _say("attn+compress bwd", dtype, S, H, d, block, window)
+    bf = dtype == "bf16"
+    B = 1
+    q = synth.make_normal((B, S, H, d), 91, bf16=bf)
+    k = synth.make_normal((B, S, H, d), 92, bf16=bf)
+    v = synth.make_normal((B, S, H, d), 93, bf16=bf)
+    dout = synth.make_normal((B, S, H, d), 94, bf16=bf)
+    wk, wv = _softmax_w(H, block, 95), _softmax_w(H, block, 96)
+    scale = float(1.0 / np.sqrt(d))
+    kw = dict(window=window, block=block, scale=scale)
+    qd, kd, vd, gd = (_dev(x, bf) for x in (q, k, v, dout))
+    wkd, wvd = dev_f32(wk), dev_f32(wv)
+    kcd, vcd = hca.hca_compress_kv(kd, vd, wkd, wvd, block)
+    o, lse = hca.hca_attn_fwd(qd, kd, vd, kcd, vcd, **kw)
+    fused = hca.hca_attn_compress_bwd(qd, kd, vd, kcd, vcd, o, lse, gd, wkd, wvd, **kw)
+    two = list(hca.hca_attn_bwd(qd, kd, vd, kcd, vcd, o, lse, gd, **kw))
+    dk2, dv2, dwk2, dwv2 = hca.hca_compress_kv_bwd(kd, vd, two[3], two[4], wkd, wvd, block, dk=two[1], dv=two[2])
+    torch.cuda.synchronize()
+    q64, k64, v64, g64 = (f64(x, bf) for x in (q, k, v, dout))
+    kc64, vc64 = oracle.compress_kv(k64, wk, block), oracle.compress_kv(v64, wv, block)
+    rq, rk, rv, rkc, rvc = oracle.hca_attention_bwd(q64, k64, v64, kc64, vc64, g64, **kw)
+    ck, rwk = oracle.compress_kv_bwd(k64, wk, rkc, block)
+    cv, rwv = oracle.compress_kv_bwd(v64, wv, rvc, block)
+    tol = BF16_TOL if bf else F32_TOL
+    ref = (rq, rk + ck, rv + cv, rkc, rvc, rwk, rwv)
+    for name, g, r in zip(("dq", "dk", "dv", "dkc", "dvc", "dw_k", "dw_v"), fused, ref):
+        _check(name, g, r, tol)
+    # same arithmetic as the two-call path up to fp32 rounding of the final add
+    for name, a_, b_ in (("dq", fused[0], two[0]), ("dk", fused[1], dk2), ("dv", fused[2], dv2),
+                         ("dw_k", fused[5], dwk2), ("dw_v", fused[6], dwv2)):
+        err = rel_err(host(a_), host(b_))
+        _say(f"  fused vs two-call {name}: {err:.2e}")
+        assert err < 1e-5, name
+
+
 # ------------------------------------------------------------------ compressor
 
 @pytest.mark.parametrize("dtype,S,H,d,block", [("f32", 100, 2, 64, 7), ("bf16", 1000, 3, 512, 128),
