@@ -15,6 +15,8 @@ row at a time, following the ERNIE 5.5 Flash Base pages:
 * DSA: a lightweight indexer scores past positions per query and core
   attention runs on the top-k only (same sections; besthub page, section
   "1. Hybrid Sparse Attention").
+* CSA: the history compressed 4x, then a top-k selection over the compressed
+  entries (mirrorspeed page, same section; besthub page, same section).
 
 Points the pages leave open are fixed as stated in each module's docstring.
 The gradients (``*_bwd``) are the chain rule through these definitions (the
@@ -28,10 +30,12 @@ from .hca import (compress_kv, window_bounds, attend_row, hca_attention, visible
                   attend_row_bwd, hca_attention_bwd, compress_kv_bwd)
 from .dsa import (index_scores_row, topk_row, index_topk, sparse_attention, sparse_attention_bwd,
                   score_error_bounds, tie_free_row, tie_free_rows, valid_topk_row)
+from .csa import visible_entries, csa_index_topk, csa_attention, csa_forward, csa_tie_free_row
 
 __all__ = [
     "compress_kv", "window_bounds", "attend_row", "hca_attention", "visible_positions",
     "attend_row_bwd", "hca_attention_bwd", "compress_kv_bwd", "sparse_attention_bwd",
     "index_scores_row", "topk_row", "index_topk", "sparse_attention",
     "score_error_bounds", "tie_free_row", "tie_free_rows", "valid_topk_row",
+    "visible_entries", "csa_index_topk", "csa_attention", "csa_forward", "csa_tie_free_row",
 ]

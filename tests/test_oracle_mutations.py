@@ -104,3 +104,27 @@ def test_sparse_bwd_value_gradient_transposed(monkeypatch):
         return dq, dv, dk                    # key and value gradients swapped
     monkeypatch.setattr(oracle, "sparse_attention_bwd", bad)
     _expect_caught([tgrad.test_sparse_attention_bwd_matches_finite_differences])
+
+
+# ---------------------------------------------------------------- CSA
+import oracle.csa as ocsa  # noqa: E402
+import test_oracle_csa as tcsa  # noqa: E402
+
+
+def test_csa_visibility_counts_the_open_block(monkeypatch):
+    monkeypatch.setattr(ocsa, "visible_entries", lambda t, block: (t + block) // block)  # block not yet complete
+    _expect_caught([lambda: tcsa.test_selection_against_explicit_loops(4, 3),
+                    tcsa.test_k_covering_every_entry_is_dense_block_causal_attention])
+
+
+def test_csa_visibility_one_block_late(monkeypatch):
+    monkeypatch.setattr(ocsa, "visible_entries", lambda t, block: t // block)
+    _expect_caught([lambda: tcsa.test_selection_against_explicit_loops(4, 100),
+                    tcsa.test_k_covering_every_entry_is_dense_block_causal_attention])
+
+
+def test_csa_attention_reads_the_wrong_entries(monkeypatch):
+    real = ocsa.csa_attention
+    # every selected entry replaced by entry 0
+    monkeypatch.setattr(ocsa, "csa_attention", lambda q, kc, vc, idx, scale: real(q, kc, vc, np.minimum(idx, 0), scale))
+    _expect_caught([tcsa.test_k_covering_every_entry_is_dense_block_causal_attention])
