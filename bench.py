@@ -7,6 +7,9 @@ are timed in the same run and reported under `components`:
   * HCA prefill at 131072 tokens (window 256): compression, attention, both;
   * HCA decode: 64 sequences x 1 query over 8192 compressed entries + 128 raw;
   * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention;
+  * CSA prefill at 65536 tokens (the DSA shapes with K, V and the index keys
+    compressed by blocks of 4): compression, indexer + top-2048 over the
+    16384 entries, sparse attention;
   * HCA training backward at 32768 tokens: the attention backward (dq, dk,
     dv, dkc, dvc) alone, and the layer backward (attention and compressor:
     dk/dv through both paths, the compressor weight gradients).
@@ -277,6 +280,57 @@ def bench_dsa_decode(torch, hca, steps, warmup):
     return res
 
 
+def csa_work(cfg):
+    """(indexer FLOPs, attention FLOPs, selected pairs) of the CSA step."""
+    S, k, blk = cfg.seqlen, cfg.topk, cfg.block
+    vis = [(t + 1) // blk for t in range(S)]
+    idx_flops = sum(vis) * cfg.h_i * (2 * cfg.d_i + 2)
+    sel = sum(min(n, k) for n in vis)
+    attn_flops = 2.0 * (cfg.d_qk + cfg.d_v) * cfg.h_q * sel
+    return idx_flops, attn_flops, sel
+
+
+def bench_csa(torch, hca, synth, cfg, steps, warmup):
+    import numpy as np
+    t0 = time.time()
+    inp = synth.make_csa(cfg)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    qI, kI, w = (torch.from_numpy(inp[n]).to("cuda:0") for n in ("qI", "kI", "w"))
+    wkv, wi = torch.from_numpy(inp["w_kv"]).to("cuda:0"), torch.from_numpy(inp["w_i"]).to("cuda:0")
+    del inp
+    log(f"[bench] csa: inputs ready in {time.time() - t0:.1f}s")
+    n = cfg.n_entries
+    kc = torch.empty((cfg.batch, n, 1, cfg.d_qk), dtype=torch.bfloat16, device="cuda:0")
+    vc = torch.empty_like(kc)
+    kI4 = kI[:, :, None, :]
+    kIc4 = torch.empty((cfg.batch, n, 1, cfg.d_i), dtype=torch.float32, device="cuda:0")
+    kIc4_v = torch.empty_like(kIc4)
+    kIc = kIc4[:, :, 0]
+    idx = torch.empty((cfg.batch, cfg.seqlen, cfg.topk), dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(hca.csa_index_topk_workspace_size(cfg.batch, cfg.seqlen, n, cfg.topk), dtype=torch.uint8,
+                     device="cuda:0")
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, cfg.h_q, cfg.seqlen), dtype=torch.float32, device="cuda:0")
+    fc = lambda: (hca.hca_compress_kv(k, v, wkv, wkv, cfg.block, kc=kc, vc=vc),
+                  hca.hca_compress_kv(kI4, kI4, wi, wi, cfg.block, kc=kIc4, vc=kIc4_v))
+    fi = lambda: hca.csa_index_topk(qI, kIc, w, cfg.topk, cfg.block, idx=idx, workspace=ws)
+    fa = lambda: hca.csa_sparse_attn_fwd(q, kc, vc, idx, scale=cfg.scale, o=o, lse=lse)
+    for _ in range(warmup):
+        fc()
+        fi()
+        fa()
+    tc, ti, ta = Timer(torch), Timer(torch), Timer(torch)
+    for _ in range(steps):
+        tc(fc)
+        ti(fi)
+        ta(fa)
+    res = {"compress_ms": tc.mean_ms(), "index_topk_ms": ti.mean_ms(), "attn_ms": ta.mean_ms()}
+    del q, k, v, qI, kI, w, kc, vc, kIc4, kIc4_v, idx, ws, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def backward_work(cfg):
     """(FLOPs, algorithmic bytes) of the HCA attention backward: 10*d FLOPs per
     visible (query head, key) pair (S, dP, dQ, dK, dV); reads Q, K, V, O, dO
@@ -364,7 +418,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c3,c4,c5,c5d,bwd",
+    ap.add_argument("--only", default="c2,c3,c4,c5,c5d,csa,bwd",
                     help="comma list of workloads to run (c2 always runs; 'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -446,6 +500,19 @@ def main():
         comps["dsa_decode_1m"] = bench_dsa_decode(torch, hca, args.steps, args.warmup)
         log(f"[bench] c5d done: {comps['dsa_decode_1m']}")
 
+    if "csa" in only:
+        cc = synth.CSA_CONFIGS["csa64k"]
+        rc = bench_csa(torch, hca, synth, cc, max(2, args.steps // 5), 1)
+        fi_c, fa_c, sel_c = csa_work(cc)
+        tot = rc["compress_ms"] + rc["index_topk_ms"] + rc["attn_ms"]
+        comps["csa_prefill_64k"] = {
+            "compress_ms": rc["compress_ms"], "index_topk_ms": rc["index_topk_ms"], "attn_ms": rc["attn_ms"],
+            "e2e_ms": tot, "tokens_per_s": cc.seqlen / tot * 1e3,
+            "index_tflops_f32": fi_c / rc["index_topk_ms"] / 1e9,
+            "attn_tflops": fa_c / rc["attn_ms"] / 1e9,
+            "attn_mfma_frac": fa_c / rc["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+        }
+        log(f"[bench] csa done: {comps['csa_prefill_64k']}")
     if "bwd" in only:
         rb = bench_backward(torch, hca, synth, c2, max(3, args.steps // 2), 2)
         fb, bb = backward_work(c2)

@@ -276,6 +276,64 @@ hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
                                     void* stream);
 
 /* ---------------------------------------------------------------------------
+ * CSA (compressed sparse attention): the history compressed 4x, then a top-k
+ * selection over the compressed entries (mirrorspeed page, "Hybrid sparse
+ * attention" section: the common CSA + HCA design; besthub page, "Core
+ * Architectural Innovations -- 1. Hybrid Sparse Attention").  The compressed
+ * K, V and index keys come from hca_compress_kv with block = 4 (the index
+ * keys as one fp32 head).  Entry j covers positions block*j .. block*j +
+ * block - 1 and belongs to the history of position t once its block is
+ * complete: block*j + block - 1 <= t.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes csa_index_topk needs (score rows for one chunk of queries). */
+size_t csa_index_topk_workspace_size(int batch, int seqlen, int n_entries, int topk);
+
+/*
+ * csa_index_topk -- the DSA indexer over the compressed entries visible to each
+ * position, then the top-k of them (same ranking as dsa_index_topk: larger
+ * fp32 score first, the smaller entry index on a tie):
+ *   s(t, j) = sum_h w[b,t,h] * max(0, <q_idx[b,t,h,:], k_idx[b,j,:]>),  j < (t + 1) / block
+ *   q_idx: [batch, seqlen, h_i, d_i] fp32 contiguous; w_idx: [batch, seqlen, h_i] fp32 contiguous
+ *   k_idx: [batch, n_entries, d_i] fp32 contiguous (the compressed index keys)
+ *   idx  : [batch, seqlen, topk] int32 contiguous (written): the selected entry
+ *          indices in unspecified order, then -1 (a position before the first
+ *          complete block lists none).
+ * Errors: HCA_ERR_INVALID when n_entries < seqlen / block (the last position
+ * needs more entries), for NULL or misaligned tensors, or when idx overlaps an
+ * input; HCA_ERR_WORKSPACE for a missing or short workspace.
+ * Supported: h_i in {4, 8}, d_i a multiple of 16 <= 128, topk <= 4096.
+ */
+hca_status_t csa_index_topk(const float* q_idx, const float* k_idx, const float* w_idx,
+                            int32_t* idx,
+                            int batch, int seqlen, int n_entries, int block,
+                            int h_i, int d_i, int topk,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * csa_sparse_attn_fwd -- attention of each position over the compressed
+ * entries listed in its row of idx (from csa_index_topk):
+ *   o[b,t,h,:] = sum_{j in idx[b,t,:], j >= 0} softmax_j(scale * <q[b,t,h], kc[b,j,g]>) * vc[b,j,g,:]
+ * with g = h / (h_q / h_kv); conventions as dsa_sparse_attn_fwd (every listed
+ * entry in [0, n_entries), else the row is NaN; a row listing none gives o = 0,
+ * lse = -inf).
+ *   q: [batch, seqlen, h_q, d_qk]; kc: [batch, n_entries, h_kv, d_qk]; vc: [batch, n_entries, h_kv, d_v];
+ *   idx: [batch, seqlen, topk] int32; o: [batch, seqlen, h_q, d_v]; lse: [batch, h_q, seqlen] fp32 or NULL.
+ * Supported: as dsa_sparse_attn_fwd (bf16, d_qk = d_v = 256, h_q / h_kv a multiple of 64).
+ */
+hca_status_t csa_sparse_attn_fwd(hca_dtype_t dt,
+                                 const void* q, hca_strides_t sq,
+                                 const void* kc, hca_strides_t skc,
+                                 const void* vc, hca_strides_t svc,
+                                 const int32_t* idx,
+                                 void* o, hca_strides_t so,
+                                 float* lse,
+                                 int batch, int seqlen, int n_entries, int h_q, int h_kv, int d_qk, int d_v,
+                                 int topk, float scale,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------
  * Backward.  The pages describe the forward only (mirrorspeed page, "Hybrid
  * sparse attention" section; training reaches 128K-token contexts).  The
  * gradients below are the chain rule through the forward definitions above:

@@ -31,6 +31,7 @@ EXPORTS = (
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
+    "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd",
 )
 
 
@@ -82,6 +83,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_index_topk_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, SZ, P]
     lib.dsa_sparse_attn_decode.restype = I
     lib.dsa_sparse_attn_decode.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
+    lib.csa_index_topk_workspace_size.restype = SZ
+    lib.csa_index_topk_workspace_size.argtypes = [I, I, I, I]
+    lib.csa_index_topk.restype = I
+    lib.csa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, SZ, P]
+    lib.csa_sparse_attn_fwd.restype = I
+    lib.csa_sparse_attn_fwd.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, I, F, P]
     lib.hca_attn_bwd_workspace_size.restype = SZ
     lib.hca_attn_bwd_workspace_size.argtypes = [I, I, I, I64, I, I, I, I, I, I]
     lib.hca_attn_bwd.restype = I
@@ -312,6 +319,55 @@ def dsa_sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, id
     return o, lse
 
 
+def csa_index_topk_workspace_size(batch: int, seqlen: int, n_entries: int, topk: int) -> int:
+    return load_library().csa_index_topk_workspace_size(batch, seqlen, n_entries, topk)
+
+
+def csa_index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w_idx: torch.Tensor, topk: int, block: int,
+                   idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexer + top-k over the compressed entries k_idx [B, n_entries, d_i] visible to each position
+    (entry j once (j + 1) * block - 1 <= t); returns idx [B, S, topk] int32 (-1 padded, unordered)."""
+    lib = load_library()
+    _dev(q_idx, k_idx, w_idx)
+    B, S, hi, di = q_idx.shape
+    n = k_idx.shape[1]
+    for t in (q_idx, k_idx, w_idx):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("indexer inputs must be contiguous float32")
+    if idx is None:
+        idx = torch.empty((B, S, topk), dtype=torch.int32, device=q_idx.device)
+    if workspace is None:
+        workspace = torch.empty(lib.csa_index_topk_workspace_size(B, S, n, topk), dtype=torch.uint8,
+                                device=q_idx.device)
+    _check(lib.csa_index_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(idx), B, S, n, block, hi, di, topk,
+                              _ptr(workspace), workspace.numel(), _stream()))
+    return idx
+
+
+def csa_sparse_attn_fwd(q: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, idx: torch.Tensor,
+                        scale: Optional[float] = None, o: Optional[torch.Tensor] = None, return_lse: bool = True,
+                        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of q [B, S, Hq, d] over the compressed entries kc, vc [B, n_entries, Hkv, d] listed in
+    idx [B, S, topk]; returns (o, lse)."""
+    lib = load_library()
+    _dev(q, kc, vc, idx)
+    B, S, Hq, dqk = q.shape
+    n, Hkv, dv = kc.shape[1], kc.shape[2], vc.shape[3]
+    topk = idx.shape[2]
+    if not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be contiguous int32 [B, S, topk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if o is None:
+        o = torch.empty((B, S, Hq, dv), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check(lib.csa_sparse_attn_fwd(_dt(q), _ptr(q), _strides(q), _ptr(kc), _strides(kc), _ptr(vc), _strides(vc),
+                                   _ptr(idx), _ptr(o), _strides(o), _ptr(lse), B, S, n, Hq, Hkv, dqk, dv, topk,
+                                   float(scale), _stream()))
+    return o, lse
+
+
 def hca_attn_bwd_workspace_size(dtype: torch.dtype, batch: int, seqlen_q: int, q_pos0: int, n_blocks: int, h_q: int,
                                 h_kv: int, head_dim: int, block: int, window: int) -> int:
     dt = HCA_DTYPE_BF16 if dtype == torch.bfloat16 else HCA_DTYPE_F32
@@ -461,4 +517,5 @@ __all__ = [
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
+    "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd",
 ]

@@ -37,12 +37,18 @@ constexpr int WAVES = 4; // a workgroup covers 32 queries x 128 keys
 
 struct ScoreParams {
   const float* qI;  // [S, h_i, d_i] of this batch
-  const float* kI;  // [S, d_i]
+  const float* kI;  // [n_keys, d_i]
   const float* w;   // [S, h_i]
   float* sc;        // [rows, ld] scores of rows r0 .. r0+rows-1
   int64_t ld;
   int seqlen, h_i, d_i, r0, rows;
+  // key u stands for positions block*u .. block*u + block - 1 and is visible
+  // to query t when its last position is <= t (block 1: u <= t)
+  int n_keys, block;
 };
+
+// Last key visible to query t (-1 when none).
+__device__ __forceinline__ int last_key(const ScoreParams& p, int t) { return (t + 1) / p.block - 1; }
 
 // S^T tile = kI (32 keys x d) . qI_h^T (d x 32 queries).  The contraction index
 // d = 32*(lane/32)... is mapped so that each lane reads a contiguous run: in
@@ -54,12 +60,12 @@ __global__ __launch_bounds__(256) void index_scores_kernel(ScoreParams p) {
   const int t0 = p.r0 + qt0;                        // absolute position
   const int k0 = blockIdx.x * (KT * WAVES) + w * KT;
   const int t_last = min(t0 + QT, p.r0 + p.rows) - 1;
-  if (k0 > t_last) return;                          // keys all in the future of every query
+  if (k0 > last_key(p, t_last)) return;             // keys all in the future of every query
   const int col = lane & 31, hf = lane >> 5;
   constexpr int HALF = DI / 2;
 
   // A operand: this lane's key row, d in [hf*HALF, hf*HALF + HALF)
-  const int key = min(k0 + col, p.seqlen - 1);
+  const int key = min(k0 + col, p.n_keys - 1);
   float ka[HALF];
   {
     const float* src = p.kI + (int64_t)key * DI + hf * HALF;
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(ScoreParams p) {
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg) {
     const int kk = k0 + 8 * rg + 4 * hf;
-    if (kk < p.seqlen) {  // ld is a multiple of 4 and >= seqlen rounded up to 4
+    if (kk < p.n_keys) {  // ld is a multiple of 4 and >= n_keys rounded up to 4
       f32x4 v = f32x4{score[4 * rg], score[4 * rg + 1], score[4 * rg + 2], score[4 * rg + 3]};
       *reinterpret_cast<f32x4*>(dst + 8 * rg) = v;
     }
@@ -117,7 +123,8 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
   const int t0 = p.r0 + qt0;                        // absolute position
   const int t_last = min(t0 + QT, p.r0 + p.rows) - 1;
   const int kbase = (blockIdx.x * WAVES + w) * (KG * KT);
-  if (kbase > t_last) return;                       // keys all in the future of every query
+  const int k_last = last_key(p, t_last);
+  if (kbase > k_last) return;                       // keys all in the future of every query
   const int col = lane & 31, hf = lane >> 5;
   constexpr int HALF = DI / 2;
 
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
   }
   // A operand of key tile kt: this lane's key row
   auto load_k = [&](int kt, float (&ka)[HALF]) __attribute__((always_inline)) {
-    const int key = min(kbase + kt * KT + col, p.seqlen - 1);
+    const int key = min(kbase + kt * KT + col, p.n_keys - 1);
     const float* src = p.kI + (int64_t)key * DI + hf * HALF;
 #pragma unroll
     for (int i = 0; i < HALF; i += 4) {
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
       ka[i] = v[0]; ka[i + 1] = v[1]; ka[i + 2] = v[2]; ka[i + 3] = v[3];
     }
   };
-  const int n_kt = min(KG, (t_last - kbase) / KT + 1);
+  const int n_kt = min(KG, (k_last - kbase) / KT + 1);
   const int qrow = qt0 + col;
   float ka[HALF], kn[HALF];
   load_k(0, ka);
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int kk = k0 + 8 * rg + 4 * hf;
-        if (kk < p.seqlen) {  // ld is a multiple of 4 and >= seqlen rounded up to 4
+        if (kk < p.n_keys) {  // ld is a multiple of 4 and >= n_keys rounded up to 4
           f32x4 v = f32x4{score[4 * rg], score[4 * rg + 1], score[4 * rg + 2], score[4 * rg + 3]};
           *reinterpret_cast<f32x4*>(dst + 8 * rg) = v;
         }
@@ -217,6 +224,9 @@ struct SelectParams {
   // 0 .. t.
   int nseg, seg_len, n_total;
   const int32_t* pos;
+  // prefill rows: the candidates of query t are keys 0 .. (t + 1) / block - 1
+  // (block <= 1: 0 .. t)
+  int block;
 };
 
 constexpr int NB = 2048;   // bins of the general radix passes (11 + 11 + 10 bits)
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     if (p.pos) prow = p.pos + (int64_t)b * p.ld + off;
   } else {
     const int t = p.r0 + row;
-    n = t + 1;
+    n = p.block > 1 ? (t + 1) / p.block : t + 1;
     srow = p.sc + (int64_t)row * p.ld;
     out = p.idx + (int64_t)t * k;
   }
@@ -830,35 +840,31 @@ __global__ __launch_bounds__(256) void decode_compact_kernel(const int32_t* sel,
   }
 }
 
-int chunk_rows(int seqlen) {
-  // keep one chunk of scores near 1 GB: few, large launches fill the GPU
-  int64_t r = ((int64_t)1 << 28) / (((int64_t)seqlen + 3) & ~3ll);
+// Query rows per chunk of score rows of row_len keys: keep one chunk near 1 GB
+// (few, large launches fill the GPU), at most all n_rows rows.
+int chunk_rows(int n_rows, int row_len) {
+  int64_t r = ((int64_t)1 << 28) / (((int64_t)row_len + 3) & ~3ll);
   if (r < 32) r = 32;
   r = r / 32 * 32;
-  if (r > seqlen) r = ((seqlen + 31) / 32) * 32;
+  if (r > n_rows) r = ((n_rows + 31) / 32) * 32;
   return (int)r;
 }
 
-}  // namespace
+int64_t score_ld(int n_keys) { return ((int64_t)n_keys + 127) / 128 * 128; }
 
-size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk) {
-  (void)batch;
-  (void)topk;
-  const int64_t ld = ((int64_t)seqlen + 127) / 128 * 128;
-  return (size_t)chunk_rows(seqlen) * ld * sizeof(float);
-}
-
-hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
-                                 int seqlen, int h_i, int d_i, int topk, void* ws, size_t ws_bytes, hipStream_t st) {
-  (void)ws_bytes;
-  const int64_t ld = ((int64_t)seqlen + 127) / 128 * 128;
-  const int R = chunk_rows(seqlen);
+// Scores + selection of seqlen queries over n_keys keys of granularity block
+// (DSA: n_keys = seqlen, block = 1), in chunks of query rows.
+hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
+                                  int seqlen, int n_keys, int block, int h_i, int d_i, int topk, void* ws,
+                                  hipStream_t st) {
+  const int64_t ld = score_ld(n_keys);
+  const int R = chunk_rows(seqlen, n_keys);
   for (int b = 0; b < batch; ++b) {
     for (int r0 = 0; r0 < seqlen; r0 += R) {
       const int rows = min(R, seqlen - r0);
       ScoreParams sp;
       sp.qI = qI + (int64_t)b * seqlen * h_i * d_i;
-      sp.kI = kI + (int64_t)b * seqlen * d_i;
+      sp.kI = kI + (int64_t)b * n_keys * d_i;
       sp.w = w + (int64_t)b * seqlen * h_i;
       sp.sc = (float*)ws;
       sp.ld = ld;
@@ -867,42 +873,75 @@ hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* 
       sp.d_i = d_i;
       sp.r0 = r0;
       sp.rows = rows;
-      const int key_tiles = (r0 + rows + KT * WAVES - 1) / (KT * WAVES);
-      dim3 grid(key_tiles, (rows + QT - 1) / QT);
-      const dim3 grid_qs((r0 + rows + KT * WAVES * KG - 1) / (KT * WAVES * KG), (rows + QT - 1) / QT);
-      bool qs = true;
-      if (h_i == 4 && d_i == 16) hipLaunchKernelGGL((index_scores_qs_kernel<16, 4>), grid_qs, dim3(256), 0, st, sp);
-      else if (h_i == 4 && d_i == 32) hipLaunchKernelGGL((index_scores_qs_kernel<32, 4>), grid_qs, dim3(256), 0, st, sp);
-      else if (h_i == 4 && d_i == 48) hipLaunchKernelGGL((index_scores_qs_kernel<48, 4>), grid_qs, dim3(256), 0, st, sp);
-      else if (h_i == 4 && d_i == 64) hipLaunchKernelGGL((index_scores_qs_kernel<64, 4>), grid_qs, dim3(256), 0, st, sp);
-      else if (h_i == 8 && d_i == 16) hipLaunchKernelGGL((index_scores_qs_kernel<16, 8>), grid_qs, dim3(256), 0, st, sp);
-      else if (h_i == 8 && d_i == 32) hipLaunchKernelGGL((index_scores_qs_kernel<32, 8>), grid_qs, dim3(256), 0, st, sp);
-      else qs = false;
-      if (!qs) switch (d_i) {
-        case 16: hipLaunchKernelGGL(index_scores_kernel<16>, grid, dim3(256), 0, st, sp); break;
-        case 32: hipLaunchKernelGGL(index_scores_kernel<32>, grid, dim3(256), 0, st, sp); break;
-        case 48: hipLaunchKernelGGL(index_scores_kernel<48>, grid, dim3(256), 0, st, sp); break;
-        case 64: hipLaunchKernelGGL(index_scores_kernel<64>, grid, dim3(256), 0, st, sp); break;
-        case 80: hipLaunchKernelGGL(index_scores_kernel<80>, grid, dim3(256), 0, st, sp); break;
-        case 96: hipLaunchKernelGGL(index_scores_kernel<96>, grid, dim3(256), 0, st, sp); break;
-        case 112: hipLaunchKernelGGL(index_scores_kernel<112>, grid, dim3(256), 0, st, sp); break;
-        case 128: hipLaunchKernelGGL(index_scores_kernel<128>, grid, dim3(256), 0, st, sp); break;
-        default: return hipErrorInvalidValue;
+      sp.n_keys = n_keys;
+      sp.block = block;
+      // keys visible to the chunk's last query
+      const int keys = min(n_keys, (r0 + rows) / block);
+      if (keys > 0) {
+        const int key_tiles = (keys + KT * WAVES - 1) / (KT * WAVES);
+        dim3 grid(key_tiles, (rows + QT - 1) / QT);
+        const dim3 grid_qs((keys + KT * WAVES * KG - 1) / (KT * WAVES * KG), (rows + QT - 1) / QT);
+        bool qs = true;
+        if (h_i == 4 && d_i == 16) hipLaunchKernelGGL((index_scores_qs_kernel<16, 4>), grid_qs, dim3(256), 0, st, sp);
+        else if (h_i == 4 && d_i == 32) hipLaunchKernelGGL((index_scores_qs_kernel<32, 4>), grid_qs, dim3(256), 0, st, sp);
+        else if (h_i == 4 && d_i == 48) hipLaunchKernelGGL((index_scores_qs_kernel<48, 4>), grid_qs, dim3(256), 0, st, sp);
+        else if (h_i == 4 && d_i == 64) hipLaunchKernelGGL((index_scores_qs_kernel<64, 4>), grid_qs, dim3(256), 0, st, sp);
+        else if (h_i == 8 && d_i == 16) hipLaunchKernelGGL((index_scores_qs_kernel<16, 8>), grid_qs, dim3(256), 0, st, sp);
+        else if (h_i == 8 && d_i == 32) hipLaunchKernelGGL((index_scores_qs_kernel<32, 8>), grid_qs, dim3(256), 0, st, sp);
+        else qs = false;
+        if (!qs) switch (d_i) {
+          case 16: hipLaunchKernelGGL(index_scores_kernel<16>, grid, dim3(256), 0, st, sp); break;
+          case 32: hipLaunchKernelGGL(index_scores_kernel<32>, grid, dim3(256), 0, st, sp); break;
+          case 48: hipLaunchKernelGGL(index_scores_kernel<48>, grid, dim3(256), 0, st, sp); break;
+          case 64: hipLaunchKernelGGL(index_scores_kernel<64>, grid, dim3(256), 0, st, sp); break;
+          case 80: hipLaunchKernelGGL(index_scores_kernel<80>, grid, dim3(256), 0, st, sp); break;
+          case 96: hipLaunchKernelGGL(index_scores_kernel<96>, grid, dim3(256), 0, st, sp); break;
+          case 112: hipLaunchKernelGGL(index_scores_kernel<112>, grid, dim3(256), 0, st, sp); break;
+          case 128: hipLaunchKernelGGL(index_scores_kernel<128>, grid, dim3(256), 0, st, sp); break;
+          default: return hipErrorInvalidValue;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
       }
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
       SelectParams pp{};
       pp.sc = (const float*)ws;
       pp.ld = ld;
       pp.idx = idx + (int64_t)b * seqlen * topk;
       pp.r0 = r0;
       pp.topk = topk;
+      pp.block = block;
       hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(256), 0, st, pp);
-      e = hipGetLastError();
+      hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk) {
+  (void)batch;
+  (void)topk;
+  return (size_t)chunk_rows(seqlen, seqlen) * score_ld(seqlen) * sizeof(float);
+}
+
+hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
+                                 int seqlen, int h_i, int d_i, int topk, void* ws, size_t ws_bytes, hipStream_t st) {
+  (void)ws_bytes;
+  return launch_index_topk_rows(qI, kI, w, idx, batch, seqlen, seqlen, 1, h_i, d_i, topk, ws, st);
+}
+
+size_t csa_topk_workspace_bytes(int batch, int seqlen, int n_keys, int topk) {
+  (void)batch;
+  (void)topk;
+  return (size_t)chunk_rows(seqlen, n_keys) * score_ld(n_keys) * sizeof(float);
+}
+
+hipError_t launch_csa_index_topk(const float* qI, const float* kIc, const float* w, int32_t* idx, int batch,
+                                 int seqlen, int n_keys, int block, int h_i, int d_i, int topk, void* ws,
+                                 hipStream_t st) {
+  return launch_index_topk_rows(qI, kIc, w, idx, batch, seqlen, n_keys, block, h_i, d_i, topk, ws, st);
 }
 
 size_t dsa_topk_decode_workspace_bytes(int batch, int n_keys, int topk) {

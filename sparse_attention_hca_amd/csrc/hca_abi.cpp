@@ -601,6 +601,53 @@ hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt, const void* q, hca_strides_t
                      d_qk, d_v, topk, scale, stream);
 }
 
+size_t csa_index_topk_workspace_size(int batch, int seqlen, int n_entries, int topk) {
+  if (batch <= 0 || seqlen <= 0 || n_entries <= 0 || topk <= 0) return 0;
+  return hca::csa_topk_workspace_bytes(batch, seqlen, n_entries, topk);
+}
+
+hca_status_t csa_index_topk(const float* q_idx, const float* k_idx, const float* w_idx, int32_t* idx, int batch,
+                            int seqlen, int n_entries, int block, int h_i, int d_i, int topk, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!q_idx || !k_idx || !w_idx || !idx) return fail(HCA_ERR_INVALID, "csa_index_topk: NULL tensor");
+  if (batch <= 0 || seqlen <= 0 || n_entries <= 0 || block <= 0 || h_i <= 0 || d_i <= 0 || topk <= 0)
+    return fail(HCA_ERR_INVALID, "csa_index_topk: sizes must be positive");
+  if (seqlen / block > n_entries)
+    return fail(HCA_ERR_INVALID, "csa_index_topk: the last query needs %d entries, %d given", seqlen / block,
+                n_entries);
+  if ((int64_t)seqlen > kPosLimit)
+    return fail(HCA_ERR_UNSUPPORTED, "csa_index_topk: positions beyond 2^30 are not supported");
+  if (h_i > 8 || h_i % 4 || d_i % 16 || d_i > 128 || topk > 4096)
+    return fail(HCA_ERR_UNSUPPORTED,
+                "csa_index_topk: needs h_i 4 or 8, d_i a multiple of 16 <= 128, topk <= 4096");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(idx))
+    return fail(HCA_ERR_INVALID, "csa_index_topk: tensors must be 16-byte aligned");
+  {
+    const Range ri{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)};
+    const Range rq{(uintptr_t)q_idx, (uintptr_t)(q_idx + (size_t)batch * seqlen * h_i * d_i)};
+    const Range rk{(uintptr_t)k_idx, (uintptr_t)(k_idx + (size_t)batch * n_entries * d_i)};
+    const Range rw{(uintptr_t)w_idx, (uintptr_t)(w_idx + (size_t)batch * seqlen * h_i)};
+    if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(ri, rw))
+      return fail(HCA_ERR_INVALID, "csa_index_topk: idx overlaps an input");
+  }
+  const size_t need = hca::csa_topk_workspace_bytes(batch, seqlen, n_entries, topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(HCA_ERR_WORKSPACE, "csa_index_topk needs a %zu-byte workspace (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
+  hipError_t e = hca::launch_csa_index_topk(q_idx, k_idx, w_idx, idx, batch, seqlen, n_entries, block, h_i, d_i,
+                                            topk, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "csa_index_topk launch");
+  return HCA_OK;
+}
+
+hca_status_t csa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* kc, hca_strides_t skc,
+                                 const void* vc, hca_strides_t svc, const int32_t* idx, void* o, hca_strides_t so,
+                                 float* lse, int batch, int seqlen, int n_entries, int h_q, int h_kv, int d_qk,
+                                 int d_v, int topk, float scale, void* stream) {
+  return sparse_attn("csa_sparse_attn_fwd", dt, q, sq, kc, skc, vc, svc, idx, o, so, lse, batch, seqlen, n_entries,
+                     h_q, h_kv, d_qk, d_v, topk, scale, stream);
+}
+
 size_t dsa_index_topk_decode_workspace_size(int batch, int n_keys, int topk) {
   if (batch <= 0 || n_keys <= 0 || topk <= 0) return 0;
   return hca::dsa_topk_decode_workspace_bytes(batch, n_keys, topk);

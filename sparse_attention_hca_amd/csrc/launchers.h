@@ -97,6 +97,12 @@ hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* 
 size_t dsa_topk_decode_workspace_bytes(int batch, int n_keys, int topk);
 hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
                                         int n_keys, int h_i, int d_i, int topk, void* ws, hipStream_t st);
+// CSA: seqlen queries over n_keys compressed index keys; key u is visible to
+// query t when (u + 1) * block - 1 <= t.
+size_t csa_topk_workspace_bytes(int batch, int seqlen, int n_keys, int topk);
+hipError_t launch_csa_index_topk(const float* qI, const float* kIc, const float* w, int32_t* idx, int batch,
+                                 int seqlen, int n_keys, int block, int h_i, int d_i, int topk, void* ws,
+                                 hipStream_t st);
 // Sparse attention of seqlen queries per sequence; selected positions must lie in [0, n_kv).
 hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, LStrides sk, const void* v,
                                      LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,

@@ -83,6 +83,30 @@ class DsaConfig:
         return 1.0 / math.sqrt(self.d_qk)
 
 
+@dataclass(frozen=True)
+class CsaConfig:
+    """CSA: the DSA shapes with K, V and the index keys compressed per block."""
+    name: str
+    batch: int
+    seqlen: int
+    h_q: int
+    d_qk: int
+    d_v: int
+    h_i: int
+    d_i: int
+    topk: int
+    block: int
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+    @property
+    def n_entries(self) -> int:
+        return self.seqlen // self.block
+
+
 _S512 = 1.0 / math.sqrt(512.0)
 
 CONFIGS = {
@@ -98,6 +122,12 @@ CONFIGS = {
     "c5": DsaConfig("c5", 1, 65536, 64, 256, 256, 4, 64, 2048),
 }
 
+# CSA workload (no config of its own in the headline list): c5's shapes with
+# the history compressed by blocks of 4 (16384 entries), top-2048 entries.
+CSA_CONFIGS = {
+    "csa64k": CsaConfig("csa64k", 1, 65536, 64, 256, 256, 4, 64, 2048, 4),
+}
+
 
 def small_prefill(base: str = "c2", **kw) -> HcaPrefillConfig:
     """A reduced copy of a prefill config (for parity at oracle-friendly sizes)."""
@@ -110,3 +140,7 @@ def small_decode(**kw) -> HcaDecodeConfig:
 
 def small_dsa(**kw) -> DsaConfig:
     return replace(CONFIGS["c5"], name=kw.pop("name", "c5-small"), **kw)
+
+
+def small_csa(**kw) -> CsaConfig:
+    return replace(CSA_CONFIGS["csa64k"], name=kw.pop("name", "csa-small"), **kw)

@@ -12,6 +12,9 @@ bfloat16 with round-to-nearest-even when the workload is bf16):
   and w can be redrawn from the sub-stream (seed, b, t, attempt) so that a
   caller can replace rows whose top-k boundary is too close to call.
 
+* CSA: Q, K, V (bf16), then qI, kI, w (float32) as DSA, then z_kv and z_i
+  [1, block]; the compressor weights of K/V and of the index keys are
+  softmax(z) as for HCA.  Rows of qI and w are redrawn as for DSA.
 * Free-standing tensors (gradients flowing into a backward call, inputs of
   other shapes): ``make_normal(shape, seed, std, bf16)``, one generator per
   call.
@@ -26,7 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import HcaPrefillConfig, HcaDecodeConfig, DsaConfig
+from .configs import HcaPrefillConfig, HcaDecodeConfig, DsaConfig, CsaConfig
 
 _CHUNK = 1 << 24
 
@@ -139,3 +142,20 @@ def make_index_lists(batch: int, seqlen: int, topk: int, seed: int, n_valid=None
                     row[dst] = row[src]
             out[b, t, :n] = row
     return out
+
+
+def make_csa(cfg: CsaConfig) -> dict:
+    """make_dsa's tensors for the CSA shapes plus compressor weights w_kv, w_i [1, block] (float32)."""
+    rng = np.random.default_rng(cfg.seed)
+    B, S = cfg.batch, cfg.seqlen
+    q = _normal(rng, (B, S, cfg.h_q, cfg.d_qk), 1.0, True)
+    k = _normal(rng, (B, S, 1, cfg.d_qk), 1.0, True)
+    v = _normal(rng, (B, S, 1, cfg.d_v), 1.0, True)
+    qI = _normal(rng, (B, S, cfg.h_i, cfg.d_i), 1.0, False)
+    kI = _normal(rng, (B, S, cfg.d_i), 1.0, False)
+    w = _normal(rng, (B, S, cfg.h_i), 1.0, False)
+    z_kv = rng.standard_normal((1, cfg.block), dtype=np.float32)
+    z_i = rng.standard_normal((1, cfg.block), dtype=np.float32)
+    return {"cfg": cfg, "q": q, "k": k, "v": v, "qI": qI, "kI": kI, "w": w,
+            "w_kv": _softmax_weights(z_kv), "w_i": _softmax_weights(z_i),
+            "redraws": np.zeros((B, S), dtype=np.int32)}

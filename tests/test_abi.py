@@ -21,7 +21,7 @@ FAKE = ctypes.c_void_p(1 << 20)   # aligned non-null pointer; never dereferenced
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:hca|dsa)_[a-z0-9_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b((?:hca|dsa|csa)_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_and_exports_agree():
@@ -286,3 +286,29 @@ def test_attn_compress_bwd_rejects_bad_arguments():
     assert "n_blocks" in hca.hca_last_error()
     assert call(dwk=g[0]) == hca.HCA_ERR_INVALID      # dw_k inside dq
     assert call(s=0) == hca.HCA_ERR_INVALID
+
+
+def test_csa_rejects_bad_arguments():
+    lib = _lib()
+    ws = lib.csa_index_topk_workspace_size(1, 4096, 1024, 256)
+    assert ws >= 1024 * 4 and lib.csa_index_topk_workspace_size(1, 4096, 0, 256) == 0
+    call = lambda **kw: lib.csa_index_topk(kw.get("q", FAKE), ctypes.c_void_p(1 << 33), ctypes.c_void_p(1 << 34),
+                                           kw.get("idx", ctypes.c_void_p(1 << 36)), 1, 4096, kw.get("n", 1024),
+                                           kw.get("block", 4), kw.get("hi", 4), 64, kw.get("k", 256),
+                                           kw.get("ws", ctypes.c_void_p(1 << 40)), kw.get("wsb", ws), None)
+    assert call(q=None) == hca.HCA_ERR_INVALID
+    assert call(n=1023) == hca.HCA_ERR_INVALID           # position 4095 needs 1024 entries
+    assert "entries" in hca.hca_last_error()
+    assert call(block=0) == hca.HCA_ERR_INVALID
+    assert call(hi=6) == hca.HCA_ERR_UNSUPPORTED
+    assert call(k=5000) == hca.HCA_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == hca.HCA_ERR_WORKSPACE
+    assert call(idx=FAKE) == hca.HCA_ERR_INVALID         # idx aliases q_idx
+    sp = lambda **kw: lib.csa_sparse_attn_fwd(1, FAKE, S(0, 64 * 256, 256), ctypes.c_void_p(1 << 33),
+                                              S(0, 256, 256), ctypes.c_void_p(1 << 34), S(0, 256, 256),
+                                              kw.get("idx", ctypes.c_void_p(1 << 35)), kw.get("o", ctypes.c_void_p(1 << 36)),
+                                              S(0, 64 * 256, 256), None, 1, 4096, kw.get("n", 1024), 64, 1, 256,
+                                              256, 64, 0.0625, None)
+    assert sp(idx=None) == hca.HCA_ERR_INVALID
+    assert sp(n=0) == hca.HCA_ERR_INVALID
+    assert sp(o=FAKE) == hca.HCA_ERR_INVALID             # o aliases q
