@@ -17,6 +17,10 @@ row at a time, following the ERNIE 5.5 Flash Base pages:
   "1. Hybrid Sparse Attention").
 * CSA: the history compressed 4x, then a top-k selection over the compressed
   entries (mirrorspeed page, same section; besthub page, same section).
+* Attention-output epilogues: the output gate from the low-rank query latent
+  and Virtual Head Attention's low-rank cross-head mixing (mirrorspeed page,
+  section "More structural improvements, data, and infrastructure"; besthub
+  page, section "Core Architectural Innovations").
 
 Points the pages leave open are fixed as stated in each module's docstring.
 The gradients (``*_bwd``) are the chain rule through these definitions (the
@@ -31,6 +35,7 @@ from .hca import (compress_kv, window_bounds, attend_row, hca_attention, visible
 from .dsa import (index_scores_row, topk_row, index_topk, sparse_attention, sparse_attention_bwd,
                   score_error_bounds, tie_free_row, tie_free_rows, valid_topk_row)
 from .csa import visible_entries, csa_index_topk, csa_attention, csa_forward, csa_tie_free_row
+from .epilogue import sigmoid, gate_values, vha_mix, gated_vha_output
 
 __all__ = [
     "compress_kv", "window_bounds", "attend_row", "hca_attention", "visible_positions",
@@ -38,4 +43,5 @@ __all__ = [
     "index_scores_row", "topk_row", "index_topk", "sparse_attention",
     "score_error_bounds", "tie_free_row", "tie_free_rows", "valid_topk_row",
     "visible_entries", "csa_index_topk", "csa_attention", "csa_forward", "csa_tie_free_row",
+    "sigmoid", "gate_values", "vha_mix", "gated_vha_output",
 ]

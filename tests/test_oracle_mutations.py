@@ -128,3 +128,30 @@ def test_csa_attention_reads_the_wrong_entries(monkeypatch):
     # every selected entry replaced by entry 0
     monkeypatch.setattr(ocsa, "csa_attention", lambda q, kc, vc, idx, scale: real(q, kc, vc, np.minimum(idx, 0), scale))
     _expect_caught([tcsa.test_k_covering_every_entry_is_dense_block_causal_attention])
+
+
+# ---------------------------------------------------------------- epilogues
+import oracle.epilogue as oepi  # noqa: E402
+import test_oracle_epilogue as tepi  # noqa: E402
+
+
+def test_vha_mixing_matrix_transposed(monkeypatch):
+    def bad(o, u, v):
+        m = (np.asarray(u) @ np.asarray(v)).T
+        return np.asarray(o) + np.einsum("gh,bshd->bsgd", m, np.asarray(o))
+    monkeypatch.setattr(oepi, "vha_mix", bad)
+    monkeypatch.setattr(oracle, "vha_mix", bad)
+    _expect_caught([tepi.test_vha_against_explicit_loops, tepi.test_vha_special_cases])
+
+
+def test_gate_applied_before_mixing(monkeypatch):
+    def bad(o, c, w_g, u, v):
+        return oepi.vha_mix(oepi.gate_values(c, w_g, o.shape[2], o.shape[3]) * o, u, v)
+    monkeypatch.setattr(oepi, "gated_vha_output", bad)
+    monkeypatch.setattr(oracle, "gated_vha_output", bad)
+    _expect_caught([tepi.test_output_is_gate_times_mixed])
+
+
+def test_gate_tanh_for_sigmoid(monkeypatch):
+    monkeypatch.setattr(oepi, "sigmoid", lambda x: np.tanh(np.asarray(x, dtype=np.float64)))
+    _expect_caught([tepi.test_gate_closed_forms, tepi.test_gate_against_explicit_loops_and_torch])
