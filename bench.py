@@ -10,6 +10,8 @@ are timed in the same run and reported under `components`:
   * CSA prefill at 65536 tokens (the DSA shapes with K, V and the index keys
     compressed by blocks of 4): compression, indexer + top-2048 over the
     16384 entries, sparse attention;
+  * attention-output epilogue at the 32768-token HCA shape: the low-rank
+    output gate (latent 2048 -> 16 x 512, sigmoid) and VHA mixing (rank 4);
   * HCA training backward at 32768 tokens: the attention backward (dq, dk,
     dv, dkc, dvc) alone, and the layer backward (attention and compressor:
     dk/dv through both paths, the compressor weight gradients).
@@ -331,6 +333,36 @@ def bench_csa(torch, hca, synth, cfg, steps, warmup):
     return res
 
 
+EPILOGUE = dict(batch=1, seqlen=32768, h=16, d_v=512, d_c=2048, r=4)
+
+
+def bench_epilogue(torch, hca, steps, warmup):
+    e = EPILOGUE
+    B, S, H, dv, dc, r = e["batch"], e["seqlen"], e["h"], e["d_v"], e["d_c"], e["r"]
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(7)
+    o = torch.randn((B, S, H, dv), generator=g, device="cuda:0").to(torch.bfloat16)
+    c = torch.randn((B, S, dc), generator=g, device="cuda:0").to(torch.bfloat16)
+    w = (torch.randn((H * dv, dc), generator=g, device="cuda:0") / dc ** 0.5).to(torch.bfloat16)
+    u = torch.randn((H, r), generator=g, device="cuda:0") * 0.5
+    v = torch.randn((r, H), generator=g, device="cuda:0") * 0.5
+    y = torch.empty_like(o)
+    f = lambda: hca.attn_output_epilogue(o, c, w, u, v, y=y)
+    for _ in range(warmup):
+        f()
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    ms = tm.mean_ms()
+    flops = 2.0 * B * S * H * dv * dc
+    byts = 2 * (B * S * dc + H * dv * dc + 2 * B * S * H * dv)
+    del o, c, w, u, v, y
+    torch.cuda.empty_cache()
+    return {"ms": ms, "tokens_per_s": B * S / ms * 1e3, "gate_tflops": flops / ms / 1e9,
+            "gate_mfma_frac": flops / ms / 1e9 / PEAK_BF16_TFLOPS, "gbs": byts / ms / 1e6,
+            "flops": flops, "algorithmic_bytes": byts}
+
+
 def backward_work(cfg):
     """(FLOPs, algorithmic bytes) of the HCA attention backward: 10*d FLOPs per
     visible (query head, key) pair (S, dP, dQ, dK, dV); reads Q, K, V, O, dO
@@ -418,7 +450,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c3,c4,c5,c5d,csa,bwd",
+    ap.add_argument("--only", default="c2,c3,c4,c5,c5d,csa,epi,bwd",
                     help="comma list of workloads to run (c2 always runs; 'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -513,6 +545,9 @@ def main():
             "attn_mfma_frac": fa_c / rc["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
         }
         log(f"[bench] csa done: {comps['csa_prefill_64k']}")
+    if "epi" in only:
+        comps["attn_epilogue_32k"] = bench_epilogue(torch, hca, args.steps, args.warmup)
+        log(f"[bench] epilogue done: {comps['attn_epilogue_32k']}")
     if "bwd" in only:
         rb = bench_backward(torch, hca, synth, c2, max(3, args.steps // 2), 2)
         fb, bb = backward_work(c2)

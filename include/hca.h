@@ -333,6 +333,35 @@ hca_status_t csa_sparse_attn_fwd(hca_dtype_t dt,
                                  int topk, float scale,
                                  void* stream);
 
+/*
+ * attn_output_epilogue -- the two attention-output epilogues of the pages
+ * (mirrorspeed page, section "More structural improvements, data, and
+ * infrastructure"; besthub page, section "Core Architectural Innovations"):
+ * the output gate computed from the layer's low-rank query latent c (a
+ * quarter of the hidden size) and Virtual Head Attention's low-rank mixing
+ * of the heads with an identity skip; heads are mixed first, then gated:
+ *   y[b,t,h,e] = sigmoid(<c[b,t,:], w_g[h*d_v + e, :]>) * (o[b,t,h,e] + sum_h' (u v)[h,h'] o[b,t,h',e])
+ *   o  : [batch, seqlen, h, d_v] bf16, the attention output (read)
+ *   c  : [batch, seqlen, 1, d_c] bf16, the query latent (read)
+ *   w_g: [h * d_v, d_c] bf16 contiguous (the [out, in] layout of a linear layer)
+ *   u  : [h, r] fp32 contiguous; v: [r, h] fp32 contiguous
+ *   y  : [batch, seqlen, h, d_v] bf16 (written; must not overlap an input)
+ * c and y must be token-contiguous across the batch (batch stride = seqlen *
+ * seq stride).  The gate projection runs on the matrix cores (fp32
+ * accumulation, sigmoid in fp32) and is stored in y as bf16, which the mixing
+ * kernel then scales in place.
+ * Supported: bf16, h in {8, 16, 32, 64}, r <= 16, d_c a multiple of 32,
+ * h * d_v a multiple of 256, d_v a multiple of 8 and at most 512.
+ */
+hca_status_t attn_output_epilogue(hca_dtype_t dt,
+                                  const void* o, hca_strides_t so,
+                                  const void* c, hca_strides_t sc,
+                                  const void* w_g,
+                                  const float* u, const float* v,
+                                  void* y, hca_strides_t sy,
+                                  int batch, int seqlen, int h, int d_v, int d_c, int r,
+                                  void* stream);
+
 /* ---------------------------------------------------------------------------
  * Backward.  The pages describe the forward only (mirrorspeed page, "Hybrid
  * sparse attention" section; training reaches 128K-token contexts).  The

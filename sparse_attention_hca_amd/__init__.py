@@ -31,7 +31,7 @@ EXPORTS = (
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
-    "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd",
+    "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd", "attn_output_epilogue",
 )
 
 
@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, SZ, P]
     lib.csa_sparse_attn_fwd.restype = I
     lib.csa_sparse_attn_fwd.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, I, F, P]
+    lib.attn_output_epilogue.restype = I
+    lib.attn_output_epilogue.argtypes = [I, P, S, P, S, P, P, P, P, S, I, I, I, I, I, I, P]
     lib.hca_attn_bwd_workspace_size.restype = SZ
     lib.hca_attn_bwd_workspace_size.argtypes = [I, I, I, I64, I, I, I, I, I, I]
     lib.hca_attn_bwd.restype = I
@@ -368,6 +370,26 @@ def csa_sparse_attn_fwd(q: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, idx
     return o, lse
 
 
+def attn_output_epilogue(o: torch.Tensor, c: torch.Tensor, w_g: torch.Tensor, u: torch.Tensor, v: torch.Tensor,
+                         y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = sigmoid(c w_g^T) * (o + (u v) o across heads) for o [B, S, H, d_v] and the query latent
+    c [B, S, d_c] (bf16), w_g [H*d_v, d_c] (bf16), u [H, r], v [r, H] (fp32)."""
+    lib = load_library()
+    _dev(o, c, w_g, u, v, y)
+    B, S, H, dv = o.shape
+    dc = c.shape[-1]
+    r = u.shape[1]
+    c4 = c.reshape(B, S, 1, dc) if c.dim() == 3 else c
+    w_g = w_g.contiguous()
+    u = u.contiguous().float()
+    v = v.contiguous().float()
+    if y is None:
+        y = torch.empty((B, S, H, dv), dtype=o.dtype, device=o.device)
+    _check(lib.attn_output_epilogue(_dt(o), _ptr(o), _strides(o), _ptr(c4), _strides(c4), _ptr(w_g), _ptr(u), _ptr(v),
+                                    _ptr(y), _strides(y), B, S, H, dv, dc, r, _stream()))
+    return y
+
+
 def hca_attn_bwd_workspace_size(dtype: torch.dtype, batch: int, seqlen_q: int, q_pos0: int, n_blocks: int, h_q: int,
                                 h_kv: int, head_dim: int, block: int, window: int) -> int:
     dt = HCA_DTYPE_BF16 if dtype == torch.bfloat16 else HCA_DTYPE_F32
@@ -517,5 +539,5 @@ __all__ = [
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
-    "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd",
+    "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd", "attn_output_epilogue",
 ]

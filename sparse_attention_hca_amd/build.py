@@ -25,6 +25,7 @@ SOURCES = [
     "dsa_attn256.hip",
     "attn_bwd.hip",
     "attn_bwd512.hip",
+    "epilogue.hip",
     "hca_abi.cpp",
 ]
 

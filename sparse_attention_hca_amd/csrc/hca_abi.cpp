@@ -648,6 +648,39 @@ hca_status_t csa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq
                      h_q, h_kv, d_qk, d_v, topk, scale, stream);
 }
 
+hca_status_t attn_output_epilogue(hca_dtype_t dt, const void* o, hca_strides_t so, const void* c, hca_strides_t sc,
+                                  const void* w_g, const float* u, const float* v, void* y, hca_strides_t sy,
+                                  int batch, int seqlen, int h, int d_v, int d_c, int r, void* stream) {
+  if (dt != HCA_DTYPE_BF16) return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: bf16 only");
+  if (batch <= 0 || seqlen <= 0 || h <= 0 || d_v <= 0 || d_c <= 0 || r <= 0)
+    return fail(HCA_ERR_INVALID, "attn_output_epilogue: sizes must be positive");
+  if (!(h == 8 || h == 16 || h == 32 || h == 64) || r > 16 || d_c % 32 || (h * d_v) % 256 || d_v % 8 || d_v > 512)
+    return fail(HCA_ERR_UNSUPPORTED,
+                "attn_output_epilogue: needs h in {8, 16, 32, 64}, r <= 16, d_c a multiple of 32, "
+                "h * d_v a multiple of 256, d_v a multiple of 8 and <= 512");
+  if ((int64_t)batch * seqlen > kPosLimit) return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: too many tokens");
+  if (!w_g || !aligned16(w_g)) return fail(HCA_ERR_INVALID, "w_g is NULL or not 16-byte aligned");
+  if (!u || !v || ((uintptr_t)u & 3u) || ((uintptr_t)v & 3u)) return fail(HCA_ERR_INVALID, "u, v NULL or misaligned");
+  HCA_TRY(check_tensor("o", o, so, 2));
+  HCA_TRY(check_tensor("c", c, sc, 2));
+  HCA_TRY(check_tensor("y", y, sy, 2));
+  if (batch > 1 && (sc.batch != (int64_t)seqlen * sc.seq || sy.batch != (int64_t)seqlen * sy.seq))
+    return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: c and y must be token-contiguous across the batch "
+                                     "(batch stride = seqlen * seq stride)");
+  {
+    const Range ry = extent(y, sy, batch, seqlen, h, d_v, 2);
+    if (overlaps(ry, extent(o, so, batch, seqlen, h, d_v, 2)) || overlaps(ry, extent(c, sc, batch, seqlen, 1, d_c, 2)) ||
+        overlaps(ry, Range{(uintptr_t)w_g, (uintptr_t)((const uint16_t*)w_g + (size_t)h * d_v * d_c)}) ||
+        overlaps(ry, Range{(uintptr_t)u, (uintptr_t)(u + (size_t)h * r)}) ||
+        overlaps(ry, Range{(uintptr_t)v, (uintptr_t)(v + (size_t)h * r)}))
+      return fail(HCA_ERR_INVALID, "attn_output_epilogue: y overlaps an input");
+  }
+  hipError_t e = hca::launch_attn_output_epilogue(o, ls(so), c, sc.seq, w_g, u, v, y, ls(sy), batch, seqlen, h, d_v,
+                                                  d_c, r, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_output_epilogue launch");
+  return HCA_OK;
+}
+
 size_t dsa_index_topk_decode_workspace_size(int batch, int n_keys, int topk) {
   if (batch <= 0 || n_keys <= 0 || topk <= 0) return 0;
   return hca::dsa_topk_decode_workspace_bytes(batch, n_keys, topk);

@@ -108,4 +108,11 @@ hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, 
                                      LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,
                                      int seqlen, int n_kv, int h_q, int h_kv, int topk, float scale, hipStream_t st);
 
+// Attention-output epilogue: y = sigmoid(c W_g^T) * (o + (U V) o across heads).
+// Token m = b*seqlen + t of c at c + m*scs (d_c contiguous) and of y at
+// y + m*sy.s (so sy.b == seqlen*sy.s); W_g [h*d_v, d_c] contiguous.
+hipError_t launch_attn_output_epilogue(const void* o, LStrides so, const void* c, int64_t scs, const void* w_g,
+                                       const float* u, const float* v, void* y, LStrides sy, int batch, int seqlen,
+                                       int h, int d_v, int d_c, int r, hipStream_t st);
+
 }  // namespace hca

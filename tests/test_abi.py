@@ -21,7 +21,7 @@ FAKE = ctypes.c_void_p(1 << 20)   # aligned non-null pointer; never dereferenced
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:hca|dsa|csa)_[a-z0-9_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b((?:hca|dsa|csa|attn)_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_and_exports_agree():
@@ -312,3 +312,23 @@ def test_csa_rejects_bad_arguments():
     assert sp(idx=None) == hca.HCA_ERR_INVALID
     assert sp(n=0) == hca.HCA_ERR_INVALID
     assert sp(o=FAKE) == hca.HCA_ERR_INVALID             # o aliases q
+
+
+def test_epilogue_rejects_bad_arguments():
+    lib = _lib()
+    so = S(0, 16 * 512, 512)
+    sc = S(0, 2048, 2048)
+
+    def call(**kw):
+        return lib.attn_output_epilogue(kw.get("dt", 1), FAKE, so, ctypes.c_void_p(1 << 33), kw.get("sc", sc),
+                                        ctypes.c_void_p(1 << 34), ctypes.c_void_p(1 << 35), ctypes.c_void_p(1 << 36),
+                                        kw.get("y", ctypes.c_void_p(1 << 37)), so, kw.get("b", 1), 100,
+                                        kw.get("h", 16), kw.get("dv", 512), kw.get("dc", 2048), kw.get("r", 4), None)
+    assert call(dt=0) == hca.HCA_ERR_UNSUPPORTED
+    assert call(h=12) == hca.HCA_ERR_UNSUPPORTED
+    assert call(r=17) == hca.HCA_ERR_UNSUPPORTED
+    assert call(dc=2000) == hca.HCA_ERR_UNSUPPORTED
+    assert call(dv=1024) == hca.HCA_ERR_UNSUPPORTED
+    assert call(r=0) == hca.HCA_ERR_INVALID
+    assert call(y=FAKE) == hca.HCA_ERR_INVALID                     # y aliases o
+    assert call(b=2, sc=S(2048 * 101, 2048, 2048)) == hca.HCA_ERR_UNSUPPORTED   # c not token-contiguous
