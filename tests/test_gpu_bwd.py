@@ -134,18 +134,19 @@ def test_hca_training_step_bf16_chain(S, H, d, block, window):
         _check(name, g, r, BF16_TOL)
 
 
-@pytest.mark.parametrize("Sq,Skv,q_pos0,kv_pos0,Hq,Hkv,block,window,nb", [
-    (3000, 3000, 0, 0, 2, 1, 16, 40, 187),       # GQA; compressed tiles cut into several chunks of queries
-    (1100, 1100, 0, 0, 1, 1, 128, 128, 7),       # the c2 block / window at a small length, ragged tiles
-    (130, 190, 400, 340, 2, 2, 32, 61, 15),      # a chunk mid-sequence, raw K/V starting before it
-    (1, 40, 999, 960, 4, 1, 128, 40, 7),         # one decode query
-    (70, 70, 0, 0, 2, 2, 16, 200, 0),            # window covers everything: no compressed entry
+@pytest.mark.parametrize("B,Sq,Skv,q_pos0,kv_pos0,Hq,Hkv,block,window,nb", [
+    (1, 3000, 3000, 0, 0, 2, 1, 16, 40, 187),    # GQA; compressed tiles cut into several chunks of queries
+    (2, 1200, 1200, 0, 0, 2, 2, 32, 64, 36),     # two sequences: batch strides, per-sequence item ranges
+    (1, 1100, 1100, 0, 0, 1, 1, 128, 128, 7),    # the c2 block / window at a small length, ragged tiles
+    (1, 130, 190, 400, 340, 2, 2, 32, 61, 15),   # a chunk mid-sequence, raw K/V starting before it
+    (2, 1, 40, 999, 960, 4, 1, 128, 40, 7),      # one decode query per sequence
+    (1, 70, 70, 0, 0, 2, 2, 16, 200, 0),         # window covers everything: no compressed entry
 ])
-def test_hca_attn_bwd_bf16_512(Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window, nb):
+def test_hca_attn_bwd_bf16_512(B, Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window, nb):
     """The MFMA path (bf16, head_dim 512): the library's forward, then its
     backward, against the oracle's gradients on the same bf16 inputs."""
-    _say("hca bwd bf16 d512", Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window, nb)
-    B, d = 1, 512
+    _say("hca bwd bf16 d512", B, Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window, nb)
+    d = 512
     q = synth.make_normal((B, Sq, Hq, d), 81, bf16=True)
     k = synth.make_normal((B, Skv, Hkv, d), 82, bf16=True)
     v = synth.make_normal((B, Skv, Hkv, d), 83, bf16=True)
@@ -168,17 +169,17 @@ def test_hca_attn_bwd_bf16_512(Sq, Skv, q_pos0, kv_pos0, Hq, Hkv, block, window,
         _check(name, g, r, BF16_TOL)
 
 
-@pytest.mark.parametrize("dtype,S,H,d,block,window", [("bf16", 1100, 2, 512, 128, 128), ("bf16", 700, 1, 512, 64, 100),
-                                                      ("f32", 300, 2, 64, 32, 40)])
-def test_hca_attn_compress_bwd(dtype, S, H, d, block, window):
+@pytest.mark.parametrize("dtype,B,S,H,d,block,window", [("bf16", 1, 1100, 2, 512, 128, 128),
+                                                        ("bf16", 2, 700, 1, 512, 64, 100),
+                                                        ("f32", 2, 300, 2, 64, 32, 40)])
+def test_hca_attn_compress_bwd(dtype, B, S, H, d, block, window):
     """The fused layer backward (compressor share added inside the key-tile
     kernel on the MFMA path) against the oracle's chain, and against the
     two-call path (hca_attn_bwd then hca_compress_kv_bwd).  S is not a whole
     number of blocks, so the rows past the last block take the window part
     only."""
-    _say("attn+compress bwd", dtype, S, H, d, block, window)
+    _say("attn+compress bwd", dtype, B, S, H, d, block, window)
     bf = dtype == "bf16"
-    B = 1
     q = synth.make_normal((B, S, H, d), 91, bf16=bf)
     k = synth.make_normal((B, S, H, d), 92, bf16=bf)
     v = synth.make_normal((B, S, H, d), 93, bf16=bf)
