@@ -12,24 +12,36 @@
 //
 // The step is a gather of 2 x 512 bytes per selected position, so the design
 // keeps as many rows in flight as LDS holds:
-//   * The query's index row is copied to LDS once (positions past topk read
-//     as -1).  Out-of-range positions are detected there; they and the -1
-//     entries are fetched as row 0 (valid memory) and masked out.
+//   * The query's index row is copied to LDS once, with a 32-bit validity mask
+//     per 32-entry tile (a wave ballot); -1 entries and out-of-range positions
+//     are fetched as row 0 (valid memory) and masked, an out-of-range position
+//     also turns the row's output into NaN.  Trailing tiles with no valid entry
+//     are not visited, so rows shorter than topk cost what they hold.
 //   * Tiles of 32 gathered K and V rows move global -> LDS with 16-byte LDS
-//     DMA (each instruction fetches two rows, one per half-wave) through a ring
-//     of 4 stages: three tiles (96 KB) in flight while one is consumed.  The
-//     DMA is written as asm so the compiler does not wait for it before LDS
-//     reads; the explicit vmcnt wait and barrier of each tile order them.
+//     DMA through a ring of 4 stages: three tiles (96 KB) in flight while one
+//     is consumed.  DMA instruction i of wave w fetches entries 8w+i (lanes
+//     0-31) and 8w+4+i (lanes 32-63) into the adjacent LDS rows 8w+2i and
+//     8w+2i+1, so a lane's four row numbers are one 16-byte LDS read; the
+//     addresses are a scalar base plus a 32-bit row offset (64-bit addresses
+//     when a plane of K or V spans 2 GiB or more).  Keys sit in the tile in
+//     this row order: S, the masks and the PV contraction all use it.
 //   * Rows are stored with their 16-byte chunks XOR-swizzled (K chunk c of
 //     row r in slot c ^ (r mod 16), V chunk c in slot c ^ 2(r mod 8); the DMA
 //     lanes fetch the matching chunks), so the 16-byte K operand reads and
 //     the gfx950 transposing V reads (ds_read_b64_tr_b16, which hands each
 //     lane four consecutive keys of one dim: the V^T operand) hit distinct
 //     bank groups.
-//   * The S^T accumulators of a lane (one head, keys 4g .. 4g+3 and
+//   * The S^T accumulators of a lane (one head, rows 4g .. 4g+3 and
 //     16+4g .. 16+4g+3) are the P^T operand of the PV product once converted
-//     to bf16; the V^T reads fetch keys in that order.
-//   * Softmax is online in fp32 with a lazy rescale.
+//     to bf16; the V^T reads fetch rows in that order.
+//   * Softmax in fp32 (log2 domain) against a fixed reference per head: the
+//     maximum of the first tile holding a valid key.  O^T is never rescaled,
+//     so it stays in AGPRs (the products are inline asm with explicit
+//     accumulator classes and wait states).  If a later logit exceeds the
+//     reference by more than 2^kGuard the whole row runs again with the exact
+//     maximum as reference.  The row sum of P comes from one more MFMA with an
+//     all-ones A operand, so it is the sum of the same bf16 probabilities
+//     that enter O.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -45,7 +57,8 @@ constexpr int KSTB = TK * ROWB;        // K part of a stage
 constexpr int STAGEB = 2 * KSTB;       // K rows then V rows
 constexpr int NRING = 4;               // ring stages; NRING - 1 tiles in flight
 constexpr int MAX_TOPK = 4096;
-constexpr int DMA_PER_TILE = 8;        // DMA instructions per wave per tile (4 K + 4 V)
+constexpr int MAX_TILES = MAX_TOPK / TK;
+constexpr float kGuard = 64.f;         // log2 headroom of the fixed softmax reference
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -57,20 +70,50 @@ struct SparseParams {
   uint16_t* o; LStrides so;
   float* lse;
   int seqlen, n_kv, h_q, h_kv, topk, n_hb;  // seqlen queries; positions < n_kv
+  uint32_t k_row_bytes, v_row_bytes;        // position strides of K and V in bytes
   float c;
 };
 
-// 16-byte LDS DMA of one wave: lane l copies 16 bytes from g (per lane) to LDS
-// byte address lds + 16 l (lds travels in M0).
+// 16-byte LDS DMA of one wave (lane l copies 16 bytes to LDS byte address
+// lds + 16 l; lds travels in M0): from a per-lane 64-bit address, or from a
+// scalar base plus a per-lane 32-bit offset.  Written as asm so the compiler
+// does not wait for it before LDS reads; the explicit vmcnt wait and barrier
+// of each tile order them.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
+__device__ __forceinline__ void dma16_so(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
 
+// v_mfma_f32_16x16x32_bf16 as inline asm: S^T accumulates in VGPRs (the
+// softmax reads it), O^T and the row sum in AGPRs.  The compiler does not see
+// these as MFMAs, so the required wait states are explicit: after the last
+// S^T step (VALU reads it), before the first PV step of a tile (P^T was just
+// written by VALU) and before the AGPRs are read back.
+__device__ __forceinline__ void mfma_s_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void zero_o(f32x4& acc, const bf16x8& z) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=&a"(acc) : "v"(z));
+}
+
+template <bool POS, bool WIDE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void sparse_attn256_kernel(SparseParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NRING * STAGEB];
   __shared__ __attribute__((aligned(16))) int sidx[MAX_TOPK];
-  __shared__ int bad_sh;
+  __shared__ uint32_t tvalid[MAX_TILES];
+  __shared__ int bad_sh, last_sh, redo_sh;
 
   const int t = blockIdx.x;
   const int hb = blockIdx.y % p.n_hb;
@@ -81,20 +124,32 @@ void sparse_attn256_kernel(SparseParams p) {
   const int col = lane & 15, grp = lane >> 4;
   const int group = p.h_q / p.h_kv;
   const int hq = g * group + hb * HPB + w * HPW + col;
-  const int ntiles = (p.topk + TK - 1) / TK;
+  const int ntiles_all = (p.topk + TK - 1) / TK;
 
-  // ---- index row -> LDS (-1 past topk); out-of-range positions flag the row
+  // ---- index row -> LDS (fetch row, 0 where invalid), per-tile validity
+  // masks, the last tile holding a valid entry, out-of-range flag
+  if (tid == 0) { bad_sh = 0; last_sh = -1; redo_sh = 0; }
+  __syncthreads();
   {
     const int32_t* irow = p.idx + ((int64_t)b * p.seqlen + t) * p.topk;
-    int bad = 0;
-    for (int j = tid; j < ntiles * TK; j += 256) {
-      int u = j < p.topk ? irow[j] : -1;
+    int bad = 0, last = -1;
+    for (int j0 = 0; j0 < ntiles_all * TK; j0 += 256) {
+      const int j = j0 + tid;
+      const int u = j < p.topk ? irow[j] : -1;
       bad |= (u < -1 || u >= p.n_kv);
-      sidx[j] = (u >= 0 && u < p.n_kv) ? u : -1;
+      const bool ok = u >= 0 && u < p.n_kv;
+      if (j < ntiles_all * TK) sidx[j] = ok ? u : 0;
+      const uint64_t bal = __ballot(ok);
+      const int tile = (j0 + 64 * w) / TK;
+      if (lane == 0) {
+        if (tile < ntiles_all) tvalid[tile] = (uint32_t)bal;
+        if (tile + 1 < ntiles_all) tvalid[tile + 1] = (uint32_t)(bal >> 32);
+      }
+      if ((uint32_t)(bal >> 32) != 0u) last = tile + 1;
+      else if ((uint32_t)bal != 0u) last = tile;
     }
-    if (tid == 0) bad_sh = 0;
-    __syncthreads();
     if (bad) atomicOr(&bad_sh, 1);
+    if (lane == 0 && last >= 0) atomicMax(&last_sh, last);
   }
 
   // ---- Q^T fragments (B operand): head `col`, dims 32ks + 8grp .. +8
@@ -106,28 +161,45 @@ void sparse_attn256_kernel(SparseParams p) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
-  __syncthreads();  // sidx and bad_sh complete; Q settled before the DMA ring
+  __syncthreads();  // sidx, tvalid, flags complete; Q settled before the DMA ring
+  const int ntiles = __builtin_amdgcn_readfirstlane(last_sh + 1);
 
   const uint16_t* kb = p.k + b * p.sk.b + (int64_t)g * p.sk.h;
   const uint16_t* vb = p.v + b * p.sv.b + (int64_t)g * p.sv.h;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
 
-  // ---- DMA of tile tt into stage st: wave w fetches rows 8w .. 8w+7 of K and V;
-  // instruction i covers rows 8w+2i (lanes 0-31) and 8w+2i+1 (lanes 32-63).
+  // ---- DMA of tile tt into stage st.  Instruction i of wave w: lanes 0-31
+  // fetch entry 8w+i into LDS row 8w+2i, lanes 32-63 entry 8w+4+i into row
+  // 8w+2i+1; lane hl of a half fetches the chunk that lands in slot hl.
   const int hrow = lane >> 5, hl = lane & 31;
+  uint32_t kch[4], vch[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * w + 2 * i + hrow;
+    kch[i] = 16 * (hl ^ (r & 15));
+    vch[i] = 16 * (hl ^ (2 * (r & 7)));
+  }
   auto issue = [&](int tt, int st) __attribute__((always_inline)) {
     const uint32_t kl = lds0 + st * STAGEB, vl = kl + KSTB;
+    const int4 u4 = *reinterpret_cast<const int4*>(sidx + tt * TK + 8 * w + 4 * hrow);
+    const int uu[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 8 * w + 2 * i + hrow;
-      const int u = max(sidx[tt * TK + r], 0);
-      dma16(kb + (int64_t)u * p.sk.s + 8 * (hl ^ (r & 15)), kl + (8 * w + 2 * i) * ROWB);
-      dma16(vb + (int64_t)u * p.sv.s + 8 * (hl ^ (2 * (r & 7))), vl + (8 * w + 2 * i) * ROWB);
+      const uint32_t ldsr = (8 * w + 2 * i) * ROWB;
+      if constexpr (WIDE) {
+        dma16(reinterpret_cast<const unsigned char*>(kb) + (uint64_t)(uint32_t)uu[i] * p.k_row_bytes + kch[i],
+              kl + ldsr);
+        dma16(reinterpret_cast<const unsigned char*>(vb) + (uint64_t)(uint32_t)uu[i] * p.v_row_bytes + vch[i],
+              vl + ldsr);
+      } else {
+        dma16_so(kb, __umul24(uu[i], p.k_row_bytes) + kch[i], kl + ldsr);
+        dma16_so(vb, __umul24(uu[i], p.v_row_bytes) + vch[i], vl + ldsr);
+      }
     }
   };
 
   // Per-lane LDS read offsets within a stage.
-  //   K (A operand, key half kt, step ks): key 16kt + col, chunk 4ks + grp in slot
+  //   K (A operand, key half kt, step ks): row 16kt + col, chunk 4ks + grp in slot
   //     (4ks + grp) ^ col: k_off[ks % 4] + 256 (ks / 4) + 16 kt ROWB.
   //   V^T (A operand of dim tile dt, read e): row 16e + 4grp + col/4, dims
   //     16dt + 4(col % 4), chunk 2dt + (col % 4)/2 in slot chunk ^ 2(row mod 8):
@@ -142,90 +214,157 @@ void sparse_attn256_kernel(SparseParams p) {
     for (int i = 0; i < 8; ++i)
       v_off[i] = KSTB + row * ROWB + 32 * (i ^ s) + 16 * ((col & 3) >> 1) + 8 * (col & 1);
   }
-
-  f32x4 o[16];
+  // Entry number (bit of the tile's validity mask) of the S^T rows this lane
+  // holds: row 16kt + 4grp + r sits in LDS row order, see the DMA above.
+  int ebit[8];
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_used = -INFINITY, l_run = 0.f;
-  const float c = p.c;
-
-  auto compute = [&](int tt, const unsigned char* sb) __attribute__((always_inline)) {
-    // S^T = K Q^T for the two 16-key halves
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(sb + k_off[ks & 3] + 256 * (ks >> 2) + 16 * kt * ROWB));
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[kt], 0, 0, 0);
-      }
-    // keys of this lane: 16kt + 4grp + r; masked when the entry is -1
-    const int4 u0 = *reinterpret_cast<const int4*>(sidx + tt * TK + 4 * grp);
-    const int4 u1 = *reinterpret_cast<const int4*>(sidx + tt * TK + 16 + 4 * grp);
-    float sv[8];
-    sv[0] = u0.x >= 0 ? s[0][0] * c : -INFINITY;
-    sv[1] = u0.y >= 0 ? s[0][1] * c : -INFINITY;
-    sv[2] = u0.z >= 0 ? s[0][2] * c : -INFINITY;
-    sv[3] = u0.w >= 0 ? s[0][3] * c : -INFINITY;
-    sv[4] = u1.x >= 0 ? s[1][0] * c : -INFINITY;
-    sv[5] = u1.y >= 0 ? s[1][1] * c : -INFINITY;
-    sv[6] = u1.z >= 0 ? s[1][2] * c : -INFINITY;
-    sv[7] = u1.w >= 0 ? s[1][3] * c : -INFINITY;
-    float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool need = mt > m_used + 8.f;
-    if (__any(need)) {
-      const float new_m = need ? mt : m_used;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_used - new_m) : 1.f;
-      m_used = new_m;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+    for (int r = 0; r < 4; ++r) {
+      const int rho = 16 * kt + 4 * grp + r;
+      ebit[4 * kt + r] = 8 * (rho >> 3) + 4 * (rho & 1) + ((rho & 7) >> 1);
     }
-    // masked logits are -inf: exp2 gives 0 (also while m_used is still -inf)
-    const float msafe = m_used == -INFINITY ? 0.f : m_used;
-    float ps[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) ps[r] = __builtin_amdgcn_exp2f(sv[r] - msafe);
-    l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-    u32x4 pk;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(ps[2 * e], ps[2 * e + 1]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
-    // O^T += V^T P^T : 16 dim tiles, k = the 32 keys of the tile
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
+
+  f32x4 o[16], lacc;
+  const float c = p.c;
+  const float NEG = POS ? -INFINITY : INFINITY;  // raw score that maps to a -inf logit
+  float m_ref = -INFINITY;                       // reference (scaled, log2 domain) of this lane's head
+  float m_run = NEG;                             // running max (POS) / min of this lane's raw scores
+  bool have_ref = false;                         // same for every lane of the workgroup
+  const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  const bf16x8 ones8 = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  auto ext = [](float a, float x) __attribute__((always_inline)) { return POS ? fmaxf(a, x) : fminf(a, x); };
+  // extreme of three raw scores (v_max3 / v_min3; written as asm so that no
+  // canonicalising moves are added around the MFMA results)
+  auto ext3 = [](float a, float x, float y) __attribute__((always_inline)) {
+    float r;
+    if constexpr (POS) asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(x), "v"(y));
+    else asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(x), "v"(y));
+    return r;
+  };
+  // first tile with a valid key: O^T is still zero, so the reference (the
+  // head's maximum logit over this tile) may be set freely
+  auto set_ref = [&](const float* sv) __attribute__((always_inline)) {
+    float mt = ext(ext3(sv[0], sv[1], sv[2]), ext3(sv[3], sv[4], ext(sv[5], ext(sv[6], sv[7]))));
+    mt = ext(mt, __shfl_xor(mt, 16));
+    mt = ext(mt, __shfl_xor(mt, 32));
+    m_ref = mt * c;
+    have_ref = true;
+  };
+
+  auto compute = [&](uint32_t vmask, const unsigned char* sb) __attribute__((always_inline)) {
+    // S^T = K Q^T for the two 16-key halves; MFMA i is step i/2 of half i%2,
+    // its K operand is read four MFMAs ahead (the scheduling barriers keep
+    // that order)
+    auto ldk = [&](int i) __attribute__((always_inline)) {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(sb + k_off[(i >> 1) & 3] + 256 * (i >> 3) + 16 * (i & 1) * ROWB));
+    };
+    auto ldv = [&](int dt) __attribute__((always_inline)) {
       const unsigned char* vp = sb + v_off[dt & 7] + 256 * (dt >> 3);
       const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
       const s16x4 hi4 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 16 * ROWB));
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[dt], 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    f32x4 s[2];
+    bf16x8 kq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kq[i] = ldk(i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8 ka = kq[i & 3];
+      if (i + 4 < 16) kq[i & 3] = ldk(i + 4);
+      if (i < 2) mfma_s_first(s[i & 1], ka, qf[i >> 1]);
+      else mfma_s(s[i & 1], ka, qf[i >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T operands do not depend on P: their reads overlap the softmax
+    bf16x8 vq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vq[i] = ldv(i);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]));
+    float sv[8] = {s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]};
+    float ps[8];
+    if (vmask == 0xffffffffu) {
+      m_run = ext3(m_run, ext3(sv[0], sv[1], sv[2]), ext3(sv[3], sv[4], ext(sv[5], ext(sv[6], sv[7]))));
+      if (!have_ref) set_ref(sv);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) ps[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -m_ref));
+    } else {
+      bool ok[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        ok[r] = (vmask >> ebit[r]) & 1u;
+        sv[r] = ok[r] ? sv[r] : NEG;
+      }
+      m_run = ext(m_run, ext(ext3(sv[0], sv[1], sv[2]), ext3(sv[3], sv[4], ext(sv[5], ext(sv[6], sv[7])))));
+      if (!have_ref) set_ref(sv);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) ps[r] = ok[r] ? __builtin_amdgcn_exp2f(fmaf(sv[r], c, -m_ref)) : 0.f;
+    }
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(ps[2 * e], ps[2 * e + 1]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T : 16 dim tiles, k = the 32 keys of the tile; then the row sum
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const bf16x8 va = vq[dt & 3];
+      if (dt + 4 < 16) vq[dt & 3] = ldv(dt + 4);
+      if (dt == 0) mfma_o_first(o[dt], va, pf);
+      else mfma_o(o[dt], va, pf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_o_first(lacc, ones8, pf);  // the ones operand may have just been rematerialised by VALU
   };
 
   // Ring: tiles 0 .. NRING-2 are issued up front; the trip for tile tt waits
   // for its rows (later tiles stay in flight), a barrier makes every wave's
   // rows visible and frees the stage tile tt-1 used, tile tt+NRING-1 is issued
-  // into it, then tile tt is computed.
-  for (int i = 0; i < NRING - 1; ++i)
-    if (i < ntiles) issue(i, i);
-  int st = 0;
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int after = min(NRING - 2, ntiles - 1 - tt);  // tiles issued after tt
-    if (after >= 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-    else if (after == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (tt + NRING - 1 < ntiles) issue(tt + NRING - 1, st == 0 ? NRING - 1 : st - 1);
-    compute(tt, ring + st * STAGEB);
-    st = st == NRING - 1 ? 0 : st + 1;
+  // into it, then tile tt is computed.  The second pass (rare, see m_ref) is
+  // decided for the whole workgroup, as the loop holds barriers.
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) zero_o(o[dt], zero8);
+    zero_o(lacc, zero8);
+    for (int i = 0; i < NRING - 1; ++i)
+      if (i < ntiles) issue(i, i);
+    int st = 0;
+    uint32_t vm = ntiles > 0 ? tvalid[0] : 0u;  // validity word of the next tile, read ahead
+    for (int tt = 0; tt < ntiles; ++tt) {
+      const uint32_t vmask = __builtin_amdgcn_readfirstlane(vm);
+      vm = tvalid[min(tt + 1, ntiles - 1)];
+      const int after = min(NRING - 2, ntiles - 1 - tt);  // tiles issued after tt
+      if (after >= 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (tt + NRING - 1 < ntiles) issue(tt + NRING - 1, st == 0 ? NRING - 1 : st - 1);
+      if (vmask != 0u) compute(vmask, ring + st * STAGEB);
+      st = st == NRING - 1 ? 0 : st + 1;
+    }
+    if (pass == 1) break;
+    float mh = ext(m_run, __shfl_xor(m_run, 16));
+    mh = ext(mh, __shfl_xor(mh, 32));
+    const float top = mh * c;  // exact maximum logit of this lane's head
+    const bool risk = have_ref && top > m_ref + kGuard;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (__any(risk) && lane == 0) redo_sh = 1;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (redo_sh == 0) break;
+    m_ref = top;  // every probability of the second pass is at most 1
   }
 
+  // ---- epilogue (wait states: the AGPRs are read right after the last MFMA)
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) asm volatile("" : "+a"(o[dt]));
+  asm volatile("" : "+a"(lacc));
   const bool poisoned = bad_sh != 0;
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = lacc[0];
   const float inv = poisoned ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
   uint16_t* op = p.o + b * p.so.b + (int64_t)t * p.so.s + (int64_t)hq * p.so.h + 4 * grp;
 #pragma unroll
@@ -237,7 +376,7 @@ void sparse_attn256_kernel(SparseParams p) {
   }
   if (p.lse && grp == 0)
     p.lse[((int64_t)b * p.h_q + hq) * p.seqlen + t] =
-        poisoned ? __builtin_nanf("") : m_used * kLn2 + __logf(l_tot);
+        poisoned ? __builtin_nanf("") : (have_ref ? m_ref * kLn2 + __logf(l_tot) : -INFINITY);
 }
 
 }  // namespace
@@ -254,11 +393,25 @@ hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, 
   p.lse = lse;
   p.seqlen = seqlen; p.n_kv = n_kv; p.h_q = h_q; p.h_kv = h_kv; p.topk = topk;
   const int group = h_q / h_kv;
-  if (group % HPB != 0 || topk > MAX_TOPK) return hipErrorInvalidValue;
+  if (group % HPB != 0 || topk > MAX_TOPK || sk.s < 0 || sv.s < 0) return hipErrorInvalidValue;
   p.n_hb = group / HPB;
   p.c = scale * kLog2e;
+  // 32-bit row offsets (with __umul24) while every gathered byte of a K or V
+  // plane lies below 2^31 from its base
+  const uint64_t kr = 2ull * (uint64_t)sk.s, vr = 2ull * (uint64_t)sv.s;
+  const uint64_t span = (uint64_t)(n_kv - 1) * (kr > vr ? kr : vr) + ROWB;
+  const bool wide = n_kv >= (1 << 24) || kr >= (1ull << 24) || vr >= (1ull << 24) || span >= (1ull << 31);
+  p.k_row_bytes = (uint32_t)kr;
+  p.v_row_bytes = (uint32_t)vr;
+  const bool pos = !(p.c < 0.f);
   dim3 grid(seqlen, h_kv * p.n_hb, batch);
-  hipLaunchKernelGGL(sparse_attn256_kernel, grid, dim3(256), 0, st, p);
+  if (wide) {
+    if (pos) hipLaunchKernelGGL((sparse_attn256_kernel<true, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((sparse_attn256_kernel<false, true>), grid, dim3(256), 0, st, p);
+  } else {
+    if (pos) hipLaunchKernelGGL((sparse_attn256_kernel<true, false>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((sparse_attn256_kernel<false, false>), grid, dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -156,6 +156,108 @@ def test_sparse_attention_bad_index_poisons_row():
     assert not np.isnan(on[0, others]).any()
 
 
+def _oracle_rows(inp, idx, scale, rows):
+    return oracle.sparse_attention(f64(inp["q"][:, rows], True), f64(inp["k"], True), f64(inp["v"], True),
+                                   idx[:, rows], scale, rows=list(range(len(rows))))
+
+
+def test_sparse_attention_holes_and_empty_tiles():
+    """-1 entries anywhere in a row: a hole in every row, whole 32-entry tiles of
+    -1 between valid ones, rows whose valid entries stop early, and a row with
+    none (o = 0, lse = -inf)."""
+    S, topk = 300, 200
+    cfg = synth.small_dsa(seqlen=S, topk=topk)
+    _say("holes", cfg)
+    inp = synth.make_dsa(cfg)
+    rng = np.random.default_rng(11)
+    idx = np.full((1, S, topk), -1, dtype=np.int32)
+    for t in range(S):
+        n = min(S, topk)
+        idx[0, t, :n] = rng.permutation(S)[:n]
+    idx[0, :, 37] = -1
+    idx[0, 250:, 64:128] = -1
+    idx[0, 200:220, 40:] = -1
+    idx[0, 123] = -1
+    o, lse = _sparse_case(cfg, inp, idx)
+    on, ln = host(o), host(lse)
+    assert (on[0, 123] == 0).all() and np.isneginf(ln[0, :, 123]).all()
+    keep = [t for t in range(S) if t != 123]
+    ro, rlse = _oracle_rows(inp, idx, cfg.scale, keep)
+    err = rel_err(on[:, keep], ro)
+    _say(f"  rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(ln[:, :, keep] - rlse)) < LSE_TOL
+
+
+def test_sparse_attention_late_dominant_keys():
+    """Two keys met in the second tile (of four) score about 2^135 above every
+    logit of the first tile, so the softmax reference of those rows is replaced
+    (the row runs again; without it the probabilities would overflow fp32); the
+    two differ slightly, so the output mixes their values."""
+    S, topk = 160, 128
+    cfg = synth.small_dsa(seqlen=S, topk=topk)
+    inp = synth.make_dsa(cfg)
+    q = synth.bf16_bits_to_f32(inp["q"]).copy()
+    k = synth.bf16_bits_to_f32(inp["k"]).copy()
+    rows = [3, 77, 140]
+    q[0, rows] = 1.0
+    k[0, 150] = 6.0
+    k[0, 151] = 6.0
+    k[0, 151, 0, :8] = 5.875
+    inp = dict(inp, q=synth.bf16_round_bits(q), k=synth.bf16_round_bits(k))
+    rng = np.random.default_rng(12)
+    idx = np.stack([rng.permutation(150)[:topk] for _ in range(S)])[None].astype(np.int32)
+    idx[0, rows, 40] = 150
+    idx[0, rows, 60] = 151
+    o, lse = _sparse_case(cfg, inp, idx)
+    ro, rlse = _oracle_rows(inp, idx, cfg.scale, list(range(S)))
+    on = host(o)
+    assert not np.isnan(on).any()
+    err = rel_err(on, ro)
+    _say(f"  rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert rel_err(on[:, rows], ro[:, rows]) < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
+def test_sparse_attention_negative_scale():
+    cfg = synth.small_dsa(seqlen=200, topk=96)
+    inp = synth.make_dsa(cfg)
+    idx = synth.make_index_lists(1, 200, 96, seed=13)
+    o, lse = hca.dsa_sparse_attn_fwd(dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]),
+                                     torch.from_numpy(idx).to("cuda:0"), scale=-cfg.scale)
+    torch.cuda.synchronize()
+    valid = [t for t in range(200) if (idx[0, t] >= 0).any()]
+    ro, rlse = _oracle_rows(inp, idx, -cfg.scale, valid)
+    assert rel_err(host(o)[:, valid], ro) < BF16_TOL
+    assert np.max(np.abs(host(lse)[:, :, valid] - rlse)) < LSE_TOL
+
+
+def test_sparse_attention_wide_position_stride():
+    """K and V rows 16 MiB apart (position stride 2^23 elements): the gather
+    takes 64-bit addresses."""
+    S, topk = 24, 40
+    cfg = synth.small_dsa(seqlen=S, topk=topk)
+    inp = synth.make_dsa(cfg)
+    st = 1 << 23
+    views = []
+    for name in ("k", "v"):
+        buf = torch.zeros(S * st, dtype=torch.bfloat16, device="cuda:0")
+        t = buf.as_strided((1, S, 1, 256), (S * st, st, 256, 1))
+        t.copy_(dev_bf16(inp[name]))
+        views.append(t)
+    rng = np.random.default_rng(14)
+    idx = np.full((1, S, topk), -1, dtype=np.int32)
+    for t in range(S):
+        idx[0, t, :S] = rng.permutation(S)
+    o, lse = hca.dsa_sparse_attn_fwd(dev_bf16(inp["q"]), views[0], views[1], torch.from_numpy(idx).to("cuda:0"),
+                                     scale=cfg.scale)
+    torch.cuda.synchronize()
+    ro, rlse = _oracle_rows(inp, idx, cfg.scale, list(range(S)))
+    assert rel_err(host(o), ro) < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
 @pytest.mark.timeout(900)
 def test_full_size_dsa_sampled():
     cfg = synth.CONFIGS["c5"]
