@@ -16,7 +16,8 @@
 //     per 32-entry tile (a wave ballot); -1 entries and out-of-range positions
 //     are fetched as row 0 (valid memory) and masked, an out-of-range position
 //     also turns the row's output into NaN.  Trailing tiles with no valid entry
-//     are not visited, so rows shorter than topk cost what they hold.
+//     are not visited, so rows shorter than topk cost what they hold; an
+//     interior tile with none takes the masked path (all probabilities 0).
 //   * Tiles of 32 gathered K and V rows move global -> LDS with 16-byte LDS
 //     DMA through a ring of 4 stages: three tiles (96 KB) in flight while one
 //     is consumed.  DMA instruction i of wave w fetches entries 8w+i (lanes
@@ -179,23 +180,26 @@ void sparse_attn256_kernel(SparseParams p) {
     kch[i] = 16 * (hl ^ (r & 15));
     vch[i] = 16 * (hl ^ (2 * (r & 7)));
   }
-  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
-    const uint32_t kl = lds0 + st * STAGEB, vl = kl + KSTB;
-    const int4 u4 = *reinterpret_cast<const int4*>(sidx + tt * TK + 8 * w + 4 * hrow);
-    const int uu[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ldsr = (8 * w + 2 * i) * ROWB;
-      if constexpr (WIDE) {
-        dma16(reinterpret_cast<const unsigned char*>(kb) + (uint64_t)(uint32_t)uu[i] * p.k_row_bytes + kch[i],
-              kl + ldsr);
-        dma16(reinterpret_cast<const unsigned char*>(vb) + (uint64_t)(uint32_t)uu[i] * p.v_row_bytes + vch[i],
-              vl + ldsr);
-      } else {
-        dma16_so(kb, __umul24(uu[i], p.k_row_bytes) + kch[i], kl + ldsr);
-        dma16_so(vb, __umul24(uu[i], p.v_row_bytes) + vch[i], vl + ldsr);
-      }
+  auto rows_of = [&](int tt) __attribute__((always_inline)) {
+    return *reinterpret_cast<const int4*>(sidx + tt * TK + 8 * w + 4 * hrow);
+  };
+  // instruction j of a tile: K (j even) or V (j odd) rows of pair j/2
+  auto dma_one = [&](const int4& u4, int st, int j) __attribute__((always_inline)) {
+    const int i = j >> 1;
+    const uint32_t u = (uint32_t)(i == 0 ? u4.x : i == 1 ? u4.y : i == 2 ? u4.z : u4.w);
+    const uint32_t lds = lds0 + st * STAGEB + (j & 1) * KSTB + (8 * w + 2 * i) * ROWB;
+    if constexpr (WIDE) {
+      if (j & 1) dma16(reinterpret_cast<const unsigned char*>(vb) + (uint64_t)u * p.v_row_bytes + vch[i], lds);
+      else dma16(reinterpret_cast<const unsigned char*>(kb) + (uint64_t)u * p.k_row_bytes + kch[i], lds);
+    } else {
+      if (j & 1) dma16_so(vb, __umul24(u, p.v_row_bytes) + vch[i], lds);
+      else dma16_so(kb, __umul24(u, p.k_row_bytes) + kch[i], lds);
     }
+  };
+  auto issue = [&](int tt, int st) __attribute__((always_inline)) {
+    const int4 u4 = rows_of(tt);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma_one(u4, st, j);
   };
 
   // Per-lane LDS read offsets within a stage.
@@ -253,7 +257,10 @@ void sparse_attn256_kernel(SparseParams p) {
     have_ref = true;
   };
 
-  auto compute = [&](uint32_t vmask, const unsigned char* sb) __attribute__((always_inline)) {
+  // One tile.  When `dma` is set, the 8 DMA instructions of tile tt+NRING-1
+  // go out between the first S^T steps, so their issue overlaps the products.
+  auto compute = [&](uint32_t vmask, const unsigned char* sb, bool dma, const int4& u4, int dst)
+      __attribute__((always_inline)) {
     // S^T = K Q^T for the two 16-key halves; MFMA i is step i/2 of half i%2,
     // its K operand is read four MFMAs ahead (the scheduling barriers keep
     // that order)
@@ -278,6 +285,7 @@ void sparse_attn256_kernel(SparseParams p) {
       if (i + 4 < 16) kq[i & 3] = ldk(i + 4);
       if (i < 2) mfma_s_first(s[i & 1], ka, qf[i >> 1]);
       else mfma_s(s[i & 1], ka, qf[i >> 1]);
+      if (i < 8 && dma) dma_one(u4, dst, i);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the first V^T operands do not depend on P: their reads overlap the softmax
@@ -301,7 +309,7 @@ void sparse_attn256_kernel(SparseParams p) {
         sv[r] = ok[r] ? sv[r] : NEG;
       }
       m_run = ext(m_run, ext(ext3(sv[0], sv[1], sv[2]), ext3(sv[3], sv[4], ext(sv[5], ext(sv[6], sv[7])))));
-      if (!have_ref) set_ref(sv);
+      if (!have_ref && vmask != 0u) set_ref(sv);
 #pragma unroll
       for (int r = 0; r < 8; ++r) ps[r] = ok[r] ? __builtin_amdgcn_exp2f(fmaf(sv[r], c, -m_ref)) : 0.f;
     }
@@ -324,8 +332,10 @@ void sparse_attn256_kernel(SparseParams p) {
 
   // Ring: tiles 0 .. NRING-2 are issued up front; the trip for tile tt waits
   // for its rows (later tiles stay in flight), a barrier makes every wave's
-  // rows visible and frees the stage tile tt-1 used, tile tt+NRING-1 is issued
-  // into it, then tile tt is computed.  The second pass (rare, see m_ref) is
+  // rows visible and frees the stage tile tt-1 used, then tile tt is computed
+  // while tile tt+NRING-1 is issued into that stage.  Every tile up to the
+  // last valid one is computed (a tile with no valid entry contributes
+  // nothing).  The second pass (rare, see m_ref) is
   // decided for the whole workgroup, as the loop holds barriers.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -338,12 +348,12 @@ void sparse_attn256_kernel(SparseParams p) {
     for (int tt = 0; tt < ntiles; ++tt) {
       const uint32_t vmask = __builtin_amdgcn_readfirstlane(vm);
       vm = tvalid[min(tt + 1, ntiles - 1)];
+      const int4 u4 = rows_of(min(tt + NRING - 1, ntiles - 1));  // rows of the tile issued in this trip
       const int after = min(NRING - 2, ntiles - 1 - tt);  // tiles issued after tt
       if (after >= 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
       else if (after == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      if (tt + NRING - 1 < ntiles) issue(tt + NRING - 1, st == 0 ? NRING - 1 : st - 1);
-      if (vmask != 0u) compute(vmask, ring + st * STAGEB);
+      compute(vmask, ring + st * STAGEB, tt + NRING - 1 < ntiles, u4, st == 0 ? NRING - 1 : st - 1);
       st = st == NRING - 1 ? 0 : st + 1;
     }
     if (pass == 1) break;
