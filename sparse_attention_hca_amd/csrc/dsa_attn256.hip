@@ -5,10 +5,13 @@
 //
 // One workgroup (4 waves) per (query position, group of 64 query heads that
 // share one KV head); every head of the group attends over the same gathered
-// rows, so the heads are the MFMA columns: each wave owns 16 heads and
-// computes S^T = K Q^T (32 keys x 16 heads, v_mfma_f32_16x16x32_bf16) and
-// O^T += V^T P^T (256 dims x 16 heads, v_mfma_f32_16x16x32_bf16, the 32 keys
-// of a tile as the contraction).
+// rows, so the heads are the MFMA columns.  Wave w owns heads 16w .. 16w+15
+// for S^T = K Q^T (32 keys x 16 heads, v_mfma_f32_16x16x32_bf16) and their
+// softmax, publishes its P^T (bf16, 1 KB per tile) in LDS, and then computes
+// O^T += V^T P^T for dims 64w .. 64w+63 of all 64 heads (the 32 keys of a
+// tile as the contraction).  Each V^T byte is thus read from LDS by one wave
+// instead of four: the loop is bound by LDS instruction issue, and the
+// transposing V reads were most of it.
 //
 // The step is a gather of 2 x 512 bytes per selected position, so the design
 // keeps as many rows in flight as LDS holds:
@@ -56,9 +59,7 @@ constexpr int HPB = 64;                // heads per workgroup
 constexpr int ROWB = 2 * D;            // bytes per K or V row
 constexpr int KSTB = TK * ROWB;        // K part of a stage
 constexpr int STAGEB = 2 * KSTB;       // K rows then V rows
-constexpr int NRING = 4;               // ring stages; NRING - 1 tiles in flight
 constexpr int MAX_TOPK = 4096;
-constexpr int MAX_TILES = MAX_TOPK / TK;
 constexpr float kGuard = 64.f;         // log2 headroom of the fixed softmax reference
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -108,12 +109,19 @@ __device__ __forceinline__ void zero_o(f32x4& acc, const bf16x8& z) {
   asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=&a"(acc) : "v"(z));
 }
 
-template <bool POS, bool WIDE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+// NRING ring stages (NRING - 1 tiles in flight) and rows of up to MAXK
+// entries: <2, 2048> keeps a workgroup under 80 KB of LDS so that two run on
+// a CU (two waves per SIMD, whose serial S -> softmax -> PV chains and
+// per-query start-up interleave); <4, 4096> is one workgroup per CU.
+template <bool POS, bool WIDE, int NRING, int MAXK>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NRING == 2 ? 2 : 1)))
 void sparse_attn256_kernel(SparseParams p) {
+  constexpr int MAX_TILES = MAXK / TK;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NRING * STAGEB];
-  __shared__ __attribute__((aligned(16))) int sidx[MAX_TOPK];
+  __shared__ __attribute__((aligned(16))) int sidx[MAXK];
   __shared__ uint32_t tvalid[MAX_TILES];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[HPB * TK * 2];  // P^T of the 4 head blocks
+  __shared__ float lsh[HPB];                                                  // row sums per head
   __shared__ int bad_sh, last_sh, redo_sh;
 
   const int t = blockIdx.x;
@@ -127,16 +135,36 @@ void sparse_attn256_kernel(SparseParams p) {
   const int hq = g * group + hb * HPB + w * HPW + col;
   const int ntiles_all = (p.topk + TK - 1) / TK;
 
-  // ---- index row -> LDS (fetch row, 0 where invalid), per-tile validity
-  // masks, the last tile holding a valid entry, out-of-range flag
+  // ---- Q^T fragments (B operand): head `col`, dims 32ks + 8grp .. +8, and
+  // the query's index row; every load is in flight at once (one round trip)
   if (tid == 0) { bad_sh = 0; last_sh = -1; redo_sh = 0; }
-  __syncthreads();
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = p.q + b * p.sq.b + (int64_t)t * p.sq.s + (int64_t)hq * p.sq.h + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
+  }
+  constexpr int NJ = MAXK / 256;
+  int uv[NJ];
   {
     const int32_t* irow = p.idx + ((int64_t)b * p.seqlen + t) * p.topk;
+#pragma unroll
+    for (int k = 0; k < NJ; ++k) {
+      const int j = 256 * k + tid;
+      uv[k] = j < p.topk ? irow[j] : -1;
+    }
+  }
+  __syncthreads();  // flags initialised
+  // index row -> LDS (fetch row, 0 where invalid), per-tile validity masks,
+  // the last tile holding a valid entry, out-of-range flag
+  {
     int bad = 0, last = -1;
-    for (int j0 = 0; j0 < ntiles_all * TK; j0 += 256) {
+#pragma unroll
+    for (int k = 0; k < NJ; ++k) {
+      const int j0 = 256 * k;
+      if (j0 >= ntiles_all * TK) break;
       const int j = j0 + tid;
-      const int u = j < p.topk ? irow[j] : -1;
+      const int u = uv[k];
       bad |= (u < -1 || u >= p.n_kv);
       const bool ok = u >= 0 && u < p.n_kv;
       if (j < ntiles_all * TK) sidx[j] = ok ? u : 0;
@@ -152,16 +180,8 @@ void sparse_attn256_kernel(SparseParams p) {
     if (bad) atomicOr(&bad_sh, 1);
     if (lane == 0 && last >= 0) atomicMax(&last_sh, last);
   }
-
-  // ---- Q^T fragments (B operand): head `col`, dims 32ks + 8grp .. +8
-  bf16x8 qf[8];
-  {
-    const uint16_t* qp = p.q + b * p.sq.b + (int64_t)t * p.sq.s + (int64_t)hq * p.sq.h + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 32 * ks));
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
   __syncthreads();  // sidx, tvalid, flags complete; Q settled before the DMA ring
   const int ntiles = __builtin_amdgcn_readfirstlane(last_sh + 1);
 
@@ -205,18 +225,20 @@ void sparse_attn256_kernel(SparseParams p) {
   // Per-lane LDS read offsets within a stage.
   //   K (A operand, key half kt, step ks): row 16kt + col, chunk 4ks + grp in slot
   //     (4ks + grp) ^ col: k_off[ks % 4] + 256 (ks / 4) + 16 kt ROWB.
-  //   V^T (A operand of dim tile dt, read e): row 16e + 4grp + col/4, dims
-  //     16dt + 4(col % 4), chunk 2dt + (col % 4)/2 in slot chunk ^ 2(row mod 8):
-  //     v_off[dt % 8] + 256 (dt / 8) + 16 e ROWB.
-  uint32_t k_off[4], v_off[8];
+  //   V^T (A operand of dim tile dt = 4w + i, read e): row 16e + 4grp + col/4,
+  //     dims 16dt + 4(col % 4), chunk 2dt + (col % 4)/2 in slot chunk ^ 2(row mod 8):
+  //     v_off[i] + 16 e ROWB.
+  uint32_t k_off[4], v_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) k_off[i] = col * ROWB + 16 * ((4 * i + grp) ^ col);
   {
     const int row = 4 * grp + (col >> 2);
     const int s = row & 7;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v_off[i] = KSTB + row * ROWB + 32 * (i ^ s) + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+    for (int i = 0; i < 4; ++i) {
+      const int dt = 4 * w + i;
+      v_off[i] = KSTB + row * ROWB + 32 * ((dt & 7) ^ s) + 256 * (dt >> 3) + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+    }
   }
   // Entry number (bit of the tile's validity mask) of the S^T rows this lane
   // holds: row 16kt + 4grp + r sits in LDS row order, see the DMA above.
@@ -229,7 +251,7 @@ void sparse_attn256_kernel(SparseParams p) {
       ebit[4 * kt + r] = 8 * (rho >> 3) + 4 * (rho & 1) + ((rho & 7) >> 1);
     }
 
-  f32x4 o[16], lacc;
+  f32x4 o[4][4], lacc;  // o[dim tile 4w + i][head block]
   const float c = p.c;
   const float NEG = POS ? -INFINITY : INFINITY;  // raw score that maps to a -inf logit
   float m_ref = -INFINITY;                       // reference (scaled, log2 domain) of this lane's head
@@ -259,8 +281,11 @@ void sparse_attn256_kernel(SparseParams p) {
 
   // One tile.  When `dma` is set, the 8 DMA instructions of tile tt+NRING-1
   // go out between the first S^T steps, so their issue overlaps the products.
-  auto compute = [&](uint32_t vmask, const unsigned char* sb, bool dma, const int4& u4, int dst)
-      __attribute__((always_inline)) {
+  // The PV product of the previous tile (its V^T and P^T operands held in vq
+  // and pq since then, when `pend` is set) is interleaved with this tile's S^T
+  // steps; on return vq and pq hold this tile's operands.
+  auto compute = [&](uint32_t vmask, const unsigned char* sb, bool dma, const int4& u4, int dst, bool pend,
+                     bf16x8 (&vq)[4], bf16x8 (&pq)[4]) __attribute__((always_inline)) {
     // S^T = K Q^T for the two 16-key halves; MFMA i is step i/2 of half i%2,
     // its K operand is read four MFMAs ahead (the scheduling barriers keep
     // that order)
@@ -268,8 +293,8 @@ void sparse_attn256_kernel(SparseParams p) {
       return __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(sb + k_off[(i >> 1) & 3] + 256 * (i >> 3) + 16 * (i & 1) * ROWB));
     };
-    auto ldv = [&](int dt) __attribute__((always_inline)) {
-      const unsigned char* vp = sb + v_off[dt & 7] + 256 * (dt >> 3);
+    auto ldv = [&](int i) __attribute__((always_inline)) {  // dim tile 4w + i
+      const unsigned char* vp = sb + v_off[i];
       const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
       const s16x4 hi4 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 16 * ROWB));
@@ -285,11 +310,11 @@ void sparse_attn256_kernel(SparseParams p) {
       if (i + 4 < 16) kq[i & 3] = ldk(i + 4);
       if (i < 2) mfma_s_first(s[i & 1], ka, qf[i >> 1]);
       else mfma_s(s[i & 1], ka, qf[i >> 1]);
+      if (pend) mfma_o(o[i >> 2][i & 3], vq[i >> 2], pq[i & 3]);
       if (i < 8 && dma) dma_one(u4, dst, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the first V^T operands do not depend on P: their reads overlap the softmax
-    bf16x8 vq[4];
+    // the V^T operands do not depend on P: their reads overlap the softmax
 #pragma unroll
     for (int i = 0; i < 4; ++i) vq[i] = ldv(i);
     __builtin_amdgcn_sched_barrier(0);
@@ -317,17 +342,23 @@ void sparse_attn256_kernel(SparseParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(ps[2 * e], ps[2 * e + 1]);
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
-    __builtin_amdgcn_sched_barrier(0);
-    // O^T += V^T P^T : 16 dim tiles, k = the 32 keys of the tile; then the row sum
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const bf16x8 va = vq[dt & 3];
-      if (dt + 4 < 16) vq[dt & 3] = ldv(dt + 4);
-      if (dt == 0) mfma_o_first(o[dt], va, pf);
-      else mfma_o(o[dt], va, pf);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // P^T of this wave's heads to LDS (lane order is the B operand's), the row
+    // sums of its heads, then every wave takes all four head blocks
+    *reinterpret_cast<u32x4*>(pbuf + w * (HPW * TK * 2) + 16 * lane) = pk;
     mfma_o_first(lacc, ones8, pf);  // the ones operand may have just been rematerialised by VALU
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int hk = 0; hk < 4; ++hk)
+      pq[hk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbuf + hk * (HPW * TK * 2) + 16 * lane));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // O^T += V^T P^T of one tile: this wave's 4 dim tiles x the 4 head blocks,
+  // k = the 32 keys of the tile
+  auto pv = [&](const bf16x8 (&vq)[4], const bf16x8 (&pq)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hk = 0; hk < 4; ++hk) mfma_o(o[i][hk], vq[i], pq[hk]);
   };
 
   // Ring: tiles 0 .. NRING-2 are issued up front; the trip for tile tt waits
@@ -339,11 +370,14 @@ void sparse_attn256_kernel(SparseParams p) {
   // decided for the whole workgroup, as the loop holds barriers.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) zero_o(o[dt], zero8);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hk = 0; hk < 4; ++hk) zero_o(o[i][hk], zero8);
     zero_o(lacc, zero8);
     for (int i = 0; i < NRING - 1; ++i)
       if (i < ntiles) issue(i, i);
     int st = 0;
+    bf16x8 vq[4], pq[4];                        // operands of the PV product still to do
     uint32_t vm = ntiles > 0 ? tvalid[0] : 0u;  // validity word of the next tile, read ahead
     for (int tt = 0; tt < ntiles; ++tt) {
       const uint32_t vmask = __builtin_amdgcn_readfirstlane(vm);
@@ -353,9 +387,10 @@ void sparse_attn256_kernel(SparseParams p) {
       if (after >= 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
       else if (after == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      compute(vmask, ring + st * STAGEB, tt + NRING - 1 < ntiles, u4, st == 0 ? NRING - 1 : st - 1);
+      compute(vmask, ring + st * STAGEB, tt + NRING - 1 < ntiles, u4, st == 0 ? NRING - 1 : st - 1, tt > 0, vq, pq);
       st = st == NRING - 1 ? 0 : st + 1;
     }
+    if (ntiles > 0) pv(vq, pq);  // the last tile's PV product
     if (pass == 1) break;
     float mh = ext(m_run, __shfl_xor(m_run, 16));
     mh = ext(mh, __shfl_xor(mh, 32));
@@ -368,25 +403,36 @@ void sparse_attn256_kernel(SparseParams p) {
     m_ref = top;  // every probability of the second pass is at most 1
   }
 
-  // ---- epilogue (wait states: the AGPRs are read right after the last MFMA)
+  // ---- epilogue (wait states: the AGPRs are read right after the last MFMA).
+  // Each head's row sum lives with the wave that owns the head; O^T of every
+  // head is spread over the four waves by dims.
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) asm volatile("" : "+a"(o[dt]));
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int hk = 0; hk < 4; ++hk) asm volatile("" : "+a"(o[i][hk]));
   asm volatile("" : "+a"(lacc));
   const bool poisoned = bad_sh != 0;
-  const float l_tot = lacc[0];
-  const float inv = poisoned ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
-  uint16_t* op = p.o + b * p.so.b + (int64_t)t * p.so.s + (int64_t)hq * p.so.h + 4 * grp;
-#pragma unroll
-  for (int dt = 0; dt < 16; ++dt) {
-    u32x2 pk;
-    pk[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-    pk[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-    *reinterpret_cast<u32x2*>(op + 16 * dt) = pk;
-  }
+  const float l_own = lacc[0];
+  if (grp == 0) lsh[HPW * w + col] = l_own;
   if (p.lse && grp == 0)
     p.lse[((int64_t)b * p.h_q + hq) * p.seqlen + t] =
-        poisoned ? __builtin_nanf("") : (have_ref ? m_ref * kLn2 + __logf(l_tot) : -INFINITY);
+        poisoned ? __builtin_nanf("") : (have_ref ? m_ref * kLn2 + __logf(l_own) : -INFINITY);
+  __syncthreads();
+#pragma unroll
+  for (int hk = 0; hk < 4; ++hk) {
+    const float l_tot = lsh[HPW * hk + col];
+    const float inv = poisoned ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
+    const int hq_k = g * group + hb * HPB + HPW * hk + col;
+    uint16_t* op = p.o + b * p.so.b + (int64_t)t * p.so.s + (int64_t)hq_k * p.so.h + 4 * grp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[i][hk][0] * inv, o[i][hk][1] * inv);
+      pk[1] = pack_bf16x2(o[i][hk][2] * inv, o[i][hk][3] * inv);
+      *reinterpret_cast<u32x2*>(op + 16 * (4 * w + i)) = pk;
+    }
+  }
 }
 
 }  // namespace
@@ -415,12 +461,13 @@ hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, 
   p.v_row_bytes = (uint32_t)vr;
   const bool pos = !(p.c < 0.f);
   dim3 grid(seqlen, h_kv * p.n_hb, batch);
-  if (wide) {
-    if (pos) hipLaunchKernelGGL((sparse_attn256_kernel<true, true>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((sparse_attn256_kernel<false, true>), grid, dim3(256), 0, st, p);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p); };
+  if (topk <= 2048) {
+    if (wide) pos ? go(sparse_attn256_kernel<true, true, 2, 2048>) : go(sparse_attn256_kernel<false, true, 2, 2048>);
+    else pos ? go(sparse_attn256_kernel<true, false, 2, 2048>) : go(sparse_attn256_kernel<false, false, 2, 2048>);
   } else {
-    if (pos) hipLaunchKernelGGL((sparse_attn256_kernel<true, false>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((sparse_attn256_kernel<false, false>), grid, dim3(256), 0, st, p);
+    if (wide) pos ? go(sparse_attn256_kernel<true, true, 4, 4096>) : go(sparse_attn256_kernel<false, true, 4, 4096>);
+    else pos ? go(sparse_attn256_kernel<true, false, 4, 4096>) : go(sparse_attn256_kernel<false, false, 4, 4096>);
   }
   return hipGetLastError();
 }

@@ -258,6 +258,21 @@ def test_sparse_attention_wide_position_stride():
     assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
 
 
+def test_sparse_attention_rows_longer_than_2048():
+    """topk in (2048, 4096] runs the one-workgroup-per-CU configuration (a
+    4-stage ring and 4096-entry rows); rows shorter than topk end in -1."""
+    S, topk = 3300, 3000
+    cfg = synth.small_dsa(seqlen=S, topk=topk)
+    _say("long rows", cfg)
+    inp = synth.make_dsa(cfg)
+    idx = synth.make_index_lists(1, S, topk, seed=15)
+    o, lse = _sparse_case(cfg, inp, idx)
+    rows = sorted(set([0, 1, 31, 32, 2047, 2999, 3000, S - 1]) | set(np.random.default_rng(16).integers(0, S, 8).tolist()))
+    ro, rlse = _oracle_rows(inp, idx, cfg.scale, rows)
+    assert rel_err(host(o)[:, rows], ro) < BF16_TOL
+    assert np.max(np.abs(host(lse)[:, :, rows] - rlse)) < LSE_TOL
+
+
 @pytest.mark.timeout(900)
 def test_full_size_dsa_sampled():
     cfg = synth.CONFIGS["c5"]
