@@ -112,7 +112,8 @@ __device__ __forceinline__ void zero_o(f32x4& acc, const bf16x8& z) {
 // NRING ring stages (NRING - 1 tiles in flight) and rows of up to MAXK
 // entries: <2, 2048> keeps a workgroup under 80 KB of LDS so that two run on
 // a CU (two waves per SIMD, whose serial S -> softmax -> PV chains and
-// per-query start-up interleave); <4, 4096> is one workgroup per CU.
+// per-query start-up interleave); <4, 4096> is one workgroup per CU (rows
+// longer than 2048, and grids too small to fill the chip twice over).
 template <bool POS, bool WIDE, int NRING, int MAXK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NRING == 2 ? 2 : 1)))
 void sparse_attn256_kernel(SparseParams p) {
@@ -462,7 +463,11 @@ hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, 
   const bool pos = !(p.c < 0.f);
   dim3 grid(seqlen, h_kv * p.n_hb, batch);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p); };
-  if (topk <= 2048) {
+  // Two workgroups per CU pay off when there are enough of them to fill the
+  // chip; a small grid (decode: one workgroup per sequence) keeps the deeper
+  // ring, which hides more gather latency per workgroup.
+  const int64_t n_wg = (int64_t)seqlen * h_kv * p.n_hb * batch;
+  if (topk <= 2048 && n_wg >= 1024) {
     if (wide) pos ? go(sparse_attn256_kernel<true, true, 2, 2048>) : go(sparse_attn256_kernel<false, true, 2, 2048>);
     else pos ? go(sparse_attn256_kernel<true, false, 2, 2048>) : go(sparse_attn256_kernel<false, false, 2, 2048>);
   } else {
