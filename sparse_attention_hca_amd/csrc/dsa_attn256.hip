@@ -9,21 +9,24 @@
 // for S^T = K Q^T (32 keys x 16 heads, v_mfma_f32_16x16x32_bf16) and their
 // softmax, publishes its P^T (bf16, 1 KB per tile) in LDS, and then computes
 // O^T += V^T P^T for dims 64w .. 64w+63 of all 64 heads (the 32 keys of a
-// tile as the contraction).  Each V^T byte is thus read from LDS by one wave
-// instead of four: the loop is bound by LDS instruction issue, and the
-// transposing V reads were most of it.
+// tile as the contraction), each V^T byte read from LDS by one wave.  The PV
+// product of a tile runs interleaved with the next tile's S^T steps.  With
+// one wave per SIMD the per-wave chain S -> softmax -> exchange -> PV and the
+// per-query start-up are serial, so for rows of up to 2048 entries the ring
+// is kept small enough for two workgroups to share a CU.
 //
-// The step is a gather of 2 x 512 bytes per selected position, so the design
-// keeps as many rows in flight as LDS holds:
+// The step is a gather of 2 x 512 bytes per selected position:
 //   * The query's index row is copied to LDS once, with a 32-bit validity mask
 //     per 32-entry tile (a wave ballot); -1 entries and out-of-range positions
 //     are fetched as row 0 (valid memory) and masked, an out-of-range position
 //     also turns the row's output into NaN.  Trailing tiles with no valid entry
 //     are not visited, so rows shorter than topk cost what they hold; an
 //     interior tile with none takes the masked path (all probabilities 0).
+//   * Q and the index row are loaded with every load in flight at once.
 //   * Tiles of 32 gathered K and V rows move global -> LDS with 16-byte LDS
-//     DMA through a ring of 4 stages: three tiles (96 KB) in flight while one
-//     is consumed.  DMA instruction i of wave w fetches entries 8w+i (lanes
+//     DMA through a ring of NRING stages (NRING - 1 tiles in flight while one
+//     is consumed), the next tile's DMA instructions interleaved with the
+//     S^T steps.  DMA instruction i of wave w fetches entries 8w+i (lanes
 //     0-31) and 8w+4+i (lanes 32-63) into the adjacent LDS rows 8w+2i and
 //     8w+2i+1, so a lane's four row numbers are one 16-byte LDS read; the
 //     addresses are a scalar base plus a 32-bit row offset (64-bit addresses
