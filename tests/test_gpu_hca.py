@@ -66,6 +66,44 @@ def test_compress_parity(dtype, d, block, S):
     assert rel_err(host(kc), rk) < tol and rel_err(host(vc), rv) < tol
 
 
+@pytest.mark.parametrize("dtype,H,d,block,S,B", [("bf16", 4, 512, 128, 1000, 2), ("bf16", 16, 512, 66, 500, 1),
+                                                  ("f32", 8, 256, 128, 700, 1), ("f32", 4, 512, 64, 300, 1)])
+def test_compress_all_heads_per_workgroup_parity(dtype, H, d, block, S, B):
+    """Shapes whose heads fill whole waves (h * d / 16-byte pieces a multiple
+    of 256) take the kernel with one workgroup per block covering every head;
+    block 66 leaves a tail of rows after the 4-row batches."""
+    cfg = synth.small_prefill("c2" if dtype == "bf16" else "c1", dtype=dtype, seqlen=S, h_q=H, h_kv=H,
+                              head_dim=d, block=block, batch=B)
+    _say("compress rows", cfg)
+    inp = synth.make_prefill(cfg)
+    k, v = _to_dev(inp, "k"), _to_dev(inp, "v")
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, block)
+    torch.cuda.synchronize()
+    rk = oracle.compress_kv(f64(inp["k"], inp["bf16"]), inp["w"], block)
+    rv = oracle.compress_kv(f64(inp["v"], inp["bf16"]), inp["w"], block)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    assert kc.shape == rk.shape
+    assert rel_err(host(kc), rk) < tol and rel_err(host(vc), rv) < tol
+
+
+def test_compress_all_heads_one_hot_is_bit_exact_with_strided_heads():
+    H = 4
+    cfg = synth.small_prefill("c2", seqlen=384, h_q=H, h_kv=H)
+    inp = synth.make_prefill(cfg)
+    big = torch.zeros(1, 384, 2 * H + 1, 512, dtype=torch.bfloat16, device="cuda:0")
+    big[:, :, 1:2 * H + 1:2] = dev_bf16(inp["k"])
+    k = big[:, :, 1:2 * H + 1:2]                        # head stride 2 * 512
+    w = torch.zeros(H, 128, device="cuda:0")
+    for h in range(H):
+        w[h, 31 * h + 5] = 1.0
+    kc, vc = hca.hca_compress_kv(k, k, w, w, 128)
+    torch.cuda.synchronize()
+    kd = dev_bf16(inp["k"])
+    ref = torch.stack([kd[0, 31 * h + 5::128, h] for h in range(H)], dim=1)[None]
+    assert torch.equal(kc, ref) and torch.equal(vc, ref)
+
+
 def test_compress_one_hot_is_bit_exact_and_strided_views_work():
     cfg = synth.small_prefill("c2", seqlen=640, h_q=2, h_kv=2)
     inp = synth.make_prefill(cfg)
