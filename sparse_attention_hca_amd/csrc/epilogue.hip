@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void vha_gate_kernel(VhaParams p) {
     float o0[H], o1[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(ob + (int64_t)h * p.so.h + e);
+      const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ob + (int64_t)h * p.so.h + e));
       o0[h] = __uint_as_float(x << 16);
       o1[h] = __uint_as_float(x & 0xffff0000u);
     }
@@ -190,8 +190,9 @@ __global__ __launch_bounds__(256) void vha_gate_kernel(VhaParams p) {
         z1 = fmaf(su[h * R + j], p1[j], z1);
       }
       uint32_t* yp = reinterpret_cast<uint32_t*>(yb + (int64_t)h * p.sy.h + e);
-      const uint32_t gx = *yp;
-      *yp = pack_bf16x2(__uint_as_float(gx << 16) * z0, __uint_as_float(gx & 0xffff0000u) * z1);
+      const uint32_t gx = __builtin_nontemporal_load(yp);
+      __builtin_nontemporal_store(pack_bf16x2(__uint_as_float(gx << 16) * z0, __uint_as_float(gx & 0xffff0000u) * z1),
+                                  yp);
     }
   }
 }
