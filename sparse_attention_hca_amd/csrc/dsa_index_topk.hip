@@ -790,6 +790,66 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const float* qI, con
   sc[(int64_t)b * ld + u] = s;
 }
 
+// The same scores for 64-wide index keys with coalesced loads: each wave
+// covers 64 keys in 4 blocks of 16, four lanes per key; load c of a block
+// reads dims 16c .. 16c+15 of its 16 keys (lane l: key l/4, dims 16c + 4(l%4)
+// .. +3), so an instruction touches 16 cache lines instead of 64.  The four
+// partial dot products of a key are summed across its lane quad.
+template <int HI>
+__global__ __launch_bounds__(256) void decode_scores64_kernel(const float* qI, const float* kI, const float* w,
+                                                              float* sc, int64_t ld, int n) {
+  constexpr int DI = 64;
+  __shared__ __attribute__((aligned(16))) float qs[HI * DI];
+  __shared__ float wsh[HI];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w4 = tid >> 6;
+  for (int i = tid; i < HI * DI; i += 256) qs[i] = qI[(int64_t)b * HI * DI + i];
+  if (tid < HI) wsh[tid] = w[(int64_t)b * HI + tid];
+  __syncthreads();
+  const int key0 = blockIdx.x * 256 + 64 * w4;
+  if (key0 >= n) return;
+  const int q4 = lane & 3;
+  float acc[4][HI];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int h = 0; h < HI; ++h) acc[kb][h] = 0.f;
+  f32x4 kv[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int u = min(key0 + 16 * kb + (lane >> 2), n - 1);
+    const float* kr = kI + ((int64_t)b * n + u) * DI + 4 * q4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kv[kb][c] = *reinterpret_cast<const f32x4*>(kr + 16 * c);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int h = 0; h < HI; ++h) {
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + h * DI + 16 * c + 4 * q4);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        acc[kb][h] = fmaf(kv[kb][c][0], qv[0], acc[kb][h]);
+        acc[kb][h] = fmaf(kv[kb][c][1], qv[1], acc[kb][h]);
+        acc[kb][h] = fmaf(kv[kb][c][2], qv[2], acc[kb][h]);
+        acc[kb][h] = fmaf(kv[kb][c][3], qv[3], acc[kb][h]);
+      }
+    }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < HI; ++h) {
+      float a = acc[kb][h];
+      a += __shfl_xor(a, 1);
+      a += __shfl_xor(a, 2);
+      s = fmaf(wsh[h], fmaxf(a, 0.f), s);
+    }
+    const int u = key0 + 16 * kb + (lane >> 2);
+    if (q4 == 0 && u < n) sc[(int64_t)b * ld + u] = s;
+  }
+}
+
 constexpr int SEG = 65536;  // keys per first-stage row of a decode selection
 
 // The first stage leaves, per (sequence, segment), the segment's selected
@@ -970,7 +1030,7 @@ hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const 
       case 16: HCA_DEC_SCORES(16, 4); break;
       case 32: HCA_DEC_SCORES(32, 4); break;
       case 48: HCA_DEC_SCORES(48, 4); break;
-      case 64: HCA_DEC_SCORES(64, 4); break;
+      case 64: hipLaunchKernelGGL((decode_scores64_kernel<4>), gs, dim3(256), 0, st, qI, kI, w, sc, ld, n_keys); break;
       case 80: HCA_DEC_SCORES(80, 4); break;
       case 96: HCA_DEC_SCORES(96, 4); break;
       case 112: HCA_DEC_SCORES(112, 4); break;
@@ -982,7 +1042,7 @@ hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const 
       case 16: HCA_DEC_SCORES(16, 8); break;
       case 32: HCA_DEC_SCORES(32, 8); break;
       case 48: HCA_DEC_SCORES(48, 8); break;
-      case 64: HCA_DEC_SCORES(64, 8); break;
+      case 64: hipLaunchKernelGGL((decode_scores64_kernel<8>), gs, dim3(256), 0, st, qI, kI, w, sc, ld, n_keys); break;
       case 80: HCA_DEC_SCORES(80, 8); break;
       case 96: HCA_DEC_SCORES(96, 8); break;
       case 112: HCA_DEC_SCORES(112, 8); break;
