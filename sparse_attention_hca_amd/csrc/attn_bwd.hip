@@ -357,6 +357,19 @@ __device__ __forceinline__ f32x4 ld4f<uint16_t>(const uint16_t* p) {
   return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
                __uint_as_float(u[1] & 0xffff0000u)};
 }
+// The same for data read once (non-temporal loads).
+template <typename T>
+__device__ __forceinline__ f32x4 ld4f_nt(const T* p);
+template <>
+__device__ __forceinline__ f32x4 ld4f_nt<float>(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+template <>
+__device__ __forceinline__ f32x4 ld4f_nt<uint16_t>(const uint16_t* p) {
+  const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+               __uint_as_float(u[1] & 0xffff0000u)};
+}
 
 // dw[h, i] = sum_{b, j} <dxc[b, j, h, :], x[b, j*block + i, h, :]>: one
 // workgroup per (row-in-block i, head h, K or V); threads hold 4 dims and
@@ -374,10 +387,11 @@ __global__ __launch_bounds__(NT) void comp_bwd_dw_kernel(CompBwdArgs c) {
   float acc = 0.f;
   if (e < c.d) {
     for (int b = 0; b < c.batch; ++b)
-#pragma unroll 4
+#pragma unroll 8
       for (int j = half; j < c.nb; j += 2) {
         const f32x4 g = *reinterpret_cast<const f32x4*>(dxc + b * sd.b + (int64_t)j * sd.s + (int64_t)h * sd.h + e);
-        const f32x4 xv = ld4f<T>(x + b * sx.b + ((int64_t)j * c.block + i) * sx.s + (int64_t)h * sx.h + e);
+        // each K/V row is read once per call: non-temporal
+        const f32x4 xv = ld4f_nt<T>(x + b * sx.b + ((int64_t)j * c.block + i) * sx.s + (int64_t)h * sx.h + e);
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc = fmaf(g[t], xv[t], acc);
       }
