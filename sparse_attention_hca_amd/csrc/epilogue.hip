@@ -5,10 +5,12 @@
 // low-rank cross-head mixing with an identity skip.
 //   y[b,t,h,e] = sigmoid(<c[b,t,:], W_g[h*d_v + e, :]>) * (o[b,t,h,e] + sum_h' (U V)[h,h'] o[b,t,h',e])
 //
-// Two kernels:
-//   * gate_proj_kernel: the gate projection as a bf16 MFMA GEMM
-//     (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with the sigmoid in its
-//     epilogue, written (bf16) into y.  Workgroup tile 256 tokens x 256
+// Two steps:
+//   * the gate projection G = C W_g^T, a plain GEMM, written as the bf16
+//     pre-activation into y: by hipBLASLt when each token's heads are
+//     contiguous in y (it runs this shape at ~1.3 PFLOP/s), else by
+//     gate_proj_kernel, a bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32
+//     accumulation; ~0.8 PFLOP/s).  Workgroup tile 256 tokens x 256
 //     outputs, 8 waves of 64 x 128 (two per SIMD), K streamed in chunks of 32 through a
 //     3-stage LDS ring (two chunks in flight) by 16-byte LDS DMA.  The
 //     product is formed transposed (W rows as the A operand) so a lane ends
@@ -19,8 +21,14 @@
 //     while each DMA instruction still fills one contiguous kilobyte.
 //   * vha_gate_kernel: one workgroup per token, one dim pair per thread; each
 //     thread holds the pair for every head, forms p = V o (rank r, padded to
-//     4, 8 or 16), then y = y * (o + U p) in place.  HBM-bound: o and y read
-//     once, y written once.
+//     4, 8 or 16), then y = sigmoid(y) * (o + U p) in place.  HBM-bound: o
+//     and y read once, y written once.
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "mfma_asm.h"
@@ -116,7 +124,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // epilogue: sigmoid, bf16; the lane's token is m, its outputs n .. n+3
+  // epilogue: the pre-activation in bf16 (the mixing kernel applies the
+  // sigmoid); the lane's token is m, its outputs n .. n+3
   // (one head, since d_v is a multiple of 8) go out as one 8-byte store
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -129,8 +138,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * hf;
         u32x2 pk;
-        pk[0] = pack_bf16x2(1.f / (1.f + __expf(-acc[j][i][4 * q])), 1.f / (1.f + __expf(-acc[j][i][4 * q + 1])));
-        pk[1] = pack_bf16x2(1.f / (1.f + __expf(-acc[j][i][4 * q + 2])), 1.f / (1.f + __expf(-acc[j][i][4 * q + 3])));
+        pk[0] = pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]);
+        pk[1] = pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
         *reinterpret_cast<u32x2*>(yr + (int64_t)(n / p.d_v) * p.syh + n % p.d_v) = pk;
       }
   }
@@ -190,9 +199,10 @@ __global__ __launch_bounds__(256) void vha_gate_kernel(VhaParams p) {
         z1 = fmaf(su[h * R + j], p1[j], z1);
       }
       uint32_t* yp = reinterpret_cast<uint32_t*>(yb + (int64_t)h * p.sy.h + e);
-      const uint32_t gx = __builtin_nontemporal_load(yp);
-      __builtin_nontemporal_store(pack_bf16x2(__uint_as_float(gx << 16) * z0, __uint_as_float(gx & 0xffff0000u) * z1),
-                                  yp);
+      const uint32_t gx = __builtin_nontemporal_load(yp);  // gate pre-activation
+      const float g0 = 1.f / (1.f + __expf(-__uint_as_float(gx << 16)));
+      const float g1 = 1.f / (1.f + __expf(-__uint_as_float(gx & 0xffff0000u)));
+      __builtin_nontemporal_store(pack_bf16x2(g0 * z0, g1 * z1), yp);
     }
   }
 }
@@ -207,24 +217,88 @@ hipError_t launch_vha(const VhaParams& vp, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+// G^T (out x tokens, column-major: y's token rows) = W_g (d_c x out,
+// column-major: W_g's [out, in] rows, transposed) ^T . C^T (d_c x tokens,
+// column-major: c's token rows), fp32 accumulation, bf16 result, no
+// workspace.  One hipBLASLt handle per device and one heuristic pick per
+// shape, created on first use.  Returns false when hipBLASLt cannot run the
+// product (the caller then uses gate_proj_kernel).
+bool gate_gemm_blaslt(const void* c, int64_t ldc_tok, const void* w_g, void* y, int64_t ldy_tok, int tokens, int out,
+                      int d_c, hipStream_t st) {
+  static std::mutex mu;
+  static std::map<int, hipblasLtHandle_t> handles;
+  static std::map<std::tuple<int, int, int, int, int64_t, int64_t>, hipblasLtMatmulAlgo_t> algos;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  hipblasLtHandle_t hdl;
+  auto hit = handles.find(dev);
+  if (hit == handles.end()) {
+    if (hipblasLtCreate(&hdl) != HIPBLAS_STATUS_SUCCESS) return false;
+    handles[dev] = hdl;
+  } else {
+    hdl = hit->second;
+  }
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+  bool ok = hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  ok = ok && hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, d_c, out, d_c) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, d_c, tokens, ldc_tok) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&ld, HIP_R_16BF, out, tokens, ldy_tok) == HIPBLAS_STATUS_SUCCESS;
+  if (ok) {
+    const auto key = std::make_tuple(dev, tokens, out, d_c, ldc_tok, ldy_tok);
+    auto ait = algos.find(key);
+    if (ait == algos.end()) {
+      hipblasLtMatmulPreference_t pref = nullptr;
+      uint64_t ws = 0;
+      hipblasLtMatmulHeuristicResult_t res[1];
+      int n = 0;
+      ok = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws, sizeof(ws)) ==
+               HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatmulAlgoGetHeuristic(hdl, op, la, lb, ld, ld, pref, 1, res, &n) == HIPBLAS_STATUS_SUCCESS &&
+           n > 0 && res[0].workspaceSize == 0;
+      if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+      if (ok) ait = algos.emplace(key, res[0].algo).first;
+    }
+    if (ok) {
+      const float alpha = 1.f, beta = 0.f;
+      ok = hipblasLtMatmul(hdl, op, &alpha, w_g, la, c, lb, &beta, y, ld, y, ld, &ait->second, nullptr, 0, st) ==
+           HIPBLAS_STATUS_SUCCESS;
+    }
+  }
+  if (ld) hipblasLtMatrixLayoutDestroy(ld);
+  if (lb) hipblasLtMatrixLayoutDestroy(lb);
+  if (la) hipblasLtMatrixLayoutDestroy(la);
+  if (op) hipblasLtMatmulDescDestroy(op);
+  return ok;
+}
+
 hipError_t launch_attn_output_epilogue(const void* o, LStrides so, const void* c, int64_t scs, const void* w_g,
                                        const float* u, const float* v, void* y, LStrides sy, int batch, int seqlen,
                                        int h, int d_v, int d_c, int r, hipStream_t st) {
-  GateParams gp;
-  gp.c = (const uint16_t*)c;
-  gp.scs = scs;
-  gp.w = (const uint16_t*)w_g;
-  gp.y = (uint16_t*)y;
-  gp.sys = sy.s;
-  gp.syh = sy.h;
-  gp.M = batch * seqlen;
-  gp.d_c = d_c;
-  gp.d_v = d_v;
-  gp.m_tiles = (gp.M + GM - 1) / GM;
-  const int n_tiles = h * d_v / GN;
-  hipLaunchKernelGGL(gate_proj_kernel, dim3(gp.m_tiles * n_tiles), dim3(64 * G_WAVES), 0, st, gp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool lib = sy.h == d_v &&
+                   gate_gemm_blaslt(c, scs, w_g, y, sy.s, batch * seqlen, h * d_v, d_c, st);
+  if (!lib) {
+    GateParams gp;
+    gp.c = (const uint16_t*)c;
+    gp.scs = scs;
+    gp.w = (const uint16_t*)w_g;
+    gp.y = (uint16_t*)y;
+    gp.sys = sy.s;
+    gp.syh = sy.h;
+    gp.M = batch * seqlen;
+    gp.d_c = d_c;
+    gp.d_v = d_v;
+    gp.m_tiles = (gp.M + GM - 1) / GM;
+    const int n_tiles = h * d_v / GN;
+    hipLaunchKernelGGL(gate_proj_kernel, dim3(gp.m_tiles * n_tiles), dim3(64 * G_WAVES), 0, st, gp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   VhaParams vp;
   vp.o = (const uint16_t*)o;
   vp.so = so;

@@ -71,6 +71,19 @@ def test_epilogue_strided_output_of_attention():
     assert rel_err(host(y), ref) < BF16_TOL
 
 
+def test_epilogue_head_strided_output_uses_the_mfma_gemm():
+    """y whose heads are not contiguous within a token (head stride 2 d_v)
+    takes the hand-written gate GEMM instead of the library one."""
+    B, S, H, dv, dc, r = 1, 300, 16, 256, 512, 4
+    o, c, w, u, v = _inputs(B, S, H, dv, dc, r, 505)
+    big = torch.zeros(B, S, H, 2 * dv, dtype=torch.bfloat16, device="cuda:0")
+    y = hca.attn_output_epilogue(dev_bf16(o), dev_bf16(c), dev_bf16(w), dev_f32(u), dev_f32(v), y=big[..., :dv])
+    torch.cuda.synchronize()
+    ref = oracle.gated_vha_output(f64(o, True), f64(c, True), f64(w, True), u, v)
+    assert rel_err(host(y), ref) < BF16_TOL
+    assert (host(big[..., dv:]) == 0).all()
+
+
 @pytest.mark.timeout(600)
 def test_full_size_epilogue_sampled():
     """The epilogue at the 32768-token HCA shape (16 heads x 512, latent 2048,
