@@ -284,13 +284,20 @@ void prefill512_kernel(PrefillParams p) {
     risk = false;
   }
 
-  // ---- epilogue: normalise, store bf16 O and the LSE (wait states: O^T is
-  // read right after the last MFMA wrote it)
+  // ---- epilogue: normalise, then stage this wave's bf16 O rows in the DMA
+  // ring (idle once every wave has passed the barrier below; each wave owns a
+  // disjoint 32-row slice) and store whole 1-KB rows with one coalesced
+  // 16-byte store per lane: storing straight from the accumulator layout
+  // writes each row in 16-byte pieces spread over 64 instructions, which costs
+  // about a third more HBM write traffic than the output holds.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // wait states: O^T is read right after the last MFMA wrote it
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
   float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* op = (uint16_t*)a.o + b * a.so.b + (int64_t)iq * a.so.s + (int64_t)h * a.so.h + 4 * hf;
+  constexpr int OROW = 2 * D + 16;  // LDS bytes per staged O row
+  static_assert(NWAVE * WQ * OROW <= 2 * STAGE, "O staging must fit in the DMA ring");
+  unsigned char* ow = smem + w * (WQ * OROW);
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
@@ -298,9 +305,18 @@ void prefill512_kernel(PrefillParams p) {
       u32x2 pk;
       pk[0] = pack_bf16x2(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv);
       pk[1] = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q4) = pk;
+      *reinterpret_cast<u32x2*>(ow + col * OROW + 2 * (32 * dt + 8 * q4 + 4 * hf)) = pk;
     }
-  if (a.lse && hf == 0) a.lse[((int64_t)b * a.h_q + h) * a.seqlen_q + iq] = m_ref * kLn2 + __logf(l_tot);
+  // rows of this wave that exist (none when the wave's queries are all past the end)
+  const int nrow = min(WQ, a.seqlen_q - iw0);
+  uint16_t* obase = (uint16_t*)a.o + b * a.so.b + (int64_t)h * a.so.h + 8 * lane;
+#pragma unroll 8
+  for (int r = 0; r < WQ; ++r) {
+    if (r >= nrow) break;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ow + r * OROW + 16 * lane);
+    *reinterpret_cast<u32x4*>(obase + (int64_t)(iw0 + r) * a.so.s) = v;
+  }
+  if (a.lse && hf == 0 && qvalid) a.lse[((int64_t)b * a.h_q + h) * a.seqlen_q + iq] = m_ref * kLn2 + __logf(l_tot);
 }
 
 }  // namespace
