@@ -1,12 +1,14 @@
 """Benchmark of the HCA / DSA forward path on one MI355X.
 
-The timed step is HCA prefill at 32768 tokens (bf16, 16 heads, head_dim 512,
-block 128, window 128): block compression of K and V followed by attention.
-`value` is tokens per second of that step.  The other workloads of the path
-are timed in the same run and reported under `components`:
-  * HCA prefill at 131072 tokens (window 256): compression, attention, both;
+The timed step is HCA prefill at 131072 tokens (bf16, 16 heads, head_dim 512,
+block 128, window 256): block compression of K and V over the whole sequence
+followed by attention.  `value` is tokens per second of that step.  The other
+workloads of the path are timed in the same run and reported under
+`components`:
+  * HCA prefill at 32768 tokens (window 128): compression, attention;
   * HCA decode: 64 sequences x 1 query over 8192 compressed entries + 128 raw;
   * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention;
+  * DSA decode: 16 sequences x 1 query over 1,048,704 positions;
   * CSA prefill at 65536 tokens (the DSA shapes with K, V and the index keys
     compressed by blocks of 4): compression, indexer + top-2048 over the
     16384 entries, sparse attention;
@@ -17,11 +19,15 @@ are timed in the same run and reported under `components`:
     dk/dv through both paths, the compressor weight gradients).
 
 Inputs are seeded synthetic draws (the library's own generators) already
-resident in HBM when timing starts.  Kernel times come from HIP events on the
-stream the kernels are launched on.  `roofline` is for the dominant kernel of
-the step (prefill attention, HBM-bound at this size): algorithmic bytes per
-launch divided by its mean launch time.  `cpu_baseline` times the float64
-oracle on a bounded sample of the same workload on this host's cores.
+resident in HBM when timing starts.  Every call is timed by a pair of HIP
+events on the stream the library launches on (torch's current stream), one
+pair per call, after the 256 MB Infinity Cache has been flushed by writing a
+512 MiB scratch buffer (outside the event pair); figures are medians over the
+timed calls unless a key says otherwise.  `roofline` is for the dominant
+kernel of the step (prefill attention, bound by the matrix cores at this
+size): algorithmic FLOPs per launch divided by its mean launch time.
+`cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload on this host.
 """
 from __future__ import annotations
 
@@ -58,12 +64,13 @@ def source_hash(kernel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the current source of this kernel; else None."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` in `workload` from the committed
+    rocprofv3 PMC summary, if it was taken on the current source of this
+    kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)[kernel]
+            rec = json.load(f)[f"{kernel}@{workload}"]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("source_sha256_16") != source_hash(kernel):
@@ -110,31 +117,72 @@ def dsa_work(cfg):
     return idx_flops, attn_flops, sel
 
 
+_FLUSH = {}
+
+
+def mall_flush(torch):
+    """Write a 512 MiB scratch buffer so that no input of the next call is
+    served from the 256 MB Infinity Cache (or the L2s)."""
+    buf = _FLUSH.get("buf")
+    if buf is None:
+        buf = _FLUSH["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    buf.zero_()
+
+
 class Timer:
-    """Mean duration of repeated launches, from HIP events on the current stream."""
+    """Per-step durations from HIP events on torch's current stream, the stream
+    every library call launches on.  A step is one or more calls; an event is
+    recorded before the first and after each, so each call of the step has its
+    own duration.  The cache flush (when enabled) runs before the first event."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, flush=True):
         self.torch = torch
-        self.pairs = []
+        self.flush = flush
+        self.steps = []
 
-    def __call__(self, fn):
+    def __call__(self, *fns):
         t = self.torch
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record()
-        out = fn()
-        b.record()
-        self.pairs.append((a, b))
+        if self.flush:
+            mall_flush(t)
+        ev = [t.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record()
+        out = []
+        for f, e in zip(fns, ev[1:]):
+            out.append(f())
+            e.record()
+        self.steps.append(ev)
         return out
 
-    def mean_ms(self):
+    def durations(self, i=None):
+        """ms per step of call i (None: the whole step)."""
         self.torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+        if i is None:
+            return [ev[0].elapsed_time(ev[-1]) for ev in self.steps]
+        return [ev[i].elapsed_time(ev[i + 1]) for ev in self.steps]
+
+    def median_ms(self, i=None):
+        d = sorted(self.durations(i))
+        n = len(d)
+        return 0.5 * (d[(n - 1) // 2] + d[n // 2]) if n else float("nan")
+
+    def mean_ms(self, i=None):
+        d = self.durations(i)
+        return sum(d) / max(1, len(d))
 
 
-def bench_prefill(torch, hca, synth, cfg, steps, warmup):
+def bench_prefill(torch, hca, synth, cfg, steps, warmup, keep_heads=()):
+    """Time `steps` prefill steps (compression, then attention).  Returns the
+    medians and means of both calls and of the step, the wall clock of the
+    timed loop (flushes included), and, for `keep_heads`, host copies of those
+    heads' inputs for the CPU baseline."""
     import numpy as np
     t0 = time.time()
     inp = synth.make_prefill(cfg)
+    kept = None
+    if keep_heads:
+        h = list(keep_heads)
+        kept = {n: synth.bf16_bits_to_f32(inp[n][:, :, h]) for n in ("q", "k", "v")}
+        kept["w"] = inp["w"][h]
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
     q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
     del inp["q"], inp["k"], inp["v"]
@@ -145,24 +193,22 @@ def bench_prefill(torch, hca, synth, cfg, steps, warmup):
     vc = torch.empty_like(kc)
     o = torch.empty_like(q)
     lse = torch.empty((cfg.batch, cfg.h_q, cfg.seqlen), dtype=torch.float32, device="cuda:0")
-
-    def step(tc=None, ta=None):
-        f1 = lambda: hca.hca_compress_kv(k, v, w, w, cfg.block, kc=kc, vc=vc)
-        f2 = lambda: hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale,
-                                      o=o, lse=lse)
-        tc(f1) if tc else f1()
-        ta(f2) if ta else f2()
-
+    f1 = lambda: hca.hca_compress_kv(k, v, w, w, cfg.block, kc=kc, vc=vc)
+    f2 = lambda: hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale,
+                                  o=o, lse=lse)
     for _ in range(warmup):
-        step()
+        f1()
+        f2()
     torch.cuda.synchronize()
-    tc, ta = Timer(torch), Timer(torch)
+    tm = Timer(torch)
     start = time.perf_counter()
     for _ in range(steps):
-        step(tc, ta)
+        tm(f1, f2)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - start) * 1e3 / steps
-    res = {"compress_ms": tc.mean_ms(), "attn_ms": ta.mean_ms(), "step_ms": wall_ms}
+    res = {"compress_ms": tm.median_ms(0), "attn_ms": tm.median_ms(1), "step_ms": tm.median_ms(),
+           "compress_mean_ms": tm.mean_ms(0), "attn_mean_ms": tm.mean_ms(1), "step_mean_ms": tm.mean_ms(),
+           "wall_ms_per_step_incl_flush": wall_ms, "kept": kept}
     del q, k, v, o, kc, vc, lse
     torch.cuda.empty_cache()
     return res
@@ -182,9 +228,12 @@ def bench_decode(torch, hca, synth, cfg, steps, warmup):
                                  q_pos0=cfg.q_pos, kv_pos0=cfg.kv_pos0, o=o, lse=lse, workspace=ws)
     for _ in range(warmup):
         f()
-    # decode runs token after token: time `steps` back-to-back calls between
-    # one pair of events (per-call event pairs add their own stream commands,
-    # a few microseconds against a 0.2 ms call; that figure is kept as well)
+    # per call: events around each call, cache flushed before it (median)
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm(f)
+    # decode runs token after token: `steps` back-to-back calls between one
+    # pair of events, no flush (the 1.09 GB cache exceeds the Infinity Cache)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -192,10 +241,7 @@ def bench_decode(torch, hca, synth, cfg, steps, warmup):
         f()
     b.record()
     torch.cuda.synchronize()
-    tm = Timer(torch)
-    for _ in range(steps):
-        tm(f)
-    res = {"ms": a.elapsed_time(b) / steps, "ms_event_per_call": tm.mean_ms()}
+    res = {"ms": tm.median_ms(), "ms_mean": tm.mean_ms(), "ms_back_to_back": a.elapsed_time(b) / steps}
     # decode-time cache upkeep: one append per token (ring write), plus the
     # block compression on the token that closes a block.  These calls are
     # tiny, so the event-bracketed time is host-bound (argument marshalling
@@ -209,10 +255,10 @@ def bench_decode(torch, hca, synth, cfg, steps, warmup):
         g = lambda: hca.hca_append_kv(kw[:, :1], vw[:, :1], k_ring, v_ring, t, cfg.block, w, w, kc, vc)
         for _ in range(warmup):
             g()
-        ta = Timer(torch)
+        ta = Timer(torch, flush=False)
         for _ in range(steps):
             ta(g)
-        res[key] = ta.mean_ms() * 1e3
+        res[key] = ta.median_ms() * 1e3
     del q, kc, vc, kw, vw, o, ws, k_ring, v_ring
     torch.cuda.empty_cache()
     return res
@@ -237,11 +283,10 @@ def bench_dsa(torch, hca, synth, cfg, steps, warmup):
     for _ in range(warmup):
         fi()
         fa()
-    ti, ta = Timer(torch), Timer(torch)
+    tm = Timer(torch)
     for _ in range(steps):
-        ti(fi)
-        ta(fa)
-    res = {"index_topk_ms": ti.mean_ms(), "attn_ms": ta.mean_ms()}
+        tm(fi, fa)
+    res = {"index_topk_ms": tm.median_ms(0), "attn_ms": tm.median_ms(1), "attn_mean_ms": tm.mean_ms(1)}
     del q, k, v, qI, kI, w, idx, ws, o
     torch.cuda.empty_cache()
     return res
@@ -275,11 +320,10 @@ def bench_dsa_decode(torch, hca, steps, warmup):
     for _ in range(warmup):
         fi()
         fa()
-    ti, ta = Timer(torch), Timer(torch)
+    tm = Timer(torch)
     for _ in range(steps):
-        ti(fi)
-        ta(fa)
-    ms_i, ms_a = ti.mean_ms(), ta.mean_ms()
+        tm(fi, fa)
+    ms_i, ms_a = tm.median_ms(0), tm.median_ms(1)
     # indexer: every index key once, the score row written and read back once
     idx_bytes = B * n * (4 * c["d_i"] + 4 + 4)
     # attention: the selected K and V rows (bf16) plus q and o
@@ -332,12 +376,10 @@ def bench_csa(torch, hca, synth, cfg, steps, warmup):
         fc()
         fi()
         fa()
-    tc, ti, ta = Timer(torch), Timer(torch), Timer(torch)
+    tm = Timer(torch)
     for _ in range(steps):
-        tc(fc)
-        ti(fi)
-        ta(fa)
-    res = {"compress_ms": tc.mean_ms(), "index_topk_ms": ti.mean_ms(), "attn_ms": ta.mean_ms()}
+        tm(fc, fi, fa)
+    res = {"compress_ms": tm.median_ms(0), "index_topk_ms": tm.median_ms(1), "attn_ms": tm.median_ms(2)}
     del q, k, v, qI, kI, w, kc, vc, kIc4, kIc4_v, idx, ws, o, lse
     torch.cuda.empty_cache()
     return res
@@ -363,7 +405,7 @@ def bench_epilogue(torch, hca, steps, warmup):
     tm = Timer(torch)
     for _ in range(steps):
         tm(f)
-    ms = tm.mean_ms()
+    ms = tm.median_ms()
     flops = 2.0 * B * S * H * dv * dc
     byts = 2 * (B * S * dc + H * dv * dc + 2 * B * S * H * dv)
     del o, c, w, u, v, y
@@ -419,40 +461,52 @@ def bench_backward(torch, hca, synth, cfg, steps, warmup):
         tm = Timer(torch)
         for _ in range(steps):
             tm(f)
-        res[name] = tm.mean_ms()
+        res[name] = tm.median_ms()
         torch.cuda.empty_cache()
     del q, k, v, o, lse, dout, kc, vc, ws
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(synth, cfg, heads=4):
-    """The float64 oracle on a bounded sample of the headline workload: block
-    compression of K and V for `heads` heads and attention for every query row
-    of those heads; scaled to tokens/s of the whole step (all heads)."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, kept, row_stride=8):
+    """The float64 oracle, as it stands, on a bounded sample of the headline
+    step: for one head, compression of all its blocks (K and V) and attention
+    for every `row_stride`-th query row; BLAS held to one thread, so one core
+    does all the work.  Scaled to tokens/s of the whole step (all heads, all
+    rows; the strided rows cover the whole range of key counts)."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    inp = synth.make_prefill(cfg)
-    h = list(range(heads))
-    q = synth.bf16_bits_to_f32(inp["q"][:, :, h]).astype(np.float64)
-    k = synth.bf16_bits_to_f32(inp["k"][:, :, h]).astype(np.float64)
-    v = synth.bf16_bits_to_f32(inp["v"][:, :, h]).astype(np.float64)
-    del inp["q"], inp["k"], inp["v"]
-    t0 = time.perf_counter()
-    kc = oracle.compress_kv(k, inp["w"][h], cfg.block)
-    vc = oracle.compress_kv(v, inp["w"][h], cfg.block)
-    oracle.hca_attention(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
-    dt = time.perf_counter() - t0
-    est = dt * cfg.h_q / heads
-    return {"value": cfg.seqlen / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 oracle, {heads} of {cfg.h_q} heads of the {cfg.seqlen}-token prefill "
-                      f"(compression of all blocks + attention for every query row): {dt:.1f}s, "
-                      f"scaled by {cfg.h_q}/{heads}"}
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()) or "none"
+    heads = kept["q"].shape[2]
+    q, k, v = (kept[n].astype(np.float64) for n in ("q", "k", "v"))
+    rows = list(range(0, cfg.seqlen, row_stride))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kc = oracle.compress_kv(k, kept["w"], cfg.block)
+        vc = oracle.compress_kv(v, kept["w"], cfg.block)
+        t_comp = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.hca_attention(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale, rows=rows)
+        t_attn = time.perf_counter() - t0
+    est = (t_comp + t_attn * cfg.seqlen / len(rows)) * cfg.h_q / heads
+    return {"value": cfg.seqlen / est, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle on {heads} of {cfg.h_q} heads of the {cfg.seqlen}-token prefill: "
+                      f"compression of every block ({t_comp:.1f}s) and attention for every {row_stride}th "
+                      f"query row ({len(rows)} rows, {t_attn:.1f}s), scaled to all rows and heads "
+                      f"(estimated {est:.0f}s for the whole step)",
+            "cpu_model": _cpu_model(), "blas": blas, "threads": 1}
 
 
 def main():
@@ -460,8 +514,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c3,c4,c5,c5d,csa,epi,bwd",
-                    help="comma list of workloads to run (c2 always runs; 'copy' runs only the counter calibration copy)")
+    ap.add_argument("--only", default="c2,c4,c5,c5d,csa,epi,bwd",
+                    help="comma list of component workloads to run besides the headline step (c3 always runs; "
+                         "'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -491,45 +546,50 @@ def main():
         return
     comps = {}
 
-    c2 = synth.CONFIGS["c2"]
-    r2 = bench_prefill(torch, hca, synth, c2, args.steps, args.warmup)
-    f2, b2 = prefill_work(c2)
-    comps["hca_prefill_32k"] = {
-        "compress_ms": r2["compress_ms"], "attn_ms": r2["attn_ms"],
-        "attn_tflops": f2 / r2["attn_ms"] / 1e9, "attn_mfma_frac": f2 / r2["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
-        "attn_gbs": b2 / r2["attn_ms"] / 1e6, "attn_hbm_frac": b2 / r2["attn_ms"] / 1e6 / PEAK_HBM_GBS,
-        "compress_gbs": compress_bytes(c2) / r2["compress_ms"] / 1e6,
+    c3 = synth.CONFIGS["c3"]
+    steps3 = max(20, args.steps)
+    r3 = bench_prefill(torch, hca, synth, c3, steps3, max(2, args.warmup),
+                       keep_heads=() if args.no_cpu_baseline else (0,))
+    f3, b3 = prefill_work(c3)
+    comps["hca_prefill_128k"] = {
+        "compress_ms": r3["compress_ms"], "attn_ms": r3["attn_ms"], "e2e_ms": r3["step_ms"],
+        "attn_mean_ms": r3["attn_mean_ms"], "timed_steps": steps3,
+        "tokens_per_s": c3.seqlen / r3["step_ms"] * 1e3,
+        "attn_tflops": f3 / r3["attn_ms"] / 1e9, "attn_mfma_frac": f3 / r3["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+        "attn_gbs": b3 / r3["attn_ms"] / 1e6,
+        "compress_gbs": compress_bytes(c3) / r3["compress_ms"] / 1e6,
+        "compress_hbm_frac": compress_bytes(c3) / r3["compress_ms"] / 1e6 / PEAK_HBM_GBS,
     }
-    log(f"[bench] c2 done: {comps['hca_prefill_32k']}")
+    log(f"[bench] c3 done: {comps['hca_prefill_128k']}")
 
-    if "c3" in only:
-        c3 = synth.CONFIGS["c3"]
-        r3 = bench_prefill(torch, hca, synth, c3, max(3, args.steps // 4), 2)
-        f3, b3 = prefill_work(c3)
-        e2e = r3["compress_ms"] + r3["attn_ms"]
-        comps["hca_prefill_128k"] = {
-            "compress_ms": r3["compress_ms"], "attn_ms": r3["attn_ms"], "e2e_ms": e2e,
-            "tokens_per_s": c3.seqlen / e2e * 1e3,
-            "attn_tflops": f3 / r3["attn_ms"] / 1e9, "attn_mfma_frac": f3 / r3["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
-            "attn_gbs": b3 / r3["attn_ms"] / 1e6,
-            "compress_gbs": compress_bytes(c3) / r3["compress_ms"] / 1e6,
-            "compress_hbm_frac": compress_bytes(c3) / r3["compress_ms"] / 1e6 / PEAK_HBM_GBS,
+    if "c2" in only:
+        c2 = synth.CONFIGS["c2"]
+        r2 = bench_prefill(torch, hca, synth, c2, max(20, args.steps), args.warmup)
+        f2, b2 = prefill_work(c2)
+        comps["hca_prefill_32k"] = {
+            "compress_ms": r2["compress_ms"], "attn_ms": r2["attn_ms"], "e2e_ms": r2["step_ms"],
+            "tokens_per_s": c2.seqlen / r2["step_ms"] * 1e3,
+            "attn_tflops": f2 / r2["attn_ms"] / 1e9, "attn_mfma_frac": f2 / r2["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+            "attn_gbs": b2 / r2["attn_ms"] / 1e6, "attn_hbm_frac": b2 / r2["attn_ms"] / 1e6 / PEAK_HBM_GBS,
+            "attn_traffic_bytes": measured_traffic("prefill512_kernel", "hca_prefill_32k"),
+            "compress_gbs": compress_bytes(c2) / r2["compress_ms"] / 1e6,
         }
-        log(f"[bench] c3 done: {comps['hca_prefill_128k']}")
+        log(f"[bench] c2 done: {comps['hca_prefill_32k']}")
     if "c4" in only:
         c4 = synth.CONFIGS["c4"]
-        r4 = bench_decode(torch, hca, synth, c4, args.steps, args.warmup)
+        r4 = bench_decode(torch, hca, synth, c4, max(20, args.steps), args.warmup)
         f4, b4 = decode_work(c4)
         comps["hca_decode_1m"] = {
-            "ms": r4["ms"], "ms_event_per_call": r4["ms_event_per_call"],
+            "ms": r4["ms"], "ms_mean": r4["ms_mean"], "ms_back_to_back": r4["ms_back_to_back"],
             "gbs": b4 / r4["ms"] / 1e6, "hbm_frac": b4 / r4["ms"] / 1e6 / PEAK_HBM_GBS,
+            "hbm_frac_back_to_back": b4 / r4["ms_back_to_back"] / 1e6 / PEAK_HBM_GBS,
             "tokens_per_s": c4.batch / r4["ms"] * 1e3, "tflops": f4 / r4["ms"] / 1e9,
             "append_call_us": r4["append_call_us"], "append_close_call_us": r4["append_close_call_us"],
         }
         log(f"[bench] c4 done: {comps['hca_decode_1m']}")
     if "c5" in only:
         c5 = synth.CONFIGS["c5"]
-        r5 = bench_dsa(torch, hca, synth, c5, max(2, args.steps // 5), 1)
+        r5 = bench_dsa(torch, hca, synth, c5, max(5, args.steps // 4), 1)
         fi, fa, sel = dsa_work(c5)
         tot = r5["index_topk_ms"] + r5["attn_ms"]
         comps["dsa_prefill_64k"] = {
@@ -540,12 +600,12 @@ def main():
         }
         log(f"[bench] c5 done: {comps['dsa_prefill_64k']}")
     if "c5d" in only:
-        comps["dsa_decode_1m"] = bench_dsa_decode(torch, hca, args.steps, args.warmup)
+        comps["dsa_decode_1m"] = bench_dsa_decode(torch, hca, max(20, args.steps), args.warmup)
         log(f"[bench] c5d done: {comps['dsa_decode_1m']}")
 
     if "csa" in only:
         cc = synth.CSA_CONFIGS["csa64k"]
-        rc = bench_csa(torch, hca, synth, cc, max(2, args.steps // 5), 1)
+        rc = bench_csa(torch, hca, synth, cc, max(5, args.steps // 4), 1)
         fi_c, fa_c, sel_c = csa_work(cc)
         tot = rc["compress_ms"] + rc["index_topk_ms"] + rc["attn_ms"]
         comps["csa_prefill_64k"] = {
@@ -557,10 +617,11 @@ def main():
         }
         log(f"[bench] csa done: {comps['csa_prefill_64k']}")
     if "epi" in only:
-        comps["attn_epilogue_32k"] = bench_epilogue(torch, hca, args.steps, args.warmup)
+        comps["attn_epilogue_32k"] = bench_epilogue(torch, hca, max(20, args.steps), args.warmup)
         log(f"[bench] epilogue done: {comps['attn_epilogue_32k']}")
     if "bwd" in only:
-        rb = bench_backward(torch, hca, synth, c2, max(3, args.steps // 2), 2)
+        c2 = synth.CONFIGS["c2"]
+        rb = bench_backward(torch, hca, synth, c2, max(10, args.steps // 2), 2)
         fb, bb = backward_work(c2)
         comps["hca_backward_32k"] = {
             "attn_bwd_ms": rb["attn_bwd_ms"], "layer_bwd_ms": rb["layer_bwd_ms"],
@@ -573,24 +634,29 @@ def main():
         }
         log(f"[bench] bwd done: {comps['hca_backward_32k']}")
 
-    value = c2.seqlen / r2["step_ms"] * 1e3
-    achieved = b2 / r2["attn_ms"] / 1e6
+    value = c3.seqlen / r3["step_ms"] * 1e3
+    achieved = f3 / r3["attn_mean_ms"] / 1e9
     line = {
         "metric": "HCA prefill tokens/s + TFLOP/s (% MFMA peak); decode GB/s (% HBM peak)",
-        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": r2["step_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps3, "warmup": max(2, args.warmup),
+        "ms_per_step": r3["step_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "HCA prefill bf16: batch 1, seq 32768, 16 heads, head_dim 512, block 128, "
-                               "window 128; step = hca_compress_kv + hca_attn_fwd",
-                   "global_batch": 1, "seq_len": c2.seqlen, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "prefill512_kernel", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic("prefill512_kernel"),
-                     "algorithmic_bytes_per_launch": b2, "launch_ms": r2["attn_ms"]},
+        "config": {"workload": "HCA prefill bf16: batch 1, seq 131072, 16 heads, head_dim 512, block 128 "
+                               "(1024 compressed entries), window 256; step = hca_compress_kv over the whole "
+                               "sequence + hca_attn_fwd",
+                   "global_batch": 1, "seq_len": c3.seqlen, "parallelism": "none (1 GPU)",
+                   "timing": "median of per-step HIP-event durations, Infinity Cache flushed before each step",
+                   "wall_ms_per_step_incl_flush": r3["wall_ms_per_step_incl_flush"]},
+        "roofline": {"bound": "mfma", "kernel": "prefill512_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("prefill512_kernel", "hca_prefill_128k"),
+                     "algorithmic_flops_per_launch": f3, "algorithmic_bytes_per_launch": b3,
+                     "launch_ms_mean": r3["attn_mean_ms"], "launch_ms_median": r3["attn_ms"]},
         "components": comps,
     }
     if not args.no_cpu_baseline:
         t0 = time.time()
-        line["cpu_baseline"] = cpu_baseline(synth, c2)
+        line["cpu_baseline"] = cpu_baseline(c3, r3["kept"])
         log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
     print(json.dumps(line), flush=True)
 

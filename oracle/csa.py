@@ -23,7 +23,8 @@ compressor and the DSA indexer as defined in ``hca.py`` and ``dsa.py``):
   index keys, s(t, j) = sum_h w[t, h] * max(0, <qI[t, h], kIc[j]>), and the
   DSA ranking (float32 decision, the smaller entry index wins a tie).
 * Attention: softmax over the selected entries' compressed keys, times their
-  compressed values (one shared K/V head as in DSA).  A position with no
+  compressed values (query head h reads KV head h // (H_q / H_kv); the
+  workload has one shared K/V head as in DSA).  A position with no
   complete block yet (t < block - 1) selects nothing: o = 0, lse = -inf.
 """
 from __future__ import annotations
@@ -58,9 +59,14 @@ def csa_index_topk(qI, kIc, w, k: int, block: int, rows=None) -> np.ndarray:
 
 def csa_attention(q, kc, vc, idx, scale: float):
     """o [B, S, Hq, dv], lse [B, Hq, S]: attention of each query over the entries listed in its
-    row of idx (-1 skipped); a row listing none gives o = 0, lse = -inf.  One K/V head."""
+    row of idx (-1 skipped); a row listing none gives o = 0, lse = -inf.  Query head h reads
+    KV head h // (Hq / Hkv)."""
     q = np.asarray(q, dtype=np.float64)
     B, S, Hq, _ = q.shape
+    Hkv = kc.shape[2]
+    if Hq % Hkv or vc.shape[2] != Hkv:
+        raise ValueError("query heads must be a multiple of the KV heads")
+    group = Hq // Hkv
     dv = vc.shape[3]
     o = np.zeros((B, S, Hq, dv))
     lse = np.full((B, Hq, S), -np.inf)
@@ -70,14 +76,16 @@ def csa_attention(q, kc, vc, idx, scale: float):
             sel = sel[sel >= 0]
             if sel.size == 0:
                 continue
-            keys = np.asarray(kc[b, sel, 0], dtype=np.float64)
-            vals = np.asarray(vc[b, sel, 0], dtype=np.float64)
-            logits = scale * (q[b, t] @ keys.T)                    # [Hq, n]
-            m = logits.max(axis=1, keepdims=True)
-            p = np.exp(logits - m)
-            den = p.sum(axis=1, keepdims=True)
-            o[b, t] = (p @ vals) / den
-            lse[b, :, t] = (m + np.log(den))[:, 0]
+            for g in range(Hkv):
+                hs = slice(g * group, (g + 1) * group)
+                keys = np.asarray(kc[b, sel, g], dtype=np.float64)
+                vals = np.asarray(vc[b, sel, g], dtype=np.float64)
+                logits = scale * (q[b, t, hs] @ keys.T)            # [group, n]
+                m = logits.max(axis=1, keepdims=True)
+                p = np.exp(logits - m)
+                den = p.sum(axis=1, keepdims=True)
+                o[b, t, hs] = (p @ vals) / den
+                lse[b, hs, t] = (m + np.log(den))[:, 0]
     return o, lse
 
 

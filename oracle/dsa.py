@@ -18,7 +18,8 @@ Readings of what the pages leave open:
   ranking.  The order inside a row's index list is unspecified; this oracle
   returns it ascending and pads with -1.
 * Attention: softmax(scale * <q[t, h], k[u]>) over the selected u, times v[u];
-  one shared K/V head (MQA).
+  query head h reads KV head h // (H_q / H_kv) (the DSA workload has one
+  shared K/V head, MQA).
 """
 from __future__ import annotations
 
@@ -57,8 +58,15 @@ def index_topk(qI, kI, w, k: int, rows=None) -> np.ndarray:
 
 
 def sparse_attention(q, k, v, idx, scale: float, rows=None):
-    """o [B, len(rows), Hq, dv], lse [B, Hq, len(rows)] over the positions listed in idx (-1 skipped)."""
+    """o [B, len(rows), Hq, dv], lse [B, Hq, len(rows)] over the positions listed in idx (-1 skipped).
+
+    Query head h reads KV head h // (Hq / Hkv) (one shared head, MQA, in the
+    DSA workload; grouped heads otherwise)."""
     B, S, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv or v.shape[2] != Hkv:
+        raise ValueError("query heads must be a multiple of the KV heads")
+    group = Hq // Hkv
     dv = v.shape[3]
     rows = list(range(S)) if rows is None else [int(r) for r in rows]
     o = np.zeros((B, len(rows), Hq, dv))
@@ -67,15 +75,17 @@ def sparse_attention(q, k, v, idx, scale: float, rows=None):
         for ri, t in enumerate(rows):
             sel = np.asarray(idx[b, ri] if idx.shape[1] == len(rows) else idx[b, t])
             sel = sel[sel >= 0]
-            keys = np.asarray(k[b, sel, 0], dtype=np.float64)
-            vals = np.asarray(v[b, sel, 0], dtype=np.float64)
             qt = np.asarray(q[b, t], dtype=np.float64)              # [Hq, d]
-            logits = scale * (qt @ keys.T)                          # [Hq, n]
-            m = logits.max(axis=1, keepdims=True)
-            p = np.exp(logits - m)
-            den = p.sum(axis=1, keepdims=True)
-            o[b, ri] = (p @ vals) / den
-            lse[b, :, ri] = (m + np.log(den))[:, 0]
+            for g in range(Hkv):
+                hs = slice(g * group, (g + 1) * group)
+                keys = np.asarray(k[b, sel, g], dtype=np.float64)
+                vals = np.asarray(v[b, sel, g], dtype=np.float64)
+                logits = scale * (qt[hs] @ keys.T)                  # [group, n]
+                m = logits.max(axis=1, keepdims=True)
+                p = np.exp(logits - m)
+                den = p.sum(axis=1, keepdims=True)
+                o[b, ri, hs] = (p @ vals) / den
+                lse[b, hs, ri] = (m + np.log(den))[:, 0]
     return o, lse
 
 

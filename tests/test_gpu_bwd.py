@@ -331,3 +331,57 @@ def test_dsa_training_step_bf16_chain(S, topk):
     rq, rk, rv = oracle.sparse_attention_bwd(f64(q, True), f64(k, True), f64(v, True), idx, scale, f64(dout, True))
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check(name, g, r, BF16_TOL)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_backward_c2_shape():
+    """The backward calls the benchmark times, at their shape (32768 tokens, 16
+    heads x 512, block 128, window 128; the c2 inputs plus a seeded dO): one
+    head's gradients checked in full against the oracle (every dq row, every raw
+    K/V row, every compressed entry, the compressor weights), and dq of sampled
+    rows on two more heads.  With MHA, head h only meets KV head h, so the
+    one-head oracle is exact for that head."""
+    cfg = synth.CONFIGS["c2"]
+    _say("full-size backward", cfg)
+    inp = synth.make_prefill(cfg)
+    dout = synth.make_normal((cfg.batch, cfg.seqlen, cfg.h_q, cfg.head_dim), cfg.seed + 1, cfg.std, bf16=True)
+    kw = dict(window=cfg.window, block=cfg.block, scale=cfg.scale)
+    qd, kd, vd, gd = (dev_bf16(x) for x in (inp["q"], inp["k"], inp["v"], dout))
+    wd = dev_f32(inp["w"])
+    kcd, vcd = hca.hca_compress_kv(kd, vd, wd, wd, cfg.block)
+    o, lse = hca.hca_attn_fwd(qd, kd, vd, kcd, vcd, **kw)
+    attn = hca.hca_attn_bwd(qd, kd, vd, kcd, vcd, o, lse, gd, **kw)
+    layer = hca.hca_attn_compress_bwd(qd, kd, vd, kcd, vcd, o, lse, gd, wd, wd, **kw)
+    torch.cuda.synchronize()
+    del qd, kd, vd, gd, kcd, vcd, o, lse
+    h = 5
+    q, k, v, g = (f64(x[:, :, [h]], True) for x in (inp["q"], inp["k"], inp["v"], dout))
+    wh = inp["w"][[h]]
+    kc, vc = oracle.compress_kv(k, wh, cfg.block), oracle.compress_kv(v, wh, cfg.block)
+    rq, rk, rv, rkc, rvc = oracle.hca_attention_bwd(q, k, v, kc, vc, g, **kw)
+    ck, rwk = oracle.compress_kv_bwd(k, wh, rkc, cfg.block)
+    cv, rwv = oracle.compress_kv_bwd(v, wh, rvc, cfg.block)
+    sl = lambda t: t[:, :, h:h + 1]
+    for name, got, ref in (("dq", sl(attn[0]), rq), ("dk", sl(attn[1]), rk), ("dv", sl(attn[2]), rv),
+                           ("dkc", sl(attn[3]), rkc), ("dvc", sl(attn[4]), rvc)):
+        _check("attn " + name, got, ref, BF16_TOL)
+    dq, dk, dv, dkc, dvc, dwk, dwv = layer
+    for name, got, ref in (("dq", sl(dq), rq), ("dk", sl(dk), rk + ck), ("dv", sl(dv), rv + cv),
+                           ("dkc", sl(dkc), rkc), ("dvc", sl(dvc), rvc),
+                           ("dw_k", dwk[h:h + 1], rwk), ("dw_v", dwv[h:h + 1], rwv)):
+        _check("layer " + name, got, ref, BF16_TOL)
+    # dq of sampled rows on two more heads
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 127, 128, 255, 256, 16383, cfg.seqlen - 1]) | set(rng.integers(0, cfg.seqlen, 8).tolist()))
+    for h2 in (0, cfg.h_q - 1):
+        q2, k2, v2, g2 = (f64(x[:, :, h2], True)[0] for x in (inp["q"], inp["k"], inp["v"], dout))
+        kc2 = oracle.compress_kv(k2[None, :, None], inp["w"][[h2]], cfg.block)[0, :, 0]
+        vc2 = oracle.compress_kv(v2[None, :, None], inp["w"][[h2]], cfg.block)[0, :, 0]
+        ref = np.zeros((len(rows), cfg.head_dim))
+        for i, t in enumerate(rows):
+            lo, n_c = oracle.window_bounds(t, cfg.window, cfg.block)
+            keys = np.concatenate([kc2[:n_c], k2[lo:t + 1]])
+            vals = np.concatenate([vc2[:n_c], v2[lo:t + 1]])
+            ref[i] = oracle.attend_row_bwd(q2[t], keys, vals, cfg.scale, g2[t])[0]
+        _check(f"dq head {h2} sampled rows", attn[0][0, rows, h2], ref, BF16_TOL)
+        _check(f"layer dq head {h2} sampled rows", dq[0, rows, h2], ref, BF16_TOL)

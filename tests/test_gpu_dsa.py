@@ -275,29 +275,35 @@ def test_sparse_attention_rows_longer_than_2048():
 
 @pytest.mark.timeout(900)
 def test_full_size_dsa_sampled():
+    """c5 at full size (65536 positions, top-2048, 64 heads x 256) in the launch
+    configuration the benchmark times.  The sampled rows are made tie-free
+    first (their qI and w redrawn from their own sub-streams, which touches no
+    other row), so every sampled index set must equal the oracle's exactly."""
     cfg = synth.CONFIGS["c5"]
     _say("full-size", cfg)
     inp = synth.make_dsa(cfg)
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 2046, 2047, 2048, 2049, 5000, 40000, cfg.seqlen - 1]) |
+                  set(rng.integers(0, cfg.seqlen, 12).tolist()))
+    for attempt in range(1, 13):
+        bad = [(0, t) for t in rows
+               if not oracle.tie_free_row(inp["qI"][0, t], inp["kI"][0], inp["w"][0, t], t, cfg.topk)]
+        if not bad:
+            break
+        synth.redraw_dsa_rows(inp, bad, attempt)
+    assert not bad, "could not make the sampled rows tie-free"
+    _say(f"  sampled rows redrawn: {int((inp['redraws'][0, rows] > 0).sum())} of {len(rows)}")
     q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
     qI, kI, w = dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"])
     idx = hca.dsa_index_topk(qI, kI, w, cfg.topk)
     o, lse = hca.dsa_sparse_attn_fwd(q, k, v, idx, scale=cfg.scale)
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
-    rng = np.random.default_rng(3)
-    rows = sorted(set([0, 1, 2046, 2047, 2048, 2049, 5000, 40000, cfg.seqlen - 1]) |
-                  set(rng.integers(0, cfg.seqlen, 12).tolist()))
-    n_exact = 0
-    for t in rows:
-        got = idx_np[0, t]
-        if oracle.tie_free_row(inp["qI"][0, t], inp["kI"][0], inp["w"][0, t], t, cfg.topk):
-            ref = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], cfg.topk, rows=[t])[0, 0]
-            v_ = np.sort(got[got >= 0])
-            assert np.array_equal(np.concatenate([v_, np.full(cfg.topk - v_.size, -1)]), ref), t
-            n_exact += 1
-        else:
-            assert oracle.valid_topk_row(got, inp["qI"][0, t], inp["kI"][0], inp["w"][0, t], t, cfg.topk), t
-    _say(f"  {n_exact}/{len(rows)} sampled rows tie-free and exact")
+    got = _sorted_rows(idx_np[:, rows])
+    ref = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], cfg.topk, rows=rows)
+    for i, t in enumerate(rows):
+        assert np.array_equal(got[0, i], ref[0, i]), t
+    _say(f"  {len(rows)}/{len(rows)} sampled rows exact")
     ro, rlse = oracle.sparse_attention(f64(inp["q"][:, rows], True)[:, :, :, :], f64(inp["k"], True),
                                        f64(inp["v"], True), idx_np[:, rows], cfg.scale,
                                        rows=list(range(len(rows))))

@@ -96,6 +96,31 @@ def test_k_covering_every_entry_is_dense_block_causal_attention():
     assert (o[0, : block - 1] == 0).all() and np.isneginf(lse[0, :, : block - 1]).all()
 
 
+def test_csa_attention_grouped_heads_against_torch():
+    """Grouped KV heads: query head h attends over KV head h // (Hq / Hkv) of the
+    listed entries; with every visible entry listed this is torch's attention
+    under the block-causal mask, per KV group."""
+    rng = np.random.default_rng(31)
+    S, Hq, Hkv, d, block = 22, 4, 2, 8, 4
+    n = S // block
+    q = rng.standard_normal((1, S, Hq, d))
+    kc = rng.standard_normal((1, n, Hkv, d))
+    vc = rng.standard_normal((1, n, Hkv, d))
+    idx = np.full((1, S, n + 2), -1, dtype=np.int32)
+    for t in range(S):
+        m = (t + 1) // block
+        idx[0, t, :m] = rng.permutation(m)
+    o, lse = oracle.csa_attention(q, kc, vc, idx, 0.3)
+    mask = torch.tensor([[block * j + block - 1 <= t for j in range(n)] for t in range(S)])
+    rows = [t for t in range(S) if t >= block - 1]
+    qt = torch.from_numpy(q[0]).permute(1, 0, 2)[:, rows]                  # [Hq, rows, d]
+    kt = torch.from_numpy(np.repeat(kc[0], Hq // Hkv, axis=1)).permute(1, 0, 2)  # [Hq, n, d]
+    vt = torch.from_numpy(np.repeat(vc[0], Hq // Hkv, axis=1)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[rows][None], scale=0.3)
+    np.testing.assert_allclose(o[0, rows].transpose(1, 0, 2), ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert (o[0, : block - 1] == 0).all() and np.isneginf(lse[0, :, : block - 1]).all()
+
+
 def test_tie_free_rows_reduce_to_dsa_on_the_visible_prefix():
     qI, kIc, w = _inputs(block=4)
     for t in range(qI.shape[1]):

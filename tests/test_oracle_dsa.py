@@ -102,6 +102,33 @@ def test_k_at_least_context_is_dense_causal_mqa():
     np.testing.assert_allclose(lse, rl.numpy(), atol=1e-12)
 
 
+def test_k_at_least_context_is_dense_causal_gqa():
+    """Grouped KV heads (Hq = 6 on Hkv = 3): query head h must read KV head
+    h // 2.  With k >= context the selection is every past position, so each
+    head's output is torch's causal attention against its own KV head."""
+    rng = np.random.default_rng(21)
+    B, S, Hq, Hkv, d = 2, 20, 6, 3, 8
+    q = rng.standard_normal((B, S, Hq, d))
+    k = rng.standard_normal((B, S, Hkv, d))
+    v = rng.standard_normal((B, S, Hkv, d))
+    idx = np.full((B, S, S + 3), -1, dtype=np.int32)
+    for t in range(S):
+        idx[:, t, : t + 1] = rng.permutation(t + 1)
+    o, lse = oracle.sparse_attention(q, k, v, idx, 0.35)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=2)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=2)).permute(0, 2, 1, 3)
+    ro = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.35)
+    np.testing.assert_allclose(o, ro.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    logits = (qt @ kt.transpose(-1, -2)) * 0.35
+    rl = torch.logsumexp(logits.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), -math.inf), -1)
+    np.testing.assert_allclose(lse, rl.numpy(), atol=1e-12)
+    # heads of one group share keys: swapping the KV heads changes the outputs of exactly the affected groups
+    o2, _ = oracle.sparse_attention(q, k[:, :, [1, 0, 2]], v[:, :, [1, 0, 2]], idx, 0.35)
+    assert not np.allclose(o2[:, :, :4], o[:, :, :4])
+    np.testing.assert_allclose(o2[:, :, 4:], o[:, :, 4:], atol=0)
+
+
 def test_sparse_attention_ignores_index_order_and_padding():
     rng = np.random.default_rng(14)
     q = rng.standard_normal((1, 3, 2, 8))

@@ -155,3 +155,17 @@ def test_gate_applied_before_mixing(monkeypatch):
 def test_gate_tanh_for_sigmoid(monkeypatch):
     monkeypatch.setattr(oepi, "sigmoid", lambda x: np.tanh(np.asarray(x, dtype=np.float64)))
     _expect_caught([tepi.test_gate_closed_forms, tepi.test_gate_against_explicit_loops_and_torch])
+
+
+def test_sparse_attention_every_head_reads_kv_head_zero(monkeypatch):
+    """The MQA shortcut (every query head reading KV head 0) must fail the
+    grouped-head pin."""
+    real = odsa.sparse_attention
+
+    def bad(q, k, v, idx, scale, rows=None):
+        Hq = q.shape[2]
+        k0 = np.repeat(np.asarray(k)[:, :, :1], k.shape[2], axis=2)
+        v0 = np.repeat(np.asarray(v)[:, :, :1], v.shape[2], axis=2)
+        return real(q, k0, v0, idx, scale, rows)
+    monkeypatch.setattr(oracle, "sparse_attention", bad)
+    _expect_caught([tdsa.test_k_at_least_context_is_dense_causal_gqa])
