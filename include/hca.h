@@ -177,6 +177,37 @@ hca_status_t hca_attn_fwd(hca_dtype_t dt,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * hca_attn_fwd_noalloc -- hca_attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, semantics, validation and kernels as
+ * hca_attn_fwd, without the workspace: the decode path's split partials go to
+ * a fixed device array inside the library (HCA_NOALLOC_SCRATCH_BYTES, 16 MiB;
+ * one copy per GPU, held from library load until the process exits).  The call allocates and frees nothing; the caller still passes q,
+ * k, v, kc, vc, o and lse.  Every fully written partial is consumed by the
+ * same call, so nothing needs clearing between calls.
+ * Calls that overlap on one GPU (two streams, or two threads) race on that
+ * array and must be serialized by the caller.
+ * Errors: as hca_attn_fwd; HCA_ERR_WORKSPACE (checked first) when
+ * hca_attn_fwd_workspace_size(batch, seqlen_q, h_q, h_kv, head_dim, n_blocks,
+ * window) exceeds the array (the c4 decode shape -- 64 sequences, 16 heads on
+ * one KV head, 8192 + 128 keys -- needs 8.4 MB).
+ */
+#define HCA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+hca_status_t hca_attn_fwd_noalloc(hca_dtype_t dt,
+                                  const void* q, hca_strides_t sq,
+                                  const void* k, hca_strides_t sk,
+                                  const void* v, hca_strides_t sv,
+                                  const void* kc, hca_strides_t skc,
+                                  const void* vc, hca_strides_t svc,
+                                  void* o, hca_strides_t so,
+                                  float* lse,
+                                  int batch, int seqlen_q, int64_t q_pos0,
+                                  int seqlen_kv, int64_t kv_pos0, int n_blocks,
+                                  int h_q, int h_kv, int head_dim, int block, int window, float scale,
+                                  void* stream);
+
 /* Workspace bytes dsa_index_topk needs (score rows for one chunk of queries). */
 size_t dsa_index_topk_workspace_size(int batch, int seqlen, int topk);
 

@@ -32,6 +32,7 @@ EXPORTS = (
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
     "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd", "attn_output_epilogue",
+    "hca_attn_fwd_noalloc",
 )
 
 
@@ -71,6 +72,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hca_attn_fwd.restype = I
     lib.hca_attn_fwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P,
                                  I, I, I64, I, I64, I, I, I, I, I, I, F, P, SZ, P]
+    lib.hca_attn_fwd_noalloc.restype = I
+    lib.hca_attn_fwd_noalloc.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, S, P,
+                                         I, I, I64, I, I64, I, I, I, I, I, I, F, P]
     lib.dsa_index_topk_workspace_size.restype = SZ
     lib.dsa_index_topk_workspace_size.argtypes = [I, I, I]
     lib.dsa_index_topk.restype = I
@@ -223,6 +227,28 @@ def hca_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional
                             window, float(scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                             _stream()))
     return o, lse
+
+
+HCA_NOALLOC_SCRATCH_BYTES = 16 << 20   # the fixed scratch array of hca_attn_fwd_noalloc (include/hca.h)
+
+
+def hca_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc: Optional[torch.Tensor],
+                         vc: Optional[torch.Tensor], o: torch.Tensor, lse: Optional[torch.Tensor], *, window: int,
+                         block: int, scale: Optional[float] = None, q_pos0: int = 0, kv_pos0: int = 0) -> None:
+    """hca_attn_fwd writing into the given o (and lse, may be None) with the
+    library's fixed scratch array instead of a workspace; allocates nothing."""
+    lib = load_library()
+    _dev(q, k, v, kc, vc, o, lse)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    nb = 0 if kc is None else kc.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    zs = Strides(0, 0, 0)
+    _check(lib.hca_attn_fwd_noalloc(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                    _ptr(kc), zs if kc is None else _strides(kc), _ptr(vc),
+                                    zs if vc is None else _strides(vc), _ptr(o), _strides(o), _ptr(lse), B, Sq,
+                                    q_pos0, Skv, kv_pos0, nb, Hq, Hkv, d, block, window, float(scale), _stream()))
 
 
 def dsa_index_topk_workspace_size(batch: int, seqlen: int, topk: int) -> int:

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/hca.h"
@@ -351,6 +352,62 @@ hca_status_t hca_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
   hipError_t e = hca::launch_attn_generic(a, st);
   if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd launch");
   return HCA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// hca_attn_fwd_noalloc: hca_attn_fwd with the decode kernel's split partials in
+// a fixed device array instead of a caller workspace.  The array is a
+// file-scope __device__ object, so every GPU the library runs on holds its own
+// copy from module load until the process ends; its device address is looked
+// up once per device (with that device current) and only that address is ever
+// passed to kernels.  No memory is allocated or freed by the call.
+constexpr size_t kNoAllocScratchBytes = HCA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on first use).
+hca_status_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HCA_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess) return hip_fail(s.err, "hca_attn_fwd_noalloc: hipGetSymbolAddress(scratch)");
+  if (!s.ptr) return fail(HCA_ERR_HIP, "hca_attn_fwd_noalloc: scratch has no device address");
+  *out = s.ptr;
+  return HCA_OK;
+}
+}  // namespace
+
+hca_status_t hca_attn_fwd_noalloc(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
+                                  const void* v, hca_strides_t sv, const void* kc, hca_strides_t skc, const void* vc,
+                                  hca_strides_t svc, void* o, hca_strides_t so, float* lse, int batch, int seqlen_q,
+                                  int64_t q_pos0, int seqlen_kv, int64_t kv_pos0, int n_blocks, int h_q, int h_kv,
+                                  int head_dim, int block, int window, float scale, void* stream) {
+  // the scratch need is an upper bound from the sizes alone (0 for every path
+  // but the bf16 / head_dim 512 decode); it is checked before anything else
+  const size_t need = dt == HCA_DTYPE_BF16
+                          ? hca_attn_fwd_workspace_size(batch, seqlen_q, h_q, h_kv, head_dim, n_blocks, window)
+                          : 0;
+  if (need > kNoAllocScratchBytes)
+    return fail(HCA_ERR_WORKSPACE,
+                "hca_attn_fwd_noalloc: these sizes need %zu bytes of scratch, beyond its fixed %zu bytes; "
+                "use hca_attn_fwd with a workspace",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need) HCA_TRY(scratch_ptr(&ws));
+  return hca_attn_fwd(dt, q, sq, k, sk, v, sv, kc, skc, vc, svc, o, so, lse, batch, seqlen_q, q_pos0, seqlen_kv,
+                      kv_pos0, n_blocks, h_q, h_kv, head_dim, block, window, scale, ws,
+                      need ? kNoAllocScratchBytes : 0, stream);
 }
 
 size_t dsa_index_topk_workspace_size(int batch, int seqlen, int topk) {

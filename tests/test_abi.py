@@ -332,3 +332,17 @@ def test_epilogue_rejects_bad_arguments():
     assert call(r=0) == hca.HCA_ERR_INVALID
     assert call(y=FAKE) == hca.HCA_ERR_INVALID                     # y aliases o
     assert call(b=2, sc=S(2048 * 101, 2048, 2048)) == hca.HCA_ERR_UNSUPPORTED   # c not token-contiguous
+
+
+def test_noalloc_rejects_oversized_scratch_before_touching_the_gpu():
+    """hca_attn_fwd_noalloc checks its fixed scratch size first: 512 decode
+    sequences x 16 heads over 8320 keys need more than 16 MiB of partials."""
+    lib = _lib()
+    B, Hq, nb, W, d = 512, 16, 8192, 128, 512
+    assert lib.hca_attn_fwd_workspace_size(B, 1, Hq, 1, d, nb, W) > hca.HCA_NOALLOC_SCRATCH_BYTES
+    st = lib.hca_attn_fwd_noalloc(1, FAKE, S(Hq * d, Hq * d, d), FAKE, S(W * d, d, d), FAKE, S(W * d, d, d),
+                                  FAKE, S(nb * d, d, d), FAKE, S(nb * d, d, d), ctypes.c_void_p(1 << 40),
+                                  S(Hq * d, Hq * d, d), None, B, 1, 128 * nb + W - 1, W, 128 * nb, nb, Hq, 1, d,
+                                  128, W, 0.04, None)
+    assert st == hca.HCA_ERR_WORKSPACE
+    assert "scratch" in hca.hca_last_error()
