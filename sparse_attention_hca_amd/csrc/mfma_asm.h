@@ -17,6 +17,13 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// dma16 with one wait state ahead of the load: an LDS DMA reads M0, which the
+// compiler writes right before the asm, and an M0 write needs a wait state
+// before an LDS DMA.
+__device__ __forceinline__ void dma16_m0(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
 // The two products are written as inline asm so that S^T accumulates in VGPRs
 // (the softmax reads it) while O^T accumulates in AGPRs: O^T takes all 256
 // AGPRs, and the compiler would otherwise put every MFMA accumulator in AGPRs
