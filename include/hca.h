@@ -51,7 +51,15 @@ typedef enum {
   HCA_ERR_HIP = 4          /* a HIP runtime or launch error; the HIP text is in hca_last_error() */
 } hca_status_t;
 
-typedef enum { HCA_DTYPE_F32 = 0, HCA_DTYPE_BF16 = 1 } hca_dtype_t;
+/* The two range markers are not dtypes: they give the type every 32-bit value,
+ * so an unknown value a caller passes is rejected (HCA_ERR_INVALID) instead of
+ * being an out-of-range enum inside the C++ library. */
+typedef enum {
+  HCA_DTYPE_F32 = 0,
+  HCA_DTYPE_BF16 = 1,
+  HCA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  HCA_DTYPE_RANGE_MAX_ = 0x7fffffff
+} hca_dtype_t;
 
 /* Element strides of a [batch, seq, head, dim] tensor whose dim axis is contiguous. */
 typedef struct {

@@ -40,14 +40,26 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 struct Range {
   uintptr_t lo, hi;
 };
-Range extent(const void* p, hca_strides_t st, int64_t b, int64_t s, int64_t h, int64_t d, size_t es) {
-  const int64_t last = (b - 1) * st.batch + (s - 1) * st.seq + (h - 1) * st.head + d;
-  return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * (int64_t)es)};
+// Tensors may span at most 2^56 bytes: beyond any device memory, and small
+// enough that every offset a kernel forms fits int64 without overflow.
+constexpr __int128 kMaxSpan = (__int128)1 << 56;
+__int128 span_bytes(hca_strides_t st, int64_t b, int64_t s, int64_t h, int64_t d, size_t es) {
+  if (b <= 0 || s <= 0 || h <= 0 || d <= 0) return 0;
+  const __int128 last = (__int128)(b - 1) * st.batch + (__int128)(s - 1) * st.seq + (__int128)(h - 1) * st.head + d;
+  return last * (__int128)es;
 }
+// Only called on tensors that passed check_tensor / check_flat, whose span fits.
+Range extent(const void* p, hca_strides_t st, int64_t b, int64_t s, int64_t h, int64_t d, size_t es) {
+  return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)span_bytes(st, b, s, h, d, es)};
+}
+Range flat_extent(const void* p, int64_t n, size_t es) { return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es}; }
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Strides must be non-negative multiples of 16 bytes (the kernels use 16-byte vectors).
-hca_status_t check_tensor(const char* name, const void* p, hca_strides_t st, size_t es, bool nullable = false) {
+// [b, s, h, d] is the tensor's shape; its byte span must stay below 2^56 and
+// must not wrap the address space.
+hca_status_t check_tensor(const char* name, const void* p, hca_strides_t st, int64_t b, int64_t s, int64_t h,
+                          int64_t d, size_t es, bool nullable = false) {
   if (!p) {
     if (nullable) return HCA_OK;
     return fail(HCA_ERR_INVALID, "%s is NULL", name);
@@ -56,6 +68,19 @@ hca_status_t check_tensor(const char* name, const void* p, hca_strides_t st, siz
   const int64_t q = (int64_t)(16 / es);
   if (st.batch < 0 || st.seq < 0 || st.head < 0 || st.batch % q || st.seq % q || st.head % q)
     return fail(HCA_ERR_INVALID, "%s strides must be non-negative multiples of 16 bytes", name);
+  const __int128 span = span_bytes(st, b, s, h, d, es);
+  if (span > kMaxSpan || (__int128)(uintptr_t)p + span > (__int128)UINTPTR_MAX)
+    return fail(HCA_ERR_INVALID, "%s spans more than 2^56 bytes (or wraps the address space)", name);
+  return HCA_OK;
+}
+
+// A contiguous tensor of n elements of es bytes (n computed by the caller in 128 bits).
+hca_status_t check_flat(const char* name, const void* p, __int128 n, size_t es, unsigned align) {
+  if (!p) return fail(HCA_ERR_INVALID, "%s is NULL", name);
+  if ((uintptr_t)p % align) return fail(HCA_ERR_INVALID, "%s is not %u-byte aligned", name, align);
+  const __int128 span = n * (__int128)es;
+  if (n < 0 || span > kMaxSpan || (__int128)(uintptr_t)p + span > (__int128)UINTPTR_MAX)
+    return fail(HCA_ERR_INVALID, "%s spans more than 2^56 bytes (or wraps the address space)", name);
   return HCA_OK;
 }
 
@@ -94,20 +119,26 @@ static hca_status_t attn_bwd_impl(const char* fn, hca_dtype_t dt, const void* q,
     return fail(HCA_ERR_UNSUPPORTED, "positions beyond 2^30 are not supported");
   if (head_dim > 512 || head_dim % 4) return fail(HCA_ERR_UNSUPPORTED, "%s: head_dim must be <= 512, a multiple of 4", fn);
   if (!(scale == scale)) return fail(HCA_ERR_INVALID, "scale is NaN");
-  if (!lse || ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is NULL or not 4-byte aligned");
   const size_t es = elem_size(dt);
-  HCA_TRY(check_tensor("q", q, sq, es));
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("kc", kc, skc, es, n_blocks == 0));
-  HCA_TRY(check_tensor("vc", vc, svc, es, n_blocks == 0));
-  HCA_TRY(check_tensor("o", o, so, es));
-  HCA_TRY(check_tensor("dout", dout, sdo, es));
-  HCA_TRY(check_tensor("dq", dq, sdq, 4));
-  HCA_TRY(check_tensor("dk", dk, sdk, 4));
-  HCA_TRY(check_tensor("dv", dv, sdv, 4));
-  HCA_TRY(check_tensor("dkc", dkc, sdkc, 4, n_blocks == 0));
-  HCA_TRY(check_tensor("dvc", dvc, sdvc, 4, n_blocks == 0));
+  HCA_TRY(check_tensor("q", q, sq, batch, seqlen_q, h_q, head_dim, es));
+  HCA_TRY(check_tensor("k", k, sk, batch, seqlen_kv, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("v", v, sv, batch, seqlen_kv, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("kc", kc, skc, batch, n_blocks, h_kv, head_dim, es, n_blocks == 0));
+  HCA_TRY(check_tensor("vc", vc, svc, batch, n_blocks, h_kv, head_dim, es, n_blocks == 0));
+  HCA_TRY(check_tensor("o", o, so, batch, seqlen_q, h_q, head_dim, es));
+  HCA_TRY(check_tensor("dout", dout, sdo, batch, seqlen_q, h_q, head_dim, es));
+  HCA_TRY(check_tensor("dq", dq, sdq, batch, seqlen_q, h_q, head_dim, 4));
+  HCA_TRY(check_tensor("dk", dk, sdk, batch, seqlen_kv, h_kv, head_dim, 4));
+  HCA_TRY(check_tensor("dv", dv, sdv, batch, seqlen_kv, h_kv, head_dim, 4));
+  HCA_TRY(check_tensor("dkc", dkc, sdkc, batch, n_blocks, h_kv, head_dim, 4, n_blocks == 0));
+  HCA_TRY(check_tensor("dvc", dvc, sdvc, batch, n_blocks, h_kv, head_dim, 4, n_blocks == 0));
+  HCA_TRY(check_flat("lse", lse, (__int128)batch * h_q * seqlen_q, 4, 4));
+  if (w_k) {
+    HCA_TRY(check_flat("w_k", w_k, (__int128)h_kv * block, 4, 4));
+    HCA_TRY(check_flat("w_v", w_v, (__int128)h_kv * block, 4, 4));
+    HCA_TRY(check_flat("dw_k", dw_k, (__int128)h_kv * block, 4, 4));
+    HCA_TRY(check_flat("dw_v", dw_v, (__int128)h_kv * block, 4, 4));
+  }
   const int64_t t0 = q_pos0, t1 = q_pos0 + seqlen_q - 1;
   const int64_t lo0 = t0 - window + 1 > 0 ? t0 - window + 1 : 0;
   const int64_t lo1 = t1 - window + 1 > 0 ? t1 - window + 1 : 0;
@@ -130,11 +161,28 @@ static hca_status_t attn_bwd_impl(const char* fn, hca_dtype_t dt, const void* q,
                           n_blocks ? extent(vc, svc, batch, n_blocks, h_kv, head_dim, es) : Range{0, 0},
                           extent(o, so, batch, seqlen_q, h_q, head_dim, es),
                           extent(dout, sdo, batch, seqlen_q, h_q, head_dim, es)};
+    const Range rl = flat_extent(lse, (int64_t)batch * h_q * seqlen_q, 4);
     for (int x = 0; x < 5; ++x) {
       for (int y = 0; y < 7; ++y)
         if (overlaps(outs[x], ins[y])) return fail(HCA_ERR_INVALID, "%s: a gradient overlaps an input", fn);
+      if (overlaps(outs[x], rl)) return fail(HCA_ERR_INVALID, "%s: a gradient overlaps lse", fn);
       for (int y = x + 1; y < 5; ++y)
         if (overlaps(outs[x], outs[y])) return fail(HCA_ERR_INVALID, "%s: gradients overlap each other", fn);
+    }
+    if (w_k) {
+      // the compressor weights' gradients against each other, the weights and every other gradient
+      const int64_t nw = (int64_t)h_kv * block;
+      const Range rw[4] = {flat_extent(w_k, nw, 4), flat_extent(w_v, nw, 4), flat_extent(dw_k, nw, 4),
+                           flat_extent(dw_v, nw, 4)};
+      for (int y = 2; y < 4; ++y) {
+        for (int x = 0; x < 5; ++x)
+          if (overlaps(outs[x], rw[y])) return fail(HCA_ERR_INVALID, "%s: gradients overlap", fn);
+        for (int x = 0; x < 4; ++x)
+          if (x != y && overlaps(rw[x], rw[y])) return fail(HCA_ERR_INVALID, "%s: weight gradients overlap", fn);
+        for (int x = 0; x < 7; ++x)
+          if (overlaps(ins[x], rw[y])) return fail(HCA_ERR_INVALID, "%s: a weight gradient overlaps an input", fn);
+        if (overlaps(rl, rw[y])) return fail(HCA_ERR_INVALID, "%s: a weight gradient overlaps lse", fn);
+      }
     }
   }
   const size_t need = hca::hca_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen_q, q_pos0, n_blocks,
@@ -177,10 +225,10 @@ hca_status_t hca_compress_kv(hca_dtype_t dt, const void* k, hca_strides_t sk, co
   if (!w_k || !w_v) return fail(HCA_ERR_INVALID, "compressor weights are NULL");
   const size_t es = elem_size(dt);
   const int nb = seqlen / block;
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("kc", kc, skc, es, nb == 0));
-  HCA_TRY(check_tensor("vc", vc, svc, es, nb == 0));
+  HCA_TRY(check_tensor("k", k, sk, batch, seqlen, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("v", v, sv, batch, seqlen, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("kc", kc, skc, batch, nb, h_kv, head_dim, es, nb == 0));
+  HCA_TRY(check_tensor("vc", vc, svc, batch, nb, h_kv, head_dim, es, nb == 0));
   if (nb == 0) return HCA_OK;  // no complete block: nothing to write
   if (nb > 0) {
     const Range rk = extent(k, sk, batch, seqlen, h_kv, head_dim, es), rv = extent(v, sv, batch, seqlen, h_kv, head_dim, es);
@@ -215,12 +263,12 @@ hca_status_t hca_append_kv(hca_dtype_t dt, const void* k_new, hca_strides_t skn,
                 (long long)t, (long long)j, n_blocks);
   if (closes && (!w_k || !w_v)) return fail(HCA_ERR_INVALID, "compressor weights are NULL");
   const size_t es = elem_size(dt);
-  HCA_TRY(check_tensor("k_new", k_new, skn, es));
-  HCA_TRY(check_tensor("v_new", v_new, svn, es));
-  HCA_TRY(check_tensor("k_ring", k_ring, skr, es));
-  HCA_TRY(check_tensor("v_ring", v_ring, svr, es));
-  HCA_TRY(check_tensor("kc", kc, skc, es, !closes));
-  HCA_TRY(check_tensor("vc", vc, svc, es, !closes));
+  HCA_TRY(check_tensor("k_new", k_new, skn, batch, 1, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("v_new", v_new, svn, batch, 1, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("k_ring", k_ring, skr, batch, 2 * (int64_t)ring, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("v_ring", v_ring, svr, batch, 2 * (int64_t)ring, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("kc", kc, skc, batch, n_blocks, h_kv, head_dim, es, !closes));
+  HCA_TRY(check_tensor("vc", vc, svc, batch, n_blocks, h_kv, head_dim, es, !closes));
   {
     const Range rkn = extent(k_new, skn, batch, 1, h_kv, head_dim, es), rvn = extent(v_new, svn, batch, 1, h_kv, head_dim, es);
     const Range rkr = extent(k_ring, skr, batch, 2 * (int64_t)ring, h_kv, head_dim, es);
@@ -280,13 +328,13 @@ hca_status_t hca_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
     return fail(HCA_ERR_UNSUPPORTED, "positions beyond 2^30 are not supported");
   if (!(scale == scale)) return fail(HCA_ERR_INVALID, "scale is NaN");
   const size_t es = elem_size(dt);
-  HCA_TRY(check_tensor("q", q, sq, es));
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("kc", kc, skc, es, n_blocks == 0));
-  HCA_TRY(check_tensor("vc", vc, svc, es, n_blocks == 0));
-  HCA_TRY(check_tensor("o", o, so, es));
-  if (lse && ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is not 4-byte aligned");
+  HCA_TRY(check_tensor("q", q, sq, batch, seqlen_q, h_q, head_dim, es));
+  HCA_TRY(check_tensor("k", k, sk, batch, seqlen_kv, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("v", v, sv, batch, seqlen_kv, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("kc", kc, skc, batch, n_blocks, h_kv, head_dim, es, n_blocks == 0));
+  HCA_TRY(check_tensor("vc", vc, svc, batch, n_blocks, h_kv, head_dim, es, n_blocks == 0));
+  HCA_TRY(check_tensor("o", o, so, batch, seqlen_q, h_q, head_dim, es));
+  if (lse) HCA_TRY(check_flat("lse", lse, (__int128)batch * h_q * seqlen_q, 4, 4));
   // every query's window must be inside the raw K/V and its compressed entries inside kc/vc
   const int64_t t0 = q_pos0, t1 = q_pos0 + seqlen_q - 1;
   const int64_t lo0 = t0 - window + 1 > 0 ? t0 - window + 1 : 0;
@@ -309,7 +357,7 @@ hca_status_t hca_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
                          overlaps(ro, extent(vc, svc, batch, n_blocks, h_kv, head_dim, es))))
       return fail(HCA_ERR_INVALID, "o overlaps an input");
     if (lse) {
-      const Range rl{(uintptr_t)lse, (uintptr_t)(lse + (size_t)batch * h_q * seqlen_q)};
+      const Range rl = flat_extent(lse, (int64_t)batch * h_q * seqlen_q, 4);
       if (overlaps(rl, ro) || overlaps(rl, ins[0]) || overlaps(rl, ins[1]) || overlaps(rl, ins[2]))
         return fail(HCA_ERR_INVALID, "lse overlaps another tensor");
     }
@@ -426,11 +474,12 @@ hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float*
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(idx))
     return fail(HCA_ERR_INVALID, "dsa_index_topk: tensors must be 16-byte aligned");
   if (h_i % 4) return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk: h_i must be a multiple of 4");
+  if ((int64_t)batch * seqlen > kPosLimit)
+    return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk: more than 2^30 positions over the batch");
   {
-    const Range ri{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)};
-    const Range rq{(uintptr_t)q_idx, (uintptr_t)(q_idx + (size_t)batch * seqlen * h_i * d_i)};
-    const Range rk{(uintptr_t)k_idx, (uintptr_t)(k_idx + (size_t)batch * seqlen * d_i)};
-    const Range rw{(uintptr_t)w_idx, (uintptr_t)(w_idx + (size_t)batch * seqlen * h_i)};
+    const int64_t n = (int64_t)batch * seqlen;
+    const Range ri = flat_extent(idx, n * topk, 4), rq = flat_extent(q_idx, n * h_i * d_i, 4);
+    const Range rk = flat_extent(k_idx, n * d_i, 4), rw = flat_extent(w_idx, n * h_i, 4);
     if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(ri, rw))
       return fail(HCA_ERR_INVALID, "dsa_index_topk: idx overlaps an input");
   }
@@ -482,22 +531,6 @@ hca_status_t hca_attn_compress_bwd(hca_dtype_t dt, const void* q, hca_strides_t 
     return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: weights must be 4-byte aligned");
   if (block >= 1 && n_blocks >= 0 && (int64_t)n_blocks * block > seqlen)
     return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: n_blocks * block exceeds seqlen");
-  {
-    const Range rw[4] = {Range{(uintptr_t)w_k, (uintptr_t)(w_k + (size_t)h_kv * block)},
-                         Range{(uintptr_t)w_v, (uintptr_t)(w_v + (size_t)h_kv * block)},
-                         Range{(uintptr_t)dw_k, (uintptr_t)(dw_k + (size_t)h_kv * block)},
-                         Range{(uintptr_t)dw_v, (uintptr_t)(dw_v + (size_t)h_kv * block)}};
-    if (overlaps(rw[2], rw[3]) || overlaps(rw[0], rw[2]) || overlaps(rw[0], rw[3]) || overlaps(rw[1], rw[2]) ||
-        overlaps(rw[1], rw[3]))
-      return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: weight gradients overlap");
-    if (batch > 0 && seqlen > 0 && h_q > 0 && h_kv > 0 && head_dim > 0) {
-      const Range outs[3] = {extent(dq, sdq, batch, seqlen, h_q, head_dim, 4), extent(dk, sdk, batch, seqlen, h_kv, head_dim, 4),
-                             extent(dv, sdv, batch, seqlen, h_kv, head_dim, 4)};
-      for (int x = 0; x < 3; ++x)
-        for (int y = 2; y < 4; ++y)
-          if (overlaps(outs[x], rw[y])) return fail(HCA_ERR_INVALID, "hca_attn_compress_bwd: gradients overlap");
-    }
-  }
   return attn_bwd_impl("hca_attn_compress_bwd", dt, q, sq, k, sk, v, sv, kc, skc, vc, svc, o, so, lse, dout, sdo, dq,
                        sdq, dk, sdk, dv, sdv, dkc, sdkc, dvc, sdvc, batch, seqlen, 0, seqlen, 0, n_blocks, h_q, h_kv,
                        head_dim, block, window, scale, workspace, workspace_bytes, stream, w_k, w_v, dw_k, dw_v);
@@ -516,16 +549,17 @@ hca_status_t hca_compress_kv_bwd(hca_dtype_t dt, const void* k, hca_strides_t sk
   if (!w_k || !w_v || !dw_k || !dw_v) return fail(HCA_ERR_INVALID, "hca_compress_kv_bwd: weights or their gradients are NULL");
   const size_t es = elem_size(dt);
   const int nb = seqlen / block;
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("dkc", dkc, sdkc, 4, nb == 0));
-  HCA_TRY(check_tensor("dvc", dvc, sdvc, 4, nb == 0));
-  HCA_TRY(check_tensor("dk", dk, sdk, 4));
-  HCA_TRY(check_tensor("dv", dv, sdv, 4));
+  HCA_TRY(check_tensor("k", k, sk, batch, seqlen, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("v", v, sv, batch, seqlen, h_kv, head_dim, es));
+  HCA_TRY(check_tensor("dkc", dkc, sdkc, batch, nb, h_kv, head_dim, 4, nb == 0));
+  HCA_TRY(check_tensor("dvc", dvc, sdvc, batch, nb, h_kv, head_dim, 4, nb == 0));
+  HCA_TRY(check_tensor("dk", dk, sdk, batch, seqlen, h_kv, head_dim, 4));
+  HCA_TRY(check_tensor("dv", dv, sdv, batch, seqlen, h_kv, head_dim, 4));
+  HCA_TRY(check_flat("dw_k", dw_k, (__int128)h_kv * block, 4, 4));
+  HCA_TRY(check_flat("dw_v", dw_v, (__int128)h_kv * block, 4, 4));
   {
     const Range rdk = extent(dk, sdk, batch, seqlen, h_kv, head_dim, 4), rdv = extent(dv, sdv, batch, seqlen, h_kv, head_dim, 4);
-    const Range rw{(uintptr_t)dw_k, (uintptr_t)(dw_k + (size_t)h_kv * block)};
-    const Range rw2{(uintptr_t)dw_v, (uintptr_t)(dw_v + (size_t)h_kv * block)};
+    const Range rw = flat_extent(dw_k, (int64_t)h_kv * block, 4), rw2 = flat_extent(dw_v, (int64_t)h_kv * block, 4);
     if (overlaps(rdk, rdv) || overlaps(rw, rw2) || overlaps(rdk, rw) || overlaps(rdk, rw2) || overlaps(rdv, rw) ||
         overlaps(rdv, rw2))
       return fail(HCA_ERR_INVALID, "hca_compress_kv_bwd: gradients overlap each other");
@@ -559,25 +593,25 @@ hca_status_t dsa_sparse_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq
   if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q must be a multiple of h_kv");
   if (d_qk > 512 || d_v > 512 || d_qk % 4 || d_v % 4 || topk > 4096)
     return fail(HCA_ERR_UNSUPPORTED, "dsa_sparse_attn_bwd: needs d_qk, d_v <= 512 (multiples of 4), topk <= 4096");
-  if (!idx || !aligned16(idx)) return fail(HCA_ERR_INVALID, "idx is NULL or not 16-byte aligned");
-  if (!lse || ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is NULL or not 4-byte aligned");
+  HCA_TRY(check_flat("idx", idx, (__int128)batch * seqlen * topk, 4, 16));
+  HCA_TRY(check_flat("lse", lse, (__int128)batch * h_q * seqlen, 4, 4));
   if (!(scale == scale)) return fail(HCA_ERR_INVALID, "scale is NaN");
   const size_t es = elem_size(dt);
-  HCA_TRY(check_tensor("q", q, sq, es));
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("o", o, so, es));
-  HCA_TRY(check_tensor("dout", dout, sdo, es));
-  HCA_TRY(check_tensor("dq", dq, sdq, 4));
-  HCA_TRY(check_tensor("dk", dk, sdk, 4));
-  HCA_TRY(check_tensor("dv", dv, sdv, 4));
+  HCA_TRY(check_tensor("q", q, sq, batch, seqlen, h_q, d_qk, es));
+  HCA_TRY(check_tensor("k", k, sk, batch, seqlen, h_kv, d_qk, es));
+  HCA_TRY(check_tensor("v", v, sv, batch, seqlen, h_kv, d_v, es));
+  HCA_TRY(check_tensor("o", o, so, batch, seqlen, h_q, d_v, es));
+  HCA_TRY(check_tensor("dout", dout, sdo, batch, seqlen, h_q, d_v, es));
+  HCA_TRY(check_tensor("dq", dq, sdq, batch, seqlen, h_q, d_qk, 4));
+  HCA_TRY(check_tensor("dk", dk, sdk, batch, seqlen, h_kv, d_qk, 4));
+  HCA_TRY(check_tensor("dv", dv, sdv, batch, seqlen, h_kv, d_v, 4));
   {
     const Range outs[3] = {extent(dq, sdq, batch, seqlen, h_q, d_qk, 4), extent(dk, sdk, batch, seqlen, h_kv, d_qk, 4),
                            extent(dv, sdv, batch, seqlen, h_kv, d_v, 4)};
     const Range ins[6] = {extent(q, sq, batch, seqlen, h_q, d_qk, es), extent(k, sk, batch, seqlen, h_kv, d_qk, es),
                           extent(v, sv, batch, seqlen, h_kv, d_v, es), extent(o, so, batch, seqlen, h_q, d_v, es),
                           extent(dout, sdo, batch, seqlen, h_q, d_v, es),
-                          Range{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)}};
+                          flat_extent(idx, (int64_t)batch * seqlen * topk, 4)};
     for (int x = 0; x < 3; ++x) {
       for (int y = 0; y < 6; ++y)
         if (overlaps(outs[x], ins[y])) return fail(HCA_ERR_INVALID, "dsa_sparse_attn_bwd: a gradient overlaps an input");
@@ -614,14 +648,13 @@ hca_status_t sparse_attn(const char* name, hca_dtype_t dt, const void* q, hca_st
   if (batch <= 0 || seqlen_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
     return fail(HCA_ERR_INVALID, "%s: sizes must be positive", name);
   if (h_q % h_kv) return fail(HCA_ERR_INVALID, "h_q must be a multiple of h_kv");
-  if (!idx) return fail(HCA_ERR_INVALID, "idx is NULL");
-  if (!aligned16(idx)) return fail(HCA_ERR_INVALID, "idx is not 16-byte aligned");
+  HCA_TRY(check_flat("idx", idx, (__int128)batch * seqlen_q * topk, 4, 16));
   const size_t es = elem_size(dt);
-  HCA_TRY(check_tensor("q", q, sq, es));
-  HCA_TRY(check_tensor("k", k, sk, es));
-  HCA_TRY(check_tensor("v", v, sv, es));
-  HCA_TRY(check_tensor("o", o, so, es));
-  if (lse && ((uintptr_t)lse & 3u)) return fail(HCA_ERR_INVALID, "lse is not 4-byte aligned");
+  HCA_TRY(check_tensor("q", q, sq, batch, seqlen_q, h_q, d_qk, es));
+  HCA_TRY(check_tensor("k", k, sk, batch, n_kv, h_kv, d_qk, es));
+  HCA_TRY(check_tensor("v", v, sv, batch, n_kv, h_kv, d_v, es));
+  HCA_TRY(check_tensor("o", o, so, batch, seqlen_q, h_q, d_v, es));
+  if (lse) HCA_TRY(check_flat("lse", lse, (__int128)batch * h_q * seqlen_q, 4, 4));
   if (dt != HCA_DTYPE_BF16 || d_qk != 256 || d_v != 256 || (h_q / h_kv) % 64 || topk > 4096)
     return fail(HCA_ERR_UNSUPPORTED, "%s: needs bf16, d_qk = d_v = 256, h_q/h_kv a multiple of 64, topk <= 4096",
                 name);
@@ -630,7 +663,8 @@ hca_status_t sparse_attn(const char* name, hca_dtype_t dt, const void* q, hca_st
     if (overlaps(ro, extent(q, sq, batch, seqlen_q, h_q, d_qk, es)) ||
         overlaps(ro, extent(k, sk, batch, n_kv, h_kv, d_qk, es)) ||
         overlaps(ro, extent(v, sv, batch, n_kv, h_kv, d_v, es)) ||
-        overlaps(ro, Range{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen_q * topk)}))
+        overlaps(ro, flat_extent(idx, (int64_t)batch * seqlen_q * topk, 4)) ||
+        (lse && overlaps(ro, flat_extent(lse, (int64_t)batch * h_q * seqlen_q, 4))))
       return fail(HCA_ERR_INVALID, "o overlaps an input");
   }
   hipError_t e = hca::launch_dsa_sparse_attn256(q, ls(sq), k, ls(sk), v, ls(sv), idx, o, ls(so), lse, batch, seqlen_q,
@@ -679,11 +713,12 @@ hca_status_t csa_index_topk(const float* q_idx, const float* k_idx, const float*
                 "csa_index_topk: needs h_i 4 or 8, d_i a multiple of 16 <= 128, topk <= 4096");
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(idx))
     return fail(HCA_ERR_INVALID, "csa_index_topk: tensors must be 16-byte aligned");
+  if ((int64_t)batch * seqlen > kPosLimit || (int64_t)batch * n_entries > kPosLimit)
+    return fail(HCA_ERR_UNSUPPORTED, "csa_index_topk: more than 2^30 positions over the batch");
   {
-    const Range ri{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * seqlen * topk)};
-    const Range rq{(uintptr_t)q_idx, (uintptr_t)(q_idx + (size_t)batch * seqlen * h_i * d_i)};
-    const Range rk{(uintptr_t)k_idx, (uintptr_t)(k_idx + (size_t)batch * n_entries * d_i)};
-    const Range rw{(uintptr_t)w_idx, (uintptr_t)(w_idx + (size_t)batch * seqlen * h_i)};
+    const int64_t n = (int64_t)batch * seqlen;
+    const Range ri = flat_extent(idx, n * topk, 4), rq = flat_extent(q_idx, n * h_i * d_i, 4);
+    const Range rk = flat_extent(k_idx, (int64_t)batch * n_entries * d_i, 4), rw = flat_extent(w_idx, n * h_i, 4);
     if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(ri, rw))
       return fail(HCA_ERR_INVALID, "csa_index_topk: idx overlaps an input");
   }
@@ -716,20 +751,20 @@ hca_status_t attn_output_epilogue(hca_dtype_t dt, const void* o, hca_strides_t s
                 "attn_output_epilogue: needs h in {8, 16, 32, 64}, r <= 16, d_c a multiple of 32, "
                 "h * d_v a multiple of 256, d_v a multiple of 8 and <= 512");
   if ((int64_t)batch * seqlen > kPosLimit) return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: too many tokens");
-  if (!w_g || !aligned16(w_g)) return fail(HCA_ERR_INVALID, "w_g is NULL or not 16-byte aligned");
-  if (!u || !v || ((uintptr_t)u & 3u) || ((uintptr_t)v & 3u)) return fail(HCA_ERR_INVALID, "u, v NULL or misaligned");
-  HCA_TRY(check_tensor("o", o, so, 2));
-  HCA_TRY(check_tensor("c", c, sc, 2));
-  HCA_TRY(check_tensor("y", y, sy, 2));
+  HCA_TRY(check_flat("w_g", w_g, (__int128)h * d_v * d_c, 2, 16));
+  HCA_TRY(check_flat("u", u, (__int128)h * r, 4, 4));
+  HCA_TRY(check_flat("v", v, (__int128)h * r, 4, 4));
+  HCA_TRY(check_tensor("o", o, so, batch, seqlen, h, d_v, 2));
+  HCA_TRY(check_tensor("c", c, sc, batch, seqlen, 1, d_c, 2));
+  HCA_TRY(check_tensor("y", y, sy, batch, seqlen, h, d_v, 2));
   if (batch > 1 && (sc.batch != (int64_t)seqlen * sc.seq || sy.batch != (int64_t)seqlen * sy.seq))
     return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: c and y must be token-contiguous across the batch "
                                      "(batch stride = seqlen * seq stride)");
   {
     const Range ry = extent(y, sy, batch, seqlen, h, d_v, 2);
     if (overlaps(ry, extent(o, so, batch, seqlen, h, d_v, 2)) || overlaps(ry, extent(c, sc, batch, seqlen, 1, d_c, 2)) ||
-        overlaps(ry, Range{(uintptr_t)w_g, (uintptr_t)((const uint16_t*)w_g + (size_t)h * d_v * d_c)}) ||
-        overlaps(ry, Range{(uintptr_t)u, (uintptr_t)(u + (size_t)h * r)}) ||
-        overlaps(ry, Range{(uintptr_t)v, (uintptr_t)(v + (size_t)h * r)}))
+        overlaps(ry, flat_extent(w_g, (int64_t)h * d_v * d_c, 2)) || overlaps(ry, flat_extent(u, (int64_t)h * r, 4)) ||
+        overlaps(ry, flat_extent(v, (int64_t)h * r, 4)))
       return fail(HCA_ERR_INVALID, "attn_output_epilogue: y overlaps an input");
   }
   hipError_t e = hca::launch_attn_output_epilogue(o, ls(so), c, sc.seq, w_g, u, v, y, ls(sy), batch, seqlen, h, d_v,
@@ -755,11 +790,11 @@ hca_status_t dsa_index_topk_decode(const float* q_idx, const float* k_idx, const
   if (n_keys >= (1 << 30)) return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk_decode: n_keys must be below 2^30");
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(idx))
     return fail(HCA_ERR_INVALID, "dsa_index_topk_decode: tensors must be 16-byte aligned");
+  if ((int64_t)batch * n_keys > kPosLimit)
+    return fail(HCA_ERR_UNSUPPORTED, "dsa_index_topk_decode: more than 2^30 keys over the batch");
   {
-    const Range ri{(uintptr_t)idx, (uintptr_t)(idx + (size_t)batch * topk)};
-    const Range rq{(uintptr_t)q_idx, (uintptr_t)(q_idx + (size_t)batch * h_i * d_i)};
-    const Range rk{(uintptr_t)k_idx, (uintptr_t)(k_idx + (size_t)batch * n_keys * d_i)};
-    const Range rw{(uintptr_t)w_idx, (uintptr_t)(w_idx + (size_t)batch * h_i)};
+    const Range ri = flat_extent(idx, (int64_t)batch * topk, 4), rq = flat_extent(q_idx, (int64_t)batch * h_i * d_i, 4);
+    const Range rk = flat_extent(k_idx, (int64_t)batch * n_keys * d_i, 4), rw = flat_extent(w_idx, (int64_t)batch * h_i, 4);
     if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(ri, rw))
       return fail(HCA_ERR_INVALID, "dsa_index_topk_decode: idx overlaps an input");
   }
