@@ -17,8 +17,7 @@
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers on the current HIP device, owned by
  *     the caller.  The library never allocates or frees memory and keeps no
- *     pointer after a call returns (one exception: attn_output_epilogue's
- *     per-device hipBLASLt handle, see there).  Scratch memory is passed in
+ *     pointer after a call returns.  Scratch memory is passed in
  *     as a caller-owned workspace whose size is given by the
  *     *_workspace_size() queries.
  *   - Tensors are batch/sequence/head/dim with the dim axis contiguous
@@ -386,18 +385,12 @@ hca_status_t csa_sparse_attn_fwd(hca_dtype_t dt,
  *   w_g: [h * d_v, d_c] bf16 contiguous (the [out, in] layout of a linear layer)
  *   u  : [h, r] fp32 contiguous; v: [r, h] fp32 contiguous
  *   y  : [batch, seqlen, h, d_v] bf16 (written; must not overlap an input)
- * c and y must be token-contiguous across the batch (batch stride = seqlen *
- * seq stride).  The gate projection runs on the matrix cores (fp32
- * accumulation) and its pre-activation is stored in y as bf16; the mixing
- * kernel applies the sigmoid (fp32) and scales y in place.  When each token's
- * heads are contiguous in y (head stride = d_v) the projection is a hipBLASLt
- * GEMM: the first call on a device creates a hipBLASLt handle for it (kept
- * until the process exits; hipBLASLt may allocate device memory for it), and
- * the first call per shape picks the algorithm (no workspace).  Other y
- * layouts, or a shape hipBLASLt has no algorithm for, use the library's own
- * GEMM kernel.
+ * One kernel: the gate projection runs on the matrix cores (bf16 operands,
+ * fp32 accumulation) and its epilogue applies the sigmoid, the head mixing
+ * and the product in fp32 before the single bf16 rounding of y; the gate
+ * pre-activations never reach memory.
  * Supported: bf16, h in {8, 16, 32, 64}, r <= 16, d_c a multiple of 32,
- * h * d_v a multiple of 256, d_v a multiple of 8 and at most 512.
+ * d_v a multiple of 256 / h.
  */
 hca_status_t attn_output_epilogue(hca_dtype_t dt,
                                   const void* o, hca_strides_t so,

@@ -746,10 +746,10 @@ hca_status_t attn_output_epilogue(hca_dtype_t dt, const void* o, hca_strides_t s
   if (dt != HCA_DTYPE_BF16) return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: bf16 only");
   if (batch <= 0 || seqlen <= 0 || h <= 0 || d_v <= 0 || d_c <= 0 || r <= 0)
     return fail(HCA_ERR_INVALID, "attn_output_epilogue: sizes must be positive");
-  if (!(h == 8 || h == 16 || h == 32 || h == 64) || r > 16 || d_c % 32 || (h * d_v) % 256 || d_v % 8 || d_v > 512)
+  if (!(h == 8 || h == 16 || h == 32 || h == 64) || r > 16 || d_c % 32 || d_v % (256 / h))
     return fail(HCA_ERR_UNSUPPORTED,
                 "attn_output_epilogue: needs h in {8, 16, 32, 64}, r <= 16, d_c a multiple of 32, "
-                "h * d_v a multiple of 256, d_v a multiple of 8 and <= 512");
+                "d_v a multiple of 256 / h");
   if ((int64_t)batch * seqlen > kPosLimit) return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: too many tokens");
   HCA_TRY(check_flat("w_g", w_g, (__int128)h * d_v * d_c, 2, 16));
   HCA_TRY(check_flat("u", u, (__int128)h * r, 4, 4));
@@ -757,9 +757,6 @@ hca_status_t attn_output_epilogue(hca_dtype_t dt, const void* o, hca_strides_t s
   HCA_TRY(check_tensor("o", o, so, batch, seqlen, h, d_v, 2));
   HCA_TRY(check_tensor("c", c, sc, batch, seqlen, 1, d_c, 2));
   HCA_TRY(check_tensor("y", y, sy, batch, seqlen, h, d_v, 2));
-  if (batch > 1 && (sc.batch != (int64_t)seqlen * sc.seq || sy.batch != (int64_t)seqlen * sy.seq))
-    return fail(HCA_ERR_UNSUPPORTED, "attn_output_epilogue: c and y must be token-contiguous across the batch "
-                                     "(batch stride = seqlen * seq stride)");
   {
     const Range ry = extent(y, sy, batch, seqlen, h, d_v, 2);
     if (overlaps(ry, extent(o, so, batch, seqlen, h, d_v, 2)) || overlaps(ry, extent(c, sc, batch, seqlen, 1, d_c, 2)) ||
@@ -767,8 +764,8 @@ hca_status_t attn_output_epilogue(hca_dtype_t dt, const void* o, hca_strides_t s
         overlaps(ry, flat_extent(v, (int64_t)h * r, 4)))
       return fail(HCA_ERR_INVALID, "attn_output_epilogue: y overlaps an input");
   }
-  hipError_t e = hca::launch_attn_output_epilogue(o, ls(so), c, sc.seq, w_g, u, v, y, ls(sy), batch, seqlen, h, d_v,
-                                                  d_c, r, (hipStream_t)stream);
+  hipError_t e = hca::launch_attn_output_epilogue(o, ls(so), c, sc.batch, sc.seq, w_g, u, v, y, ls(sy), batch, seqlen,
+                                                  h, d_v, d_c, r, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_output_epilogue launch");
   return HCA_OK;
 }

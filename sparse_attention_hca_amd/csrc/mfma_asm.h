@@ -58,6 +58,11 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// dma4 with the wait state an M0 write needs before an LDS DMA (see dma16_m0).
+__device__ __forceinline__ void dma4_m0(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
 // Transposing LDS read of the A operand of a 32x32x16 step whose rows are the
 // contiguous axis of a row-major LDS tile: `p` already holds the lane offset
 // (see the kernels); the second half comes from 8 rows further down.

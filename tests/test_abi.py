@@ -328,10 +328,11 @@ def test_epilogue_rejects_bad_arguments():
     assert call(h=12) == hca.HCA_ERR_UNSUPPORTED
     assert call(r=17) == hca.HCA_ERR_UNSUPPORTED
     assert call(dc=2000) == hca.HCA_ERR_UNSUPPORTED
-    assert call(dv=1024) == hca.HCA_ERR_UNSUPPORTED
+    assert call(dv=40) == hca.HCA_ERR_UNSUPPORTED                  # not a multiple of 256 / h = 16
+    assert call(h=8, dv=48) == hca.HCA_ERR_UNSUPPORTED             # not a multiple of 256 / h = 32
     assert call(r=0) == hca.HCA_ERR_INVALID
     assert call(y=FAKE) == hca.HCA_ERR_INVALID                     # y aliases o
-    assert call(b=2, sc=S(2048 * 101, 2048, 2048)) == hca.HCA_ERR_UNSUPPORTED   # c not token-contiguous
+    assert call(y=ctypes.c_void_p((1 << 37) + 8)) == hca.HCA_ERR_INVALID   # y misaligned
 
 
 def test_noalloc_rejects_oversized_scratch_before_touching_the_gpu():

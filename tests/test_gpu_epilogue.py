@@ -71,9 +71,9 @@ def test_epilogue_strided_output_of_attention():
     assert rel_err(host(y), ref) < BF16_TOL
 
 
-def test_epilogue_head_strided_output_uses_the_mfma_gemm():
-    """y whose heads are not contiguous within a token (head stride 2 d_v)
-    takes the hand-written gate GEMM instead of the library one."""
+def test_epilogue_head_strided_output():
+    """y whose heads are not contiguous within a token (head stride 2 d_v):
+    only the addressed half is written."""
     B, S, H, dv, dc, r = 1, 300, 16, 256, 512, 4
     o, c, w, u, v = _inputs(B, S, H, dv, dc, r, 505)
     big = torch.zeros(B, S, H, 2 * dv, dtype=torch.bfloat16, device="cuda:0")
@@ -82,6 +82,22 @@ def test_epilogue_head_strided_output_uses_the_mfma_gemm():
     ref = oracle.gated_vha_output(f64(o, True), f64(c, True), f64(w, True), u, v)
     assert rel_err(host(y), ref) < BF16_TOL
     assert (host(big[..., dv:]) == 0).all()
+
+
+def test_epilogue_batch_strided_latent_and_output():
+    """Several sequences whose latent and output rows are not token-contiguous
+    across the batch (each sequence padded to a longer buffer), with a token
+    count that is not a multiple of the 256-token tile."""
+    B, S, H, dv, dc, r = 3, 200, 16, 128, 256, 4
+    o, c, w, u, v = _inputs(B, S, H, dv, dc, r, 606)
+    cbig = torch.zeros(B, S + 37, dc, dtype=torch.bfloat16, device="cuda:0")
+    cbig[:, :S] = dev_bf16(c)
+    ybig = torch.zeros(B, S + 11, H, dv, dtype=torch.bfloat16, device="cuda:0")
+    y = hca.attn_output_epilogue(dev_bf16(o), cbig[:, :S], dev_bf16(w), dev_f32(u), dev_f32(v), y=ybig[:, :S])
+    torch.cuda.synchronize()
+    ref = oracle.gated_vha_output(f64(o, True), f64(c, True), f64(w, True), u, v)
+    assert rel_err(host(y), ref) < BF16_TOL
+    assert (host(ybig[:, S:]) == 0).all()
 
 
 @pytest.mark.timeout(600)
