@@ -7,7 +7,8 @@ workloads of the path are timed in the same run and reported under
 `components`:
   * HCA prefill at 32768 tokens (window 128): compression, attention;
   * HCA decode: 64 sequences x 1 query over 8192 compressed entries + 128 raw;
-  * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention;
+  * DSA prefill at 65536 tokens: indexer + top-2048, sparse attention, and
+    the training backward of the sparse attention over the same selections;
   * DSA decode: 16 sequences x 1 query over 1,048,704 positions;
   * CSA prefill at 65536 tokens (the DSA shapes with K, V and the index keys
     compressed by blocks of 4): compression, indexer + top-2048 over the
@@ -268,7 +269,7 @@ def bench_decode(torch, hca, synth, cfg, steps, warmup):
     return res
 
 
-def bench_dsa(torch, hca, synth, cfg, steps, warmup):
+def bench_dsa(torch, hca, synth, cfg, steps, warmup, bwd_steps=0):
     import numpy as np
     t0 = time.time()
     inp = synth.make_dsa(cfg)
@@ -291,7 +292,24 @@ def bench_dsa(torch, hca, synth, cfg, steps, warmup):
     for _ in range(steps):
         tm(fi, fa)
     res = {"index_topk_ms": tm.median_ms(0), "attn_ms": tm.median_ms(1), "attn_mean_ms": tm.mean_ms(1)}
-    del q, k, v, qI, kI, w, idx, ws, o
+    del qI, kI, w, ws
+    if bwd_steps:
+        # the training backward of the sparse attention over the same selections
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(11)
+        dout = torch.randn(q.shape, generator=g, device="cuda:0").to(torch.bfloat16)
+        wsb = torch.empty(hca.dsa_sparse_attn_bwd_workspace_size(torch.bfloat16, cfg.batch, cfg.seqlen, cfg.h_q, 1,
+                                                                 cfg.d_qk, cfg.d_v, cfg.topk),
+                          dtype=torch.uint8, device="cuda:0")
+        fb = lambda: hca.dsa_sparse_attn_bwd(q, k, v, idx, o, lse, dout, scale=cfg.scale, workspace=wsb)
+        fb()
+        tmb = Timer(torch)
+        for _ in range(bwd_steps):
+            tmb(fb)
+        res["bwd_ms"] = tmb.median_ms()
+        res["bwd_workspace_gb"] = wsb.numel() / 1e9
+        del dout, wsb
+    del q, k, v, idx, o
     torch.cuda.empty_cache()
     return res
 
@@ -518,7 +536,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="c2,c4,c5,c5d,csa,epi,bwd",
+    ap.add_argument("--only", default="c2,c4,c5,c5b,c5d,csa,epi,bwd",
                     help="comma list of component workloads to run besides the headline step (c3 always runs; "
                          "'copy' runs only the counter calibration copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -593,7 +611,7 @@ def main():
         log(f"[bench] c4 done: {comps['hca_decode_1m']}")
     if "c5" in only:
         c5 = synth.CONFIGS["c5"]
-        r5 = bench_dsa(torch, hca, synth, c5, max(5, args.steps // 4), 1)
+        r5 = bench_dsa(torch, hca, synth, c5, max(5, args.steps // 4), 1, bwd_steps=3 if "c5b" in only else 0)
         fi, fa, sel = dsa_work(c5)
         tot = r5["index_topk_ms"] + r5["attn_ms"]
         comps["dsa_prefill_64k"] = {
@@ -602,7 +620,15 @@ def main():
             "index_tflops_f32": fi / r5["index_topk_ms"] / 1e9,
             "attn_tflops": fa / r5["attn_ms"] / 1e9, "attn_mfma_frac": fa / r5["attn_ms"] / 1e9 / PEAK_BF16_TFLOPS,
         }
-        log(f"[bench] c5 done: {comps['dsa_prefill_64k']}")
+        if "bwd_ms" in r5:
+            # per selected (query, position) pair and head: S, dP, dQ, dK, dV (5 x 2 x 256 FLOPs)
+            fbw = 2.0 * 5 * c5.d_qk * c5.h_q * sel
+            comps["dsa_backward_64k"] = {
+                "ms": r5["bwd_ms"], "tokens_per_s": c5.seqlen / r5["bwd_ms"] * 1e3,
+                "tflops": fbw / r5["bwd_ms"] / 1e9, "mfma_frac": fbw / r5["bwd_ms"] / 1e9 / PEAK_BF16_TFLOPS,
+                "flops": fbw, "workspace_gb": r5["bwd_workspace_gb"],
+            }
+        log(f"[bench] c5 done: {comps['dsa_prefill_64k']} {comps.get('dsa_backward_64k', '')}")
     if "c5d" in only:
         comps["dsa_decode_1m"] = bench_dsa_decode(torch, hca, max(20, args.steps), args.warmup)
         log(f"[bench] c5d done: {comps['dsa_decode_1m']}")

@@ -535,8 +535,12 @@ hca_status_t hca_attn_compress_bwd(hca_dtype_t dt,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
 
-/* Workspace bytes dsa_sparse_attn_bwd needs (D, and an inverted index of idx). */
-size_t dsa_sparse_attn_bwd_workspace_size(int batch, int seqlen, int h_q, int topk);
+/* Workspace bytes dsa_sparse_attn_bwd needs for these arguments (0 for
+ * invalid sizes): an inverted index of idx, and on the bf16 / 256-wide path
+ * the position-ordered contribution rows of one chunk of queries (at most
+ * 8 GiB plus the index; proportionally less for short sequences). */
+size_t dsa_sparse_attn_bwd_workspace_size(hca_dtype_t dt, int batch, int seqlen, int h_q, int h_kv, int d_qk,
+                                          int d_v, int topk);
 
 /*
  * dsa_sparse_attn_bwd -- gradients of dsa_sparse_attn_fwd's output with
@@ -551,6 +555,12 @@ size_t dsa_sparse_attn_bwd_workspace_size(int batch, int seqlen, int h_q, int to
  *         (written; positions no query lists get zeros)
  * dk and dv sum over the queries that list a position in an order set by
  * atomic slot claims, so they are reproducible up to fp32 rounding only.
+ * Kernels: bf16 with d_qk = d_v = 256 and h_q / h_kv a multiple of 64 (the
+ * DSA workload) runs the MFMA path -- one workgroup per (query, 64 heads)
+ * over the gathered rows, dq accumulated in fp32, each (query, position)
+ * pair's dk and dv contributions written as bf16 rows ordered by position and
+ * summed in fp32 per position, queries taken in chunks (launches several
+ * kernels per chunk); everything else the generic fp32 kernels.
  * Errors: HCA_ERR_INVALID for bad pointers, sizes or overlaps;
  * HCA_ERR_WORKSPACE for a missing or short workspace.
  * Supported: fp32 and bf16, d_qk and d_v <= 512 (multiples of 4), any

@@ -106,7 +106,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hca_compress_kv_bwd.restype = I
     lib.hca_compress_kv_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, P, P, S, P, S, P, P, I, I, I, I, I, P]
     lib.dsa_sparse_attn_bwd_workspace_size.restype = SZ
-    lib.dsa_sparse_attn_bwd_workspace_size.argtypes = [I, I, I, I]
+    lib.dsa_sparse_attn_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
     lib.dsa_sparse_attn_bwd.restype = I
     lib.dsa_sparse_attn_bwd.argtypes = [I, P, S, P, S, P, S, P, P, S, P, P, S, P, S, P, S, P, S,
                                         I, I, I, I, I, I, I, F, P, SZ, P]
@@ -522,8 +522,10 @@ def hca_attn_compress_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kc:
     return dq, dk, dv, dkc, dvc, dw_k, dw_v
 
 
-def dsa_sparse_attn_bwd_workspace_size(batch: int, seqlen: int, h_q: int, topk: int) -> int:
-    return load_library().dsa_sparse_attn_bwd_workspace_size(batch, seqlen, h_q, topk)
+def dsa_sparse_attn_bwd_workspace_size(dtype: torch.dtype, batch: int, seqlen: int, h_q: int, h_kv: int, d_qk: int,
+                                       d_v: int, topk: int) -> int:
+    dt = HCA_DTYPE_BF16 if dtype == torch.bfloat16 else HCA_DTYPE_F32
+    return load_library().dsa_sparse_attn_bwd_workspace_size(dt, batch, seqlen, h_q, h_kv, d_qk, d_v, topk)
 
 
 def dsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, o: torch.Tensor,
@@ -547,8 +549,8 @@ def dsa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: 
     dk = torch.empty(k.shape, **f32)
     dv = torch.empty(v.shape, **f32)
     if workspace is None:
-        workspace = torch.empty(lib.dsa_sparse_attn_bwd_workspace_size(B, S, Hq, topk), dtype=torch.uint8,
-                                device=q.device)
+        workspace = torch.empty(lib.dsa_sparse_attn_bwd_workspace_size(_dt(q), B, S, Hq, Hkv, dqk, dv_, topk),
+                                dtype=torch.uint8, device=q.device)
     _check(lib.dsa_sparse_attn_bwd(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                    _ptr(idx), _ptr(o), _strides(o), _ptr(lse), _ptr(dout), _strides(dout),
                                    _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),

@@ -26,6 +26,7 @@ SOURCES = [
     "attn_bwd.hip",
     "attn_bwd512.hip",
     "epilogue.hip",
+    "dsa_bwd256.hip",
     "hca_abi.cpp",
 ]
 

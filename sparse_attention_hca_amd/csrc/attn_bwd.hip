@@ -453,7 +453,8 @@ hipError_t launch_hca_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st) {
   return dt == 1 ? run_hca_bwd<uint16_t>(a, st) : run_hca_bwd<float>(a, st);
 }
 
-size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk) {
+size_t dsa_bwd_workspace_bytes(int dt, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v, int topk) {
+  if (dsa_bwd_uses_mfma(dt, d_qk, d_v, h_q, h_kv)) return dsa_bwd256_workspace_bytes(batch, seqlen, h_q, h_kv, topk);
   size_t bytes = delta_bytes(batch, seqlen, h_q);                                  // delta
   bytes += ((size_t)batch * (seqlen + 1) * sizeof(int32_t) + 255) / 256 * 256;      // counts -> offsets
   bytes += ((size_t)batch * seqlen * sizeof(int32_t) + 255) / 256 * 256;            // cursors
@@ -462,6 +463,7 @@ size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk) {
 }
 
 hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st) {
+  if (dsa_bwd_uses_mfma(dt, a.d, a.d_v, a.h_q, a.h_kv)) return launch_dsa_bwd256(a, ws, st);
   char* p = (char*)ws;
   a.delta = (float*)p;
   p += delta_bytes(a.batch, a.seqlen_q, a.h_q);

@@ -576,9 +576,12 @@ hca_status_t hca_compress_kv_bwd(hca_dtype_t dt, const void* k, hca_strides_t sk
   return HCA_OK;
 }
 
-size_t dsa_sparse_attn_bwd_workspace_size(int batch, int seqlen, int h_q, int topk) {
-  if (batch <= 0 || seqlen <= 0 || h_q <= 0 || topk <= 0) return 0;
-  return hca::dsa_bwd_workspace_bytes(batch, seqlen, h_q, topk);
+size_t dsa_sparse_attn_bwd_workspace_size(hca_dtype_t dt, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v,
+                                          int topk) {
+  if ((dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) || batch <= 0 || seqlen <= 0 || h_q <= 0 || h_kv <= 0 ||
+      h_q % h_kv || d_qk <= 0 || d_v <= 0 || topk <= 0)
+    return 0;
+  return hca::dsa_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen, h_q, h_kv, d_qk, d_v, topk);
 }
 
 hca_status_t dsa_sparse_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
@@ -619,7 +622,8 @@ hca_status_t dsa_sparse_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq
         if (overlaps(outs[x], outs[y])) return fail(HCA_ERR_INVALID, "dsa_sparse_attn_bwd: gradients overlap each other");
     }
   }
-  const size_t need = hca::dsa_bwd_workspace_bytes(batch, seqlen, h_q, topk);
+  const size_t need =
+      hca::dsa_bwd_workspace_bytes(dt == HCA_DTYPE_BF16 ? 1 : 0, batch, seqlen, h_q, h_kv, d_qk, d_v, topk);
   if (!workspace || workspace_bytes < need)
     return fail(HCA_ERR_WORKSPACE, "dsa_sparse_attn_bwd needs a %zu-byte workspace (got %zu)", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");

@@ -80,7 +80,12 @@ size_t hca_bwd512_workspace_bytes(int batch, int seqlen_q, int64_t q_pos0, int n
 // fw_k/fw_v non-null: fused compressor backward into the raw-row gradients.
 hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st, const float* fw_k = nullptr,
                                   const float* fw_v = nullptr);
-size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk);
+// bf16 with d_qk = d_v = 256 and a multiple of 64 query heads per KV head runs
+// the MFMA kernels (dsa_bwd256.hip); everything else the generic ones.
+bool dsa_bwd_uses_mfma(int dt, int d_qk, int d_v, int h_q, int h_kv);
+size_t dsa_bwd256_workspace_bytes(int batch, int seqlen, int h_q, int h_kv, int topk);
+hipError_t launch_dsa_bwd256(const BwdArgs& a, void* ws, hipStream_t st);
+size_t dsa_bwd_workspace_bytes(int dt, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v, int topk);
 hipError_t launch_dsa_attn_bwd(int dt, BwdArgs a, void* ws, hipStream_t st);
 // dk/dv (fp32, accumulated) += the compressor's backward of dkc/dvc; dw_k/dw_v written.
 hipError_t launch_compress_bwd(int dt, const void* k, LStrides sk, const void* v, LStrides sv, const float* dkc,

@@ -144,6 +144,21 @@ def make_index_lists(batch: int, seqlen: int, topk: int, seed: int, n_valid=None
     return out
 
 
+def make_index_lists_long(batch: int, seqlen: int, topk: int, seed: int) -> np.ndarray:
+    """int32 [batch, seqlen, topk]: row t lists min(t + 1, topk) distinct positions in [0, t] in random
+    order, then -1 -- make_index_lists without padding or duplicates, drawing each long row without
+    replacement instead of permuting its whole prefix (fast enough for 65536-position sequences)."""
+    rng = np.random.default_rng(seed)
+    out = np.full((batch, seqlen, topk), -1, dtype=np.int32)
+    for b in range(batch):
+        for t in range(seqlen):
+            if t + 1 <= topk:
+                out[b, t, : t + 1] = rng.permutation(t + 1)
+            else:
+                out[b, t] = rng.choice(t + 1, size=topk, replace=False)
+    return out
+
+
 def make_csa(cfg: CsaConfig) -> dict:
     """make_dsa's tensors for the CSA shapes plus compressor weights w_kv, w_i [1, block] (float32)."""
     rng = np.random.default_rng(cfg.seed)

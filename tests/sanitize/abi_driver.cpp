@@ -235,7 +235,7 @@ int main() {
     void* dout = A(size_t(B) * S * Hq * D * 2);
     float* dq = AT<float>(size_t(B) * S * Hq * D); float* dk = AT<float>(size_t(B) * S * D);
     float* dv = AT<float>(size_t(B) * S * D);
-    const size_t ws = dsa_sparse_attn_bwd_workspace_size(B, S, Hq, K);
+    const size_t ws = dsa_sparse_attn_bwd_workspace_size(BF, B, S, Hq, Hkv, D, D, K);
     void* wsp = A(ws ? ws : 16);
     auto bwd = [&](float* gq, float* gk, void* w, size_t wb) {
       return dsa_sparse_attn_bwd(BF, q, sq, k, skv, v, skv, idx, o, sq, lse, dout, sq, gq, sq, gk, skv, dv, skv, B, S,

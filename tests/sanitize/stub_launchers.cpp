@@ -33,8 +33,8 @@ size_t hca_bwd512_workspace_bytes(int batch, int seqlen_q, int64_t, int, int h_q
   return (size_t)batch * seqlen_q * h_q * 4 + 256;
 }
 hipError_t launch_hca_attn_bwd512(BwdArgs, void*, hipStream_t, const float*, const float*) { return hit(); }
-size_t dsa_bwd_workspace_bytes(int batch, int seqlen, int h_q, int topk) {
-  return (size_t)batch * seqlen * (h_q * 4 + (size_t)topk * 4 + 8);
+size_t dsa_bwd_workspace_bytes(int dt, int batch, int seqlen, int h_q, int, int d_qk, int, int topk) {
+  return (size_t)batch * seqlen * (h_q * 4 + (size_t)topk * 4 + 8) + (dt == 1 && d_qk == 256 ? (size_t)seqlen * topk * 1024 : 0);
 }
 hipError_t launch_dsa_attn_bwd(int, BwdArgs, void*, hipStream_t) { return hit(); }
 hipError_t launch_compress_bwd(int, const void*, LStrides, const void*, LStrides, const float*, LStrides, const float*,

@@ -333,6 +333,100 @@ def test_dsa_training_step_bf16_chain(S, topk):
         _check(name, g, r, BF16_TOL)
 
 
+def _dsa_bwd_bf16_case(B, S, Hq, Hkv, idx, seed, empty_rows=()):
+    """bf16 inputs, the oracle's forward (o rounded to bf16, lse fp32) as the
+    forward outputs, the library's backward against the oracle's gradients.
+    Entries at or past S are skipped (the oracle sees -1 there).  Rows in
+    empty_rows reach the library as all -1 with the empty row's forward
+    (o = 0, lse = -inf); the oracle keeps their lists but gets zero dout for
+    them, which gives the same gradients (every gradient is linear in dout)."""
+    d = 256
+    q = synth.make_normal((B, S, Hq, d), seed, bf16=True)
+    k = synth.make_normal((B, S, Hkv, d), seed + 1, bf16=True)
+    v = synth.make_normal((B, S, Hkv, d), seed + 2, bf16=True)
+    dout = synth.make_normal((B, S, Hq, d), seed + 3, bf16=True)
+    scale = float(1.0 / np.sqrt(d))
+    q64, k64, v64, g64 = (f64(x, True) for x in (q, k, v, dout))
+    idx_o = np.where(idx < S, idx, -1)
+    o, lse = _oracle_dsa_fwd(q64, k64, v64, idx_o, scale)
+    idx_k = idx.copy()
+    for b, t in empty_rows:
+        g64[b, t] = 0.0
+        idx_k[b, t] = -1
+        o[b, t], lse[b, :, t] = 0.0, -np.inf
+    got = hca.dsa_sparse_attn_bwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(idx_k).cuda(),
+                                  torch.from_numpy(o).to(torch.bfloat16).cuda(), dev_f32(lse), dev_bf16(dout),
+                                  scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_attention_bwd(q64, k64, v64, idx_o, scale, g64)
+    return got, ref
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,topk,n_valid,dup", [
+    (2, 200, 64, 1, 40, 35, 2),      # topk not a multiple of 32, -1 padding, duplicates, two sequences
+    (1, 150, 128, 2, 64, None, 0),   # two KV heads of 64 query heads each
+    (1, 130, 128, 1, 100, None, 0),  # two 64-head groups on one KV head (their contributions add)
+])
+def test_dsa_bwd_mfma_path(B, S, Hq, Hkv, topk, n_valid, dup):
+    """The bf16 / 256-wide kernels (64 heads per workgroup, position-ordered
+    contribution rows) on ragged, padded and grouped shapes."""
+    _say("dsa bwd mfma", B, S, Hq, Hkv, topk, n_valid, dup)
+    idx = synth.make_index_lists(B, S, topk, seed=95, n_valid=n_valid, dup_per_row=dup)
+    got, ref = _dsa_bwd_bf16_case(B, S, Hq, Hkv, idx, 90)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, g, r, BF16_TOL)
+
+
+def test_dsa_bwd_mfma_empty_and_out_of_range_rows():
+    """An all -1 row adds nothing and gets dq = 0; an entry past the sequence is skipped."""
+    B, S, Hq, Hkv, topk = 1, 96, 64, 1, 48
+    idx = synth.make_index_lists(B, S, topk, seed=96)
+    idx[0, 70, 3] = S + 5
+    got, ref = _dsa_bwd_bf16_case(B, S, Hq, Hkv, idx, 97, empty_rows=[(0, 40)])
+    assert (host(got[0])[0, 40] == 0).all()
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, g, r, BF16_TOL)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_dsa_backward_sampled():
+    """The DSA backward at the 65536-token workload (64 heads x 256 on one KV
+    head, top-2048; the contribution rows go through 16 chunks of 4096
+    queries): dq on sampled rows, dk and dv on sampled positions, against the
+    oracle's gradients of the same selections."""
+    cfg = synth.CONFIGS["c5"]
+    _say("full-size dsa backward", cfg)
+    inp = synth.make_dsa(cfg)
+    S, Hq, d = cfg.seqlen, cfg.h_q, cfg.d_qk
+    idx = synth.make_index_lists_long(1, S, cfg.topk, seed=98)
+    dout = synth.make_normal((1, S, Hq, d), 99, bf16=True)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    idd = torch.from_numpy(idx).cuda()
+    o, lse = hca.dsa_sparse_attn_fwd(q, k, v, idd, scale=cfg.scale)
+    dq, dk, dv = hca.dsa_sparse_attn_bwd(q, k, v, idd, o, lse, dev_bf16(dout), scale=cfg.scale)
+    torch.cuda.synchronize()
+    _say("  backward done")
+    k64, v64 = f64(inp["k"], True), f64(inp["v"], True)
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 2047, 2048, 4095, 4096, 40000, S - 1]) | set(rng.integers(0, S, 6).tolist()))
+    rq, _, _ = oracle.sparse_attention_bwd(f64(inp["q"][:, rows], True), k64, v64, idx[:, rows], cfg.scale,
+                                           f64(dout[:, rows], True))
+    err = rel_err(host(dq[:, rows]), rq)
+    _say(f"  dq on {len(rows)} rows: {err:.3e}")
+    assert err < BF16_TOL
+    for u in (S - 1, S - 2, S - 37, S - 700, S - 3000):
+        sel = np.nonzero((idx[0] == u).any(axis=1))[0]
+        _, rk, rv = oracle.sparse_attention_bwd(f64(inp["q"][:, sel], True), k64, v64, idx[:, sel], cfg.scale,
+                                                f64(dout[:, sel], True))
+        ek = rel_err(host(dk[:, u]), rk[:, u])
+        ev = rel_err(host(dv[:, u]), rv[:, u])
+        _say(f"  position {u}: {len(sel)} selecting queries, dk {ek:.2e}, dv {ev:.2e}")
+        assert ek < BF16_TOL and ev < BF16_TOL
+    # a position no query selects gets zeros (every position of a full row is selected by some later
+    # query with overwhelming probability, so check the structure instead: dk, dv finite everywhere)
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
 @pytest.mark.timeout(900)
 def test_full_size_backward_c2_shape():
     """The backward calls the benchmark times, at their shape (32768 tokens, 16

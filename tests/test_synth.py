@@ -53,3 +53,15 @@ def test_index_lists_are_causal_distinct_and_padded():
     assert any(len(set(dup[0, t][dup[0, t] >= 0].tolist())) < min(t + 1, 8) for t in range(40))
     assert (dup[dup >= 0] <= np.arange(40)[None, :, None].repeat(8, 2)[dup >= 0]).all()
     np.testing.assert_array_equal(synth.make_index_lists(2, 50, 8, seed=4, n_valid=6), idx)
+
+
+def test_long_index_lists_are_distinct_causal_prefix_samples():
+    x = synth.make_index_lists_long(2, 300, 64, seed=9)
+    assert x.shape == (2, 300, 64) and x.dtype == np.int32
+    for b in range(2):
+        for t in (0, 5, 63, 64, 65, 299):
+            n = min(t + 1, 64)
+            row = x[b, t]
+            assert (row[n:] == -1).all()
+            assert len(np.unique(row[:n])) == n and row[:n].min() >= 0 and row[:n].max() <= t
+    assert np.array_equal(x, synth.make_index_lists_long(2, 300, 64, seed=9))
