@@ -19,6 +19,7 @@ SOURCES = [
     "compress.hip",
     "append.hip",
     "attn_generic.hip",
+    "attn_f32mfma.hip",
     "attn_prefill512.hip",
     "attn_decode512.hip",
     "dsa_index_topk.hip",

@@ -39,6 +39,9 @@ hipError_t launch_ring_write(int dt, const void* k_new, LStrides skn, const void
 // One workgroup per (query, head): any dtype, head_dim <= 512, keys per query <= kGenericMaxKeys.
 constexpr int kGenericMaxKeys = 16384;
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t st);
+// fp32 with head_dim 32, 64 or 128: the fp32 MFMA kernel (attn_f32mfma.hip).
+bool attn_f32mfma_supports(int dt, int head_dim);
+hipError_t launch_attn_f32mfma(const AttnArgs& a, hipStream_t st);
 
 // bf16, head_dim 512, MFMA prefill.
 hipError_t launch_attn_prefill512(const AttnArgs& a, hipStream_t st);

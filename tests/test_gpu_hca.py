@@ -132,6 +132,12 @@ PREFILL_CASES = [
     ("bf16-block1", "bf16", 150, 1, 1, 512, 1, 5),
     ("bf16-tiny", "bf16", 2, 1, 1, 512, 128, 128),
     ("f32-d64", "f32", 500, 2, 1, 64, 16, 40),
+    # the fp32 MFMA kernel: ragged query tiles, grouped heads, degenerate windows
+    ("f32-gqa-ragged", "f32", 333, 3, 1, 64, 8, 50),
+    ("f32-window1", "f32", 130, 1, 1, 64, 4, 1),
+    ("f32-block1", "f32", 97, 2, 2, 128, 1, 3),
+    ("f32-window-covers", "f32", 70, 2, 2, 128, 128, 100),
+    ("f32-tiny", "f32", 3, 1, 1, 128, 128, 128),
 ]
 
 
