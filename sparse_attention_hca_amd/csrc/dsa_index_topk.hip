@@ -354,6 +354,11 @@ constexpr int NS = 1024;  // samples of a row used to bracket the k-th largest k
 //   keys (256 spread groups of 4) bracket the k-th largest key; one pass emits
 //   the keys above the bracket and collects the keys inside it (at most CAP),
 //   where T and the tie-break are resolved in LDS.  When the bracket misses, the paths above run.
+// POS: positions come from p.pos (the candidate rows of the decode merge)
+// rather than being the element index; without it the row scans hold no
+// load besides the row's own, so the next step's loads stay in flight while
+// a step's elements are emitted.
+template <bool POS>
 __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
   __shared__ uint32_t hist[HB];
   __shared__ uint32_t ckey[CAP];
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     n = min(p.seg_len, p.n_total - off);
     srow = p.sc + (int64_t)b * p.ld + off;
     out = p.idx + (int64_t)row * k;
-    if (p.pos) prow = p.pos + (int64_t)b * p.ld + off;
+    if (POS) prow = p.pos + (int64_t)b * p.ld + off;
   } else {
     const int t = p.r0 + row;
     n = p.block > 1 ? (t + 1) / p.block : t + 1;
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     out = p.idx + (int64_t)t * k;
   }
   // position of element u (monotonic in u)
-  auto P = [&](int u) __attribute__((always_inline)) { return prow ? prow[u] : u + off; };
+  auto P = [&](int u) __attribute__((always_inline)) { return POS ? prow[u] : u + off; };
   if (n <= k) {
     for (int j = tid; j < k; j += 256) out[j] = j < n ? P(j) : -1;
     return;
@@ -489,20 +494,25 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
         run_i += tot >> 16;
       };
       // full steps: unguarded loads, those of step s+1 issued before step s
-      // is classified
+      // is classified, in two register sets taken in turn (no copies).  The
+      // next step's loads are issued on every path (the last step re-reads
+      // the final full step), so the wait before a classification counts
+      // exactly the four loads issued after its own.
       const int n_full = n & ~4095;
       auto load_full = [&](int base, f32x4 (&v)[4]) __attribute__((always_inline)) {
+        base = base < n_full - 4096 ? base : n_full - 4096;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const f32x4*>(srow + base + 1024 * e + 4 * tid);
       };
       if (n_full > 0) {
-        f32x4 v[4], vn[4];
-        load_full(0, v);
-        for (int base = 0; base < n_full; base += 4096) {
-          if (base + 4096 < n_full) load_full(base + 4096, vn);
-          classify(v[0], v[1], v[2], v[3], base);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = vn[e];
+        f32x4 va[4], vb[4];
+        load_full(0, va);
+        for (int base = 0; base < n_full; base += 8192) {
+          load_full(base + 4096, vb);
+          classify(va[0], va[1], va[2], va[3], base);
+          if (base + 4096 >= n_full) break;
+          load_full(base + 8192, va);
+          classify(vb[0], vb[1], vb[2], vb[3], base + 4096);
         }
       }
       if (n_full < n) {
@@ -970,7 +980,7 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
       pp.r0 = r0;
       pp.topk = topk;
       pp.block = block;
-      hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(256), 0, st, pp);
+      hipLaunchKernelGGL(topk_select_kernel<false>, dim3(rows), dim3(256), 0, st, pp);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1067,7 +1077,7 @@ hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const 
   s1.nseg = nseg;
   s1.seg_len = SEG;
   s1.n_total = n_keys;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(batch * nseg), dim3(256), 0, st, s1);
+  hipLaunchKernelGGL(topk_select_kernel<false>, dim3(batch * nseg), dim3(256), 0, st, s1);
   e = hipGetLastError();
   if (e != hipSuccess || nseg == 1) return e;
   // second stage: the segments' selections, in position order, hold the top-k
@@ -1090,7 +1100,7 @@ hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const 
   s2.seg_len = n2;
   s2.n_total = n2;
   s2.pos = cand_pos;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(batch), dim3(256), 0, st, s2);
+  hipLaunchKernelGGL(topk_select_kernel<true>, dim3(batch), dim3(256), 0, st, s2);
   return hipGetLastError();
 }
 
