@@ -31,6 +31,11 @@ namespace {
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int DI_MAX = 128;
+// max(x, 0) as one integer max on the bits: a set sign bit (negative, -0)
+// reads as a negative int and gives +0, a clear one keeps x (a float max would
+// add a NaN-quieting instruction per value).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 constexpr int QT = 32;   // queries per wave tile
 constexpr int KT = 32;   // keys per wave tile
 constexpr int WAVES = 4; // a workgroup covers 32 queries x 128 keys
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(ScoreParams p) {
     }
     const float wh = p.w[(int64_t)tq * p.h_i + h];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) score[r] = fmaf(wh, fmaxf(acc[r], 0.f), score[r]);
+    for (int r = 0; r < 16; ++r) score[r] = fmaf(wh, relu(acc[r]), score[r]);
   }
   // lane holds query col, keys 8*(r/4) + 4*hf + (r%4): four runs of 4 consecutive keys
   const int qrow = qt0 + col;
@@ -154,19 +159,10 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
   };
   const int n_kt = min(KG, (k_last - kbase) / KT + 1);
   const int qrow = qt0 + col;
-  float ka[HALF], kn[HALF];
-  load_k(0, ka);
-  // settle the prologue loads here: otherwise the loop's waits, placed for its
-  // first iteration, would also hold every later iteration until the next
-  // tile's prefetch has landed
-#pragma unroll
-  for (int h = 0; h < HI; ++h)
-#pragma unroll
-    for (int i = 0; i < HALF; ++i) asm volatile("" ::"v"(qb[h][i]));
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) asm volatile("" ::"v"(ka[i]));
-  for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt) load_k(kt + 1, kn);
+  // One key tile: two heads' MFMA chains at a time (independent, so
+  // consecutive MFMAs do not wait on each other), each pair folded as
+  // w * relu(.) into the score tile.
+  auto tile = [&](int kt, const float (&ka)[HALF]) __attribute__((always_inline)) {
     f32x16_t score;
 #pragma unroll
     for (int r = 0; r < 16; ++r) score[r] = 0.f;
@@ -182,8 +178,8 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        score[r] = fmaf(wq[h], fmaxf(a0[r], 0.f), score[r]);
-        score[r] = fmaf(wq[h + 1], fmaxf(a1[r], 0.f), score[r]);
+        score[r] = fmaf(wq[h], relu(a0[r]), score[r]);
+        score[r] = fmaf(wq[h + 1], relu(a1[r]), score[r]);
       }
     }
     // lane holds query col, keys 8*(r/4) + 4*hf + (r%4) of the tile
@@ -199,8 +195,26 @@ __global__ __launch_bounds__(256) void index_scores_qs_kernel(ScoreParams p) {
         }
       }
     }
+  };
+  // two key-row register sets taken in turn (no copies); the next tile's rows
+  // are loaded while the current tile runs
+  float ka[HALF], kb[HALF];
+  load_k(0, ka);
+  // settle the prologue loads here: otherwise the loop's waits, placed for its
+  // first iteration, would also hold every later iteration until the next
+  // tile's prefetch has landed
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) ka[i] = kn[i];
+  for (int h = 0; h < HI; ++h)
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) asm volatile("" ::"v"(qb[h][i]));
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) asm volatile("" ::"v"(ka[i]));
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    load_k(min(kt + 1, n_kt - 1), kb);
+    tile(kt, ka);
+    if (kt + 1 >= n_kt) break;
+    load_k(min(kt + 2, n_kt - 1), ka);
+    tile(kt + 1, kb);
   }
 }
 
@@ -796,7 +810,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const float* qI, con
   }
   float s = 0.f;
 #pragma unroll
-  for (int h = 0; h < HI; ++h) s = fmaf(wsh[h], fmaxf(acc[h], 0.f), s);
+  for (int h = 0; h < HI; ++h) s = fmaf(wsh[h], relu(acc[h]), s);
   sc[(int64_t)b * ld + u] = s;
 }
 
@@ -853,7 +867,7 @@ __global__ __launch_bounds__(256) void decode_scores64_kernel(const float* qI, c
       float a = acc[kb][h];
       a += __shfl_xor(a, 1);
       a += __shfl_xor(a, 2);
-      s = fmaf(wsh[h], fmaxf(a, 0.f), s);
+      s = fmaf(wsh[h], relu(a), s);
     }
     const int u = key0 + 16 * kb + (lane >> 2);
     if (q4 == 0 && u < n) sc[(int64_t)b * ld + u] = s;

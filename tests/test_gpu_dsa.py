@@ -43,6 +43,22 @@ def test_index_topk_exact_sets(S, topk, B):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("h_i,d_i", [(4, 16), (4, 32), (4, 48), (8, 16), (8, 32), (4, 80), (8, 128)])
+def test_index_topk_indexer_shapes(h_i, d_i):
+    """The other indexer shapes the library takes (h_i 4 or 8, d_i a multiple of
+    16 up to 128): the query-stationary score kernels of the small shapes and the
+    per-tile kernel of the rest, over several key blocks, give the oracle's sets."""
+    S, topk = 1800, 128
+    cfg = synth.small_dsa(seqlen=S, topk=topk, h_i=h_i, d_i=d_i)
+    _say("index_topk shape", cfg)
+    inp = make_tie_free(cfg)
+    idx = hca.dsa_index_topk(dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"]), topk)
+    torch.cuda.synchronize()
+    got = _sorted_rows(idx.cpu().numpy())
+    ref = oracle.index_topk(inp["qI"], inp["kI"], inp["w"], topk)
+    assert np.array_equal(got, ref)
+
+
 def test_index_topk_long_rows_exact():
     """Rows of 4096+ positions take the sampling selection path; tie-free rows
     must give exactly the oracle's sets."""
