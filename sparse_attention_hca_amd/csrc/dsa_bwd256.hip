@@ -9,8 +9,8 @@
 //
 // One workgroup (4 waves) per (query, group of 64 query heads sharing one KV
 // head), the forward's layout: the selected K and V rows are gathered 32 at a
-// time into LDS by 16-byte DMA (two stages, one tile in flight), and for each
-// tile
+// time into LDS by 16-byte DMA (three stages, two tiles in flight), and for
+// each tile
 //   * wave w forms S^T = K Q^T and dP^T = V dO^T for heads 16w .. 16w+15
 //     (v_mfma_f32_16x16x32_bf16, Q and dO fragments in registers), then P and
 //     dS = P (dP - D) in fp32;
@@ -44,7 +44,7 @@ constexpr int HPB = 64;                // heads per workgroup
 constexpr int ROWB = 2 * D;            // bytes per K or V row
 constexpr int KSTB = TK * ROWB;        // K part of a stage
 constexpr int STAGEB = 2 * KSTB;       // K rows then V rows
-constexpr int NSTAGE = 2;
+constexpr int NSTAGE = 3;
 constexpr int MAX_TOPK = 4096;
 constexpr int CROW = 2 * D;            // contribution row: dk (256 bf16) then dv (256 bf16)
 constexpr size_t kContribBudget = (size_t)8 << 30;  // workspace for the contribution rows of one chunk
@@ -61,6 +61,7 @@ struct DsaBwdParams {
   LStrides sdq;
   const int32_t* pslot;   // [chunk queries, topk]: contribution row of each entry, -1 if none
   uint16_t* contrib;      // rows of CROW bf16, G per slot
+  uint16_t* dummy;        // one CROW row per workgroup: the stores of entries without a slot
   int b, q0, seqlen, n_kv, h_q, h_kv, topk, n_hb, G;
   float scale, c;         // c = scale * log2(e)
 };
@@ -235,13 +236,24 @@ void dsa_bwd256_kernel(DsaBwdParams p) {
     for (int hk = 0; hk < 4; ++hk) dqa[i][hk] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float c = p.c, sc = p.scale;
 
-  if (ntiles > 0) issue(0, 0);
+  // Two tiles in flight.  Every wave issues exactly 8 DMA instructions per
+  // tile (re-reading the last tile past the end) and 16 contribution stores
+  // per tile (entries without a slot store to the workgroup's dummy row), so
+  // the wait for tile tt counts what was issued after its DMA: the stores of
+  // tiles tt-2 and tt-1 and the DMA of tile tt+1 -- the stores stay in flight.
+  const int last = ntiles - 1;
+  if (ntiles > 0) {
+    issue(0, 0);
+    issue(min(1, last), 1);
+  }
   for (int tt = 0; tt < ntiles; ++tt) {
-    const int st = tt & 1;
-    // tile tt landed (and the previous tile's contribution stores drained);
-    // every wave is done with the exchange buffers and with stage st ^ 1
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (tt + 1 < ntiles) issue(tt + 1, st ^ 1);
+    const int st = tt % NSTAGE;
+    // tile tt landed; every wave is done with the exchange buffers and with
+    // the stage of tile tt - 1, which the DMA of tile tt + 2 refills
+    if (tt >= 2) asm volatile("s_waitcnt vmcnt(40)\n\ts_barrier" ::: "memory");
+    else if (tt == 1) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    issue(min(tt + 2, last), (tt + 2) % NSTAGE);
     const unsigned char* sk_ = ring + st * STAGEB;
     const unsigned char* sv_ = sk_ + KSTB;
     const uint32_t vmask = tvalid[tt];
@@ -308,7 +320,9 @@ void dsa_bwd256_kernel(DsaBwdParams p) {
     }
     // dK^T = Q^T dS^T and dV^T = dO^T P^T for this wave's 64 dims and the
     // tile's 32 keys (columns: key half kh, key row 16kh + col), k = 64 heads
-    // in the transposing reads' order
+    // in the transposing reads' order.  At most 47 memory operations may be
+    // in flight before the tile's 16 stores (the counter holds 63).
+    asm volatile("s_waitcnt vmcnt(47)" ::: "memory");
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const unsigned char* xs = which ? xp : xk;
@@ -324,25 +338,26 @@ void dsa_bwd256_kernel(DsaBwdParams p) {
           bk[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
         }
         const int slot = sslot[tt * TK + entry_of(rho)];
-        uint16_t* dst = slot >= 0
-                            ? p.contrib + ((int64_t)slot * p.G + (g * p.n_hb + hb)) * CROW + which * D + 64 * w + 4 * grp
-                            : nullptr;
+        uint16_t* dst = (slot >= 0 ? p.contrib + ((int64_t)slot * p.G + (g * p.n_hb + hb)) * CROW
+                                   : p.dummy + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * CROW) +
+                        which * D + 64 * w + 4 * grp;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(which ? da[i][ks] : qa[i][ks], bk[ks], acc, 0, 0, 0);
-          if (dst) {
-            u32x2 pk;
-            pk[0] = pack_bf16x2(acc[0], acc[1]);
-            pk[1] = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<u32x2*>(dst + 16 * i) = pk;
-          }
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[0], acc[1]);
+          pk[1] = pack_bf16x2(acc[2], acc[3]);
+          *reinterpret_cast<u32x2*>(dst + 16 * i) = pk;
         }
       }
     }
   }
+
+  // no DMA may still target this workgroup's LDS when it exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- dq (the scale is in dS): lane holds dims 16(4w+i) + 4grp .. +3 of head 16hk + col
 #pragma unroll
@@ -482,7 +497,8 @@ size_t dsa_bwd256_workspace_bytes(int batch, int seqlen, int h_q, int h_kv, int 
   size_t bytes = align256((size_t)(seqlen + 1) * 4);            // counts -> offsets
   bytes += align256((size_t)seqlen * 4);                         // cursors
   bytes += align256((size_t)cq * topk * 4);                      // slots
-  bytes += (size_t)cq * topk * G * CROW * 2;                     // contribution rows
+  bytes += align256((size_t)cq * topk * G * CROW * 2);           // contribution rows
+  bytes += (size_t)cq * G * CROW * 2;                            // one dummy row per workgroup
   return bytes;
 }
 
@@ -498,13 +514,15 @@ hipError_t launch_dsa_bwd256(const BwdArgs& a, void* ws, hipStream_t st) {
   int32_t* pslot = (int32_t*)pw;
   pw += align256((size_t)cq * a.topk * 4);
   uint16_t* contrib = (uint16_t*)pw;
+  pw += align256((size_t)cq * a.topk * G * CROW * 2);
+  uint16_t* dummy = (uint16_t*)pw;
 
   DsaBwdParams p;
   p.q = (const uint16_t*)a.q; p.k = (const uint16_t*)a.k; p.v = (const uint16_t*)a.v;
   p.o = (const uint16_t*)a.o; p.dout = (const uint16_t*)a.dout;
   p.sq = a.sq; p.sk = a.sk; p.sv = a.sv; p.so = a.so; p.sdo = a.sdo;
   p.lse = a.lse; p.idx = a.idx; p.dq = a.dq; p.sdq = a.sdq;
-  p.pslot = pslot; p.contrib = contrib;
+  p.pslot = pslot; p.contrib = contrib; p.dummy = dummy;
   p.seqlen = a.seqlen_q; p.n_kv = a.seqlen_kv; p.h_q = a.h_q; p.h_kv = a.h_kv; p.topk = a.topk;
   p.n_hb = n_hb; p.G = G;
   p.scale = a.scale; p.c = a.scale * kLog2e;
