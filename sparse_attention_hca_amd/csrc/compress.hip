@@ -114,10 +114,9 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(const T* __restrict_
                                                             const float* __restrict__ w0, T* __restrict__ out0,
                                                             LStrides so0, const T* __restrict__ x1, LStrides sx1,
                                                             const float* __restrict__ w1, T* __restrict__ out1,
-                                                            LStrides so1, int block, int d) {
+                                                            LStrides so1, int block, int d, int nblocks) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int U = 4;
-  const int j = blockIdx.x;
   const int b = blockIdx.y >> 1;
   const bool second = blockIdx.y & 1;
   const T* x = second ? x1 : x0;
@@ -128,6 +127,10 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(const T* __restrict_
   const int tid = threadIdx.x;
   const int dchunks = d / EPV;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // blocks j = blockIdx.x, + gridDim.x, ...: the grid is sized to one round of
+  // resident workgroups, so long sequences stream without a second wave of
+  // launches
+  for (int j = blockIdx.x; j < nblocks; j += gridDim.x) {
   const T* ptr[CPT];
   const float* wp[CPT];
   int hh[CPT], cc[CPT];
@@ -187,6 +190,7 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(const T* __restrict_
       st16(dst, pk);
     }
   }
+  }
 }
 
 template <typename T, int D>
@@ -208,11 +212,14 @@ hipError_t launch_compress(int dt, const void* x, LStrides sx, const float* w, v
     const int epv = dt == 1 ? 8 : 4;
     const int pieces = h * d / epv;
     if ((d / epv) % 64 == 0 && pieces % 256 == 0) {
-      const dim3 grid(seqlen / block, 2 * batch);
+      // at most 1024 resident workgroups (4 per CU) over every (block, tensor, batch)
+      const int nb = seqlen / block;
+      const int per = (1024 + 2 * batch - 1) / (2 * batch);
+      const dim3 grid(nb < per ? nb : per, 2 * batch);
 #define HCA_COMPRESS_ROWS(T, CPT)                                                                               \
   if (pieces == 256 * CPT) {                                                                                    \
     hipLaunchKernelGGL((compress_rows_kernel<T, CPT>), grid, dim3(256), 0, st, (const T*)x, sx, w, (T*)out, so, \
-                       (const T*)x2, sx2, w2, (T*)out2, so2, block, d);                                        \
+                       (const T*)x2, sx2, w2, (T*)out2, so2, block, d, nb);                                    \
     return hipGetLastError();                                                                                   \
   }
       if (dt == 1) {
