@@ -656,6 +656,71 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       }
       return;
     }
+    if (c_hi < (uint32_t)k && c_hi + nc >= (uint32_t)k) {
+      // The bracket holds the k-th key but more than CAP candidates (a mass of
+      // equal scores, e.g. ReLU zeros).  One pass histograms the keys inside
+      // [lo, hi] into 2048 bins of width 2^bs, with each bin's smallest and
+      // largest key (in the free candidate arrays); when the bin holding the
+      // k-th key has a single key value T, one ordered pass emits the bracket's
+      // keys above T and the lowest positions equal to T.  Otherwise the general
+      // path below runs.
+      uint32_t* bmin = ckey;
+      uint32_t* bmax = reinterpret_cast<uint32_t*>(cpos);
+      const uint32_t span = hi - lo;
+      int bs = 0;
+      while ((span >> bs) >= 2048u) ++bs;
+      __syncthreads();
+      for (int i = tid; i < 2048; i += 256) {
+        hist[i] = 0;
+        bmin[i] = 0xffffffffu;
+        bmax[i] = 0;
+      }
+      __syncthreads();
+      auto add = [&](float x) __attribute__((always_inline)) {
+        const uint32_t key = okey(x);
+        if (key >= lo && key <= hi) {
+          const uint32_t bin = (key - lo) >> bs;
+          atomicAdd(&hist[bin], 1u);
+          atomicMin(&bmin[bin], key);
+          atomicMax(&bmax[bin], key);
+        }
+      };
+      {
+        const int n4 = n & ~3;
+        for (int u = 4 * tid; u < n4; u += 1024) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(srow + u);
+          add(v[0]);
+          add(v[1]);
+          add(v[2]);
+          add(v[3]);
+        }
+        for (int u = n4 + tid; u < n; u += 256) add(srow[u]);
+      }
+      __syncthreads();
+      find_bin(hist, 2048, (uint32_t)k - c_hi, part, sel_info);
+      const uint32_t bt = sel_info[0], above = sel_info[1];
+      const uint32_t T = bmin[bt];
+      if (T == bmax[bt]) {
+        const uint32_t need = (uint32_t)k - c_hi - above;  // taken from the keys equal to T
+        __syncthreads();
+        if (tid == 0) sel_info[2] = c_hi;
+        __syncthreads();
+        uint32_t eq_base = 0;
+        for (int base = 0; base < n; base += 256) {
+          const int u = base + tid;
+          uint32_t key = 0;
+          const bool valid = u < n;
+          if (valid) key = okey(srow[u]);
+          if (valid && key > T && key <= hi) out[atomicAdd(&sel_info[2], 1u)] = P(u);
+          uint32_t tot;
+          const bool eq = valid && key == T;
+          const uint32_t r = ordered_rank(eq, wave_cnt, tot);
+          if (eq && eq_base + r < need) out[c_hi + above + eq_base + r] = P(u);
+          eq_base += tot;
+        }
+        return;
+      }
+    }
     __syncthreads();
   }
 

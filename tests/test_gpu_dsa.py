@@ -95,6 +95,24 @@ def test_index_topk_long_rows_heavy_ties():
     assert np.array_equal(got[:, rows], ref)
 
 
+def test_index_topk_long_rows_zero_mass_at_the_boundary():
+    """Most index keys are zero, so most scores are exactly 0, and the weights
+    are negative, so every other score is below 0: on rows past ~4800
+    positions the zeros outnumber the candidate buffer and the k-th key is a
+    tie among thousands of zeros (the lowest positions win)."""
+    S, k = 6000, 512
+    rng = np.random.default_rng(21)
+    kI = rng.standard_normal((1, S, 64)).astype(np.float32)
+    kI[0, rng.random(S) < 0.8] = 0.0
+    qI = rng.standard_normal((1, S, 4, 64)).astype(np.float32)
+    w = -np.abs(rng.standard_normal((1, S, 4))).astype(np.float32) - 0.1
+    idx = hca.dsa_index_topk(dev_f32(qI), dev_f32(kI), dev_f32(w), k)
+    got = _sorted_rows(idx.cpu().numpy())
+    rows = list(range(4095, S, 37)) + [S - 1]
+    ref = oracle.index_topk(qI, kI, w, k, rows=rows)
+    assert np.array_equal(got[:, rows], ref)
+
+
 def test_index_topk_ties_break_by_position():
     """Equal index keys make every score equal: the first k positions win."""
     S, k = 600, 64
