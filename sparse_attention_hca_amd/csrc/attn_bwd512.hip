@@ -310,16 +310,37 @@ void bwd512_dq_kernel(DqParams p) {
     compute(tt, tt & 1, tt + 1 < ntiles);
   }
 
+  // dq rows leave whole: the tile's 64 x 512 fp32 values are staged in the
+  // idle LDS ([query][2 KB], 16-byte chunk c of row r in slot c ^ (r % 32)),
+  // then each wave stores 16 rows with two 1-KB instructions each.
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-  if (!qvalid) return;
-  float* dqp = a.dq + b * a.sdq.b + (int64_t)iq * a.sdq.s + (int64_t)h * a.sdq.h + 4 * hf;
-  const float sc = a.scale;
+  barrier_lds();  // every wave is done with the last tile's stage
+  {
+    const float sc = a.scale;
+    const int r = 32 * pair + col;  // this lane's query row in the tile
+    float* rowp = reinterpret_cast<float*>(smem + r * 2048);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<f32x4*>(dqp + 32 * (8 * role + i) + 8 * q4) =
-          f32x4{dq[i][4 * q4] * sc, dq[i][4 * q4 + 1] * sc, dq[i][4 * q4 + 2] * sc, dq[i][4 * q4 + 3] * sc};
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int cch = 8 * (8 * role + i) + 2 * q4 + hf;  // dims 32 (8 role + i) + 8 q4 + 4 hf .. +3
+        *reinterpret_cast<f32x4*>(rowp + 4 * (cch ^ (r & 31))) =
+            f32x4{dq[i][4 * q4] * sc, dq[i][4 * q4 + 1] * sc, dq[i][4 * q4 + 2] * sc, dq[i][4 * q4 + 3] * sc};
+      }
+  }
+  barrier_lds();
+#pragma unroll 4
+  for (int j = 0; j < DQ_BM / 4; ++j) {
+    const int r = (DQ_BM / 4) * w + j;
+    if (i0 + r >= a.seqlen_q) break;
+    const float* rowp = reinterpret_cast<const float*>(smem + r * 2048);
+    float* dst = a.dq + b * a.sdq.b + (int64_t)(i0 + r) * a.sdq.s + (int64_t)h * a.sdq.h;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int cch = 64 * half + lane;
+      *reinterpret_cast<f32x4*>(dst + 4 * cch) = *reinterpret_cast<const f32x4*>(rowp + 4 * (cch ^ (r & 31)));
+    }
+  }
 }
 
 // ------------------------------------------------------------------ dkv kernel
