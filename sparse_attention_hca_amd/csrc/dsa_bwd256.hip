@@ -76,6 +76,14 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// Byte offset of head-byte hb of key row rho in the [key][head] exchange
+// buffers (64 bf16 heads = 128 B per row): the 8-byte chunk index is XORed with
+// rho % 16, so the dK/dV operand reads of 16 rows (each lane 8 bytes of one
+// row) spread over the banks instead of piling onto two.
+__device__ __forceinline__ uint32_t xoff(int rho, int hb) {
+  return rho * (HPB * 2) + 8 * ((hb >> 3) ^ (rho & 15)) + (hb & 7);
+}
+
 // Transposing read offset of the A operand of a 16x16x32 step whose 16 rows
 // are consecutive 16-element columns of a row-major LDS tile: lane (col, grp)
 // reads, for read e (0, 1), 4 elements of row 16e + 4grp + col/4 at columns
@@ -299,8 +307,8 @@ void dsa_bwd256_kernel(DsaBwdParams p) {
         for (int r = 0; r < 4; ++r) {
           const int rho = 16 * kt + 4 * grp + r;
           const uint32_t ds2 = pack_bf16x2(dsv[4 * kt + r], 0.f), p2 = pack_bf16x2(pv[4 * kt + r], 0.f);
-          *reinterpret_cast<uint16_t*>(xk + rho * (HPB * 2) + 2 * hl_) = (uint16_t)ds2;
-          *reinterpret_cast<uint16_t*>(xp + rho * (HPB * 2) + 2 * hl_) = (uint16_t)p2;
+          *reinterpret_cast<uint16_t*>(xk + xoff(rho, 2 * hl_)) = (uint16_t)ds2;
+          *reinterpret_cast<uint16_t*>(xp + xoff(rho, 2 * hl_)) = (uint16_t)p2;
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -332,9 +340,9 @@ void dsa_bwd256_kernel(DsaBwdParams p) {
         bf16x8 bk[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const unsigned char* rp = xs + rho * (HPB * 2) + 2 * (32 * ks + 4 * grp);
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(rp);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(rp + 32);
+          const int hb = 2 * (32 * ks + 4 * grp);  // heads 32ks + 4grp .. +3, then 16 further
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(xs + xoff(rho, hb));
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(xs + xoff(rho, hb + 32));
           bk[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
         }
         const int slot = sslot[tt * TK + entry_of(rho)];
