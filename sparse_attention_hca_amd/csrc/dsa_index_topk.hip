@@ -22,6 +22,8 @@
 //      that bin and gathers the bin, and 11- and 10-bit passes find T; rows
 //      whose boundary bin is too large use four radix passes over the row.  In
 //      every path keys > T and the lowest positions with key == T are emitted.
+#include <mutex>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -1001,21 +1003,79 @@ int chunk_rows(int n_rows, int row_len) {
 
 int64_t score_ld(int n_keys) { return ((int64_t)n_keys + 127) / 128 * 128; }
 
+// Number of score chunks of a call: the workspace holds two chunk buffers
+// when there is more than one, so that the selection of one chunk runs beside
+// the scores of the next.
+int64_t n_chunks(int batch, int seqlen, int R) { return (int64_t)batch * ((seqlen + R - 1) / R); }
+
+// The second stream of the chunk pipeline (default priority, non-blocking)
+// and its events, created once per device on first use.
+struct SideStream {
+  bool ready = false;
+  hipStream_t s = nullptr;
+  hipEvent_t sc[2] = {nullptr, nullptr};   // scores of buffer i written (recorded on the caller's stream)
+  hipEvent_t sel[2] = {nullptr, nullptr};  // selection of buffer i done (recorded on the side stream)
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream(SideStream*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.ready) {
+    e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&ss.sc[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.sel[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) return e;
+    ss.ready = true;
+  }
+  out = &ss;
+  return hipSuccess;
+}
+
 // Scores + selection of seqlen queries over n_keys keys of granularity block
-// (DSA: n_keys = seqlen, block = 1), in chunks of query rows.
+// (DSA: n_keys = seqlen, block = 1), in chunks of query rows.  With more than
+// one chunk the scores run on the caller's stream into two alternating
+// buffers and each chunk's selection runs on the side stream as soon as its
+// scores are written: the selection (memory-latency bound) overlaps the next
+// chunk's scores (matrix cores).  A buffer is rewritten only after the
+// selection that read it is done, and the caller's stream waits for the last
+// selection before anything queued after this call.  Enqueueing holds a lock,
+// so concurrent callers share the side stream in turn.
 hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
                                   int seqlen, int n_keys, int block, int h_i, int d_i, int topk, void* ws,
                                   hipStream_t st) {
   const int64_t ld = score_ld(n_keys);
   const int R = chunk_rows(seqlen, n_keys);
+  const bool overlap = n_chunks(batch, seqlen, R) > 1;
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  SideStream* ss = nullptr;
+  if (overlap) {
+    lock.lock();
+    hipError_t e = side_stream(ss);
+    if (e != hipSuccess) return e;
+  }
+  int c = 0;  // chunk counter over the call
   for (int b = 0; b < batch; ++b) {
-    for (int r0 = 0; r0 < seqlen; r0 += R) {
+    for (int r0 = 0; r0 < seqlen; r0 += R, ++c) {
       const int rows = min(R, seqlen - r0);
+      float* buf = (float*)ws + (overlap ? (size_t)(c & 1) * (size_t)R * (size_t)ld : 0);
+      hipStream_t sel_st = st;
+      if (overlap) {
+        // the selection that last read this buffer is done
+        hipError_t e = hipStreamWaitEvent(st, ss->sel[c & 1], 0);
+        if (e != hipSuccess) return e;
+      }
       ScoreParams sp;
       sp.qI = qI + (int64_t)b * seqlen * h_i * d_i;
       sp.kI = kI + (int64_t)b * n_keys * d_i;
       sp.w = w + (int64_t)b * seqlen * h_i;
-      sp.sc = (float*)ws;
+      sp.sc = buf;
       sp.ld = ld;
       sp.seqlen = seqlen;
       sp.h_i = h_i;
@@ -1052,17 +1112,29 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
+      if (overlap) {
+        hipError_t e = hipEventRecord(ss->sc[c & 1], st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->sc[c & 1], 0);
+        if (e != hipSuccess) return e;
+        sel_st = ss->s;
+      }
       SelectParams pp{};
-      pp.sc = (const float*)ws;
+      pp.sc = buf;
       pp.ld = ld;
       pp.idx = idx + (int64_t)b * seqlen * topk;
       pp.r0 = r0;
       pp.topk = topk;
       pp.block = block;
-      hipLaunchKernelGGL(topk_select_kernel<false>, dim3(rows), dim3(256), 0, st, pp);
+      hipLaunchKernelGGL(topk_select_kernel<false>, dim3(rows), dim3(256), 0, sel_st, pp);
       hipError_t e = hipGetLastError();
+      if (e == hipSuccess && overlap) e = hipEventRecord(ss->sel[c & 1], ss->s);
       if (e != hipSuccess) return e;
     }
+  }
+  if (overlap) {
+    // the caller's stream sees every selection (the side stream runs them in order)
+    hipError_t e = hipStreamWaitEvent(st, ss->sel[(c - 1) & 1], 0);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -1070,9 +1142,9 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
 }  // namespace
 
 size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk) {
-  (void)batch;
   (void)topk;
-  return (size_t)chunk_rows(seqlen, seqlen) * score_ld(seqlen) * sizeof(float);
+  const int R = chunk_rows(seqlen, seqlen);
+  return (n_chunks(batch, seqlen, R) > 1 ? 2 : 1) * (size_t)R * score_ld(seqlen) * sizeof(float);
 }
 
 hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* w, int32_t* idx, int batch,
@@ -1082,9 +1154,9 @@ hipError_t launch_dsa_index_topk(const float* qI, const float* kI, const float* 
 }
 
 size_t csa_topk_workspace_bytes(int batch, int seqlen, int n_keys, int topk) {
-  (void)batch;
   (void)topk;
-  return (size_t)chunk_rows(seqlen, n_keys) * score_ld(n_keys) * sizeof(float);
+  const int R = chunk_rows(seqlen, n_keys);
+  return (n_chunks(batch, seqlen, R) > 1 ? 2 : 1) * (size_t)R * score_ld(n_keys) * sizeof(float);
 }
 
 hipError_t launch_csa_index_topk(const float* qI, const float* kIc, const float* w, int32_t* idx, int batch,

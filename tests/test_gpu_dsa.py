@@ -31,8 +31,11 @@ def _sorted_rows(idx):
     return out
 
 
-@pytest.mark.parametrize("S,topk,B", [(1500, 256, 1), (700, 64, 2), (300, 512, 1), (1000, 100, 1)])
+@pytest.mark.parametrize("S,topk,B", [(1500, 256, 1), (700, 64, 2), (300, 512, 1), (1000, 100, 1), (500, 48, 5)])
 def test_index_topk_exact_sets(S, topk, B):
+    """Exact sets on tie-free rows; more than one chunk (here one per sequence)
+    runs each chunk's selection on the side stream beside the next chunk's
+    scores, with the two score buffers reused in turn (B = 5)."""
     cfg = synth.small_dsa(seqlen=S, topk=topk, batch=B)
     _say("index_topk", cfg)
     inp = make_tie_free(cfg)
