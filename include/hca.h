@@ -217,7 +217,8 @@ hca_status_t hca_attn_fwd_noalloc(hca_dtype_t dt,
                                   int h_q, int h_kv, int head_dim, int block, int window, float scale,
                                   void* stream);
 
-/* Workspace bytes dsa_index_topk needs (score rows for one chunk of queries). */
+/* Workspace bytes dsa_index_topk needs: score rows for one chunk of queries,
+ * two chunks' worth when the call has more than one chunk. */
 size_t dsa_index_topk_workspace_size(int batch, int seqlen, int topk);
 
 /*
@@ -233,6 +234,12 @@ size_t dsa_index_topk_workspace_size(int batch, int seqlen, int topk);
  *   w_idx: [batch, seqlen, h_i]      fp32 contiguous (read)
  *   idx  : [batch, seqlen, topk]     int32 contiguous (written)
  * Supported: h_i <= 8, d_i a multiple of 16 and <= 128, topk <= 4096.
+ * Streams: the scores run on `stream` in chunks of query rows.  When there
+ * is more than one chunk, each chunk's selection runs on a library-owned
+ * second stream of the current device (default priority, created on first
+ * use), ordered by events.  `stream` waits for the last selection before any
+ * work queued after the call, so the call behaves as if it ran entirely on
+ * `stream`.  Calls from several host threads take the second stream in turn.
  */
 hca_status_t dsa_index_topk(const float* q_idx, const float* k_idx, const float* w_idx,
                             int32_t* idx,
@@ -327,7 +334,8 @@ hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
  * complete: block*j + block - 1 <= t.
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes csa_index_topk needs (score rows for one chunk of queries). */
+/* Workspace bytes csa_index_topk needs: score rows for one chunk of queries,
+ * two chunks' worth when the call has more than one chunk. */
 size_t csa_index_topk_workspace_size(int batch, int seqlen, int n_entries, int topk);
 
 /*
@@ -344,6 +352,8 @@ size_t csa_index_topk_workspace_size(int batch, int seqlen, int n_entries, int t
  * needs more entries), for NULL or misaligned tensors, or when idx overlaps an
  * input; HCA_ERR_WORKSPACE for a missing or short workspace.
  * Supported: h_i in {4, 8}, d_i a multiple of 16 <= 128, topk <= 4096.
+ * Streams: as dsa_index_topk (selections of all but a single chunk run on the
+ * library's second stream; `stream` waits for them).
  */
 hca_status_t csa_index_topk(const float* q_idx, const float* k_idx, const float* w_idx,
                             int32_t* idx,
