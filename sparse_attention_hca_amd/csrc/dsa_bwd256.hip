@@ -31,6 +31,8 @@
 // fixed workspace; each chunk's reduction adds into dk, dv.  (fp32 atomics
 // instead of the sorted rows: measured ~1.3 TB/s of row updates on MI355X,
 // five times slower than writing and re-reading bf16 rows.)
+#include <mutex>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -492,6 +494,39 @@ int chunk_queries(int seqlen, int topk, int G) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// One set of chunk buffers: counts -> offsets, cursors, slots, contribution rows.
+size_t chunk_set_bytes(int n_kv, int cq, int topk, int G) {
+  return align256((size_t)(n_kv + 1) * 4) + align256((size_t)n_kv * 4) + align256((size_t)cq * topk * 4) +
+         align256((size_t)cq * topk * G * CROW * 2);
+}
+
+// Events of the backward's chunk pipeline, created once per device.
+struct BwdEvents {
+  bool ready = false;
+  hipEvent_t start = nullptr;                // the caller's stream reached the call (dk, dv zeroed)
+  hipEvent_t idx[2] = {nullptr, nullptr};    // inverted index of buffer set i built (side stream)
+  hipEvent_t main[2] = {nullptr, nullptr};   // contributions of buffer set i written (caller's stream)
+  hipEvent_t end = nullptr;                  // last reduction done (side stream)
+};
+std::mutex g_bwd_mu;
+BwdEvents g_bwd_ev[64];
+
+hipError_t bwd_events(BwdEvents*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  BwdEvents& ev = g_bwd_ev[dev];
+  if (!ev.ready) {
+    hipEvent_t* all[6] = {&ev.start, &ev.idx[0], &ev.idx[1], &ev.main[0], &ev.main[1], &ev.end};
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(all[i], hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    ev.ready = true;
+  }
+  out = &ev;
+  return hipSuccess;
+}
+
 }  // namespace
 
 bool dsa_bwd_uses_mfma(int dt, int d_qk, int d_v, int h_q, int h_kv) {
@@ -499,30 +534,47 @@ bool dsa_bwd_uses_mfma(int dt, int d_qk, int d_v, int h_q, int h_kv) {
 }
 
 size_t dsa_bwd256_workspace_bytes(int batch, int seqlen, int h_q, int h_kv, int topk) {
-  (void)batch;
   const int G = h_kv * (h_q / h_kv / HPB);
   const int cq = chunk_queries(seqlen, topk, G);
-  size_t bytes = align256((size_t)(seqlen + 1) * 4);            // counts -> offsets
-  bytes += align256((size_t)seqlen * 4);                         // cursors
-  bytes += align256((size_t)cq * topk * 4);                      // slots
-  bytes += align256((size_t)cq * topk * G * CROW * 2);           // contribution rows
-  bytes += (size_t)cq * G * CROW * 2;                            // one dummy row per workgroup
-  return bytes;
+  const int64_t chunks = (int64_t)batch * ((seqlen + cq - 1) / cq);
+  return (chunks > 1 ? 2 : 1) * chunk_set_bytes(seqlen, cq, topk, G)  // one or two buffer sets
+         + (size_t)cq * G * CROW * 2;                                 // one dummy row per workgroup
 }
 
+// The call runs in chunks of cq queries; chunk c uses buffer set c % 2.  With
+// more than one chunk the inverted index of each chunk (zero, count, scan,
+// fill) and its per-position reduction run on the library's side stream, and
+// the MFMA kernel on the caller's stream, ordered by events: the MFMA kernel
+// of chunk c needs its index; its reduction needs its contributions; the index
+// of chunk c + 2 (same buffer set) is built after the reduction of chunk c,
+// and the MFMA kernel of chunk c + 2 waits for that index, hence for the
+// reduction too.  So the reduction of chunk c - 1 and the index of chunk c + 1
+// run beside the MFMA kernel of chunk c.  The reductions add into dk, dv in
+// chunk order on the one side stream.
 hipError_t launch_dsa_bwd256(const BwdArgs& a, void* ws, hipStream_t st) {
   const int group = a.h_q / a.h_kv;
   const int n_hb = group / HPB, G = a.h_kv * n_hb;
   const int cq = chunk_queries(a.seqlen_q, a.topk, G);
+  if (a.topk > MAX_TOPK) return hipErrorInvalidValue;
+  const int per_batch = (a.seqlen_q + cq - 1) / cq;
+  const int total = a.batch * per_batch;
+  const bool overlap = total > 1;
+
+  struct Set {
+    int32_t *cnt, *cur, *pslot;
+    uint16_t* contrib;
+  } set[2];
   char* pw = (char*)ws;
-  int32_t* cnt = (int32_t*)pw;
-  pw += align256((size_t)(a.seqlen_kv + 1) * 4);
-  int32_t* cur = (int32_t*)pw;
-  pw += align256((size_t)a.seqlen_kv * 4);
-  int32_t* pslot = (int32_t*)pw;
-  pw += align256((size_t)cq * a.topk * 4);
-  uint16_t* contrib = (uint16_t*)pw;
-  pw += align256((size_t)cq * a.topk * G * CROW * 2);
+  for (int k = 0; k < (overlap ? 2 : 1); ++k) {
+    set[k].cnt = (int32_t*)pw;
+    pw += align256((size_t)(a.seqlen_kv + 1) * 4);
+    set[k].cur = (int32_t*)pw;
+    pw += align256((size_t)a.seqlen_kv * 4);
+    set[k].pslot = (int32_t*)pw;
+    pw += align256((size_t)cq * a.topk * 4);
+    set[k].contrib = (uint16_t*)pw;
+    pw += align256((size_t)cq * a.topk * G * CROW * 2);
+  }
   uint16_t* dummy = (uint16_t*)pw;
 
   DsaBwdParams p;
@@ -530,33 +582,80 @@ hipError_t launch_dsa_bwd256(const BwdArgs& a, void* ws, hipStream_t st) {
   p.o = (const uint16_t*)a.o; p.dout = (const uint16_t*)a.dout;
   p.sq = a.sq; p.sk = a.sk; p.sv = a.sv; p.so = a.so; p.sdo = a.sdo;
   p.lse = a.lse; p.idx = a.idx; p.dq = a.dq; p.sdq = a.sdq;
-  p.pslot = pslot; p.contrib = contrib; p.dummy = dummy;
+  p.dummy = dummy;
   p.seqlen = a.seqlen_q; p.n_kv = a.seqlen_kv; p.h_q = a.h_q; p.h_kv = a.h_kv; p.topk = a.topk;
   p.n_hb = n_hb; p.G = G;
   p.scale = a.scale; p.c = a.scale * kLog2e;
-  if (a.topk > MAX_TOPK) return hipErrorInvalidValue;
+
+  std::unique_lock<std::mutex> lock(g_bwd_mu, std::defer_lock);
+  BwdEvents* ev = nullptr;
+  hipStream_t side = st;
+  if (overlap) {
+    lock.lock();
+    hipError_t e = bwd_events(ev);
+    if (e == hipSuccess) e = side_stream(&side);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipSuccess;
+  // dk, dv of every sequence start at zero; the side stream starts after them
+  // (and after everything queued before this call)
   for (int b = 0; b < a.batch; ++b) {
-    p.b = b;
     hipLaunchKernelGGL(zero_rows_kernel, dim3(1024), dim3(256), 0, st, a.dk, a.sdk, b, a.seqlen_kv, a.h_kv, a.d);
     hipLaunchKernelGGL(zero_rows_kernel, dim3(1024), dim3(256), 0, st, a.dv, a.sdv, b, a.seqlen_kv, a.h_kv, a.d_v);
-    for (int q0 = 0; q0 < a.seqlen_q; q0 += cq) {
-      const int nq = cq < a.seqlen_q - q0 ? cq : a.seqlen_q - q0;
-      const int64_t ne = (int64_t)nq * a.topk;
-      const int gx = (int)((ne + 255) / 256 < 4096 ? (ne + 255) / 256 : 4096);
-      hipLaunchKernelGGL(fill_i32_kernel, dim3(256), dim3(256), 0, st, cnt, (int64_t)a.seqlen_kv + 1);
-      hipLaunchKernelGGL(fill_i32_kernel, dim3(256), dim3(256), 0, st, cur, (int64_t)a.seqlen_kv);
-      hipLaunchKernelGGL(chunk_count_kernel, dim3(gx), dim3(256), 0, st, a.idx, b, a.seqlen_q, a.seqlen_kv, a.topk,
-                         q0, nq, cnt);
-      hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(256), 0, st, cnt, a.seqlen_kv);
-      hipLaunchKernelGGL(chunk_fill_kernel, dim3(gx), dim3(256), 0, st, a.idx, b, a.seqlen_q, a.seqlen_kv, a.topk, q0,
-                         nq, (const int32_t*)cnt, cur, pslot);
-      p.q0 = q0;
-      hipLaunchKernelGGL(dsa_bwd256_kernel, dim3(nq, a.h_kv * n_hb), dim3(256), 0, st, p);
-      hipLaunchKernelGGL(chunk_reduce_kernel, dim3(a.seqlen_kv, a.h_kv), dim3(64), 0, st, (const uint16_t*)contrib,
-                         (const int32_t*)cnt, G, n_hb, a.dk, a.sdk, a.dv, a.sdv, b);
-    }
   }
-  return hipGetLastError();
+  if (overlap) {
+    e = hipEventRecord(ev->start, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev->start, 0);
+    if (e != hipSuccess) return e;
+  }
+  auto chunk_b = [&](int c) { return c / per_batch; };
+  auto chunk_q0 = [&](int c) { return (c % per_batch) * cq; };
+  auto chunk_nq = [&](int c) { return cq < a.seqlen_q - chunk_q0(c) ? cq : a.seqlen_q - chunk_q0(c); };
+  auto build_index = [&](int c) -> hipError_t {
+    const Set& S = set[c & 1];
+    const int b = chunk_b(c), q0 = chunk_q0(c), nq = chunk_nq(c);
+    const int64_t ne = (int64_t)nq * a.topk;
+    const int gx = (int)((ne + 255) / 256 < 4096 ? (ne + 255) / 256 : 4096);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(256), dim3(256), 0, side, S.cnt, (int64_t)a.seqlen_kv + 1);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(256), dim3(256), 0, side, S.cur, (int64_t)a.seqlen_kv);
+    hipLaunchKernelGGL(chunk_count_kernel, dim3(gx), dim3(256), 0, side, a.idx, b, a.seqlen_q, a.seqlen_kv, a.topk,
+                       q0, nq, S.cnt);
+    hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(256), 0, side, S.cnt, a.seqlen_kv);
+    hipLaunchKernelGGL(chunk_fill_kernel, dim3(gx), dim3(256), 0, side, a.idx, b, a.seqlen_q, a.seqlen_kv, a.topk, q0,
+                       nq, (const int32_t*)S.cnt, S.cur, S.pslot);
+    hipError_t r = hipGetLastError();
+    if (r == hipSuccess && overlap) r = hipEventRecord(ev->idx[c & 1], side);
+    return r;
+  };
+  e = build_index(0);
+  if (e == hipSuccess && total > 1) e = build_index(1);
+  for (int c = 0; c < total && e == hipSuccess; ++c) {
+    const Set& S = set[c & 1];
+    if (overlap) e = hipStreamWaitEvent(st, ev->idx[c & 1], 0);
+    if (e != hipSuccess) break;
+    p.b = chunk_b(c);
+    p.q0 = chunk_q0(c);
+    p.pslot = S.pslot;
+    p.contrib = S.contrib;
+    hipLaunchKernelGGL(dsa_bwd256_kernel, dim3(chunk_nq(c), a.h_kv * n_hb), dim3(256), 0, st, p);
+    e = hipGetLastError();
+    if (e == hipSuccess && overlap) {
+      e = hipEventRecord(ev->main[c & 1], st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side, ev->main[c & 1], 0);
+    }
+    if (e != hipSuccess) break;
+    hipLaunchKernelGGL(chunk_reduce_kernel, dim3(a.seqlen_kv, a.h_kv), dim3(64), 0, side, (const uint16_t*)S.contrib,
+                       (const int32_t*)S.cnt, G, n_hb, a.dk, a.sdk, a.dv, a.sdv, chunk_b(c));
+    e = hipGetLastError();
+    if (e == hipSuccess && c + 2 < total) e = build_index(c + 2);
+  }
+  if (e == hipSuccess && overlap) {
+    // the caller's stream waits for the last reduction (the side stream runs
+    // every earlier one before it)
+    e = hipEventRecord(ev->end, side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, ev->end, 0);
+  }
+  return e;
 }
 
 }  // namespace hca

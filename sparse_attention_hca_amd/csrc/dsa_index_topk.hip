@@ -1008,33 +1008,30 @@ int64_t score_ld(int n_keys) { return ((int64_t)n_keys + 127) / 128 * 128; }
 // the scores of the next.
 int64_t n_chunks(int batch, int seqlen, int R) { return (int64_t)batch * ((seqlen + R - 1) / R); }
 
-// The second stream of the chunk pipeline (default priority, non-blocking)
-// and its events, created once per device on first use.
-struct SideStream {
+// Events of the indexer's chunk pipeline, created once per device on first use.
+struct IndexEvents {
   bool ready = false;
-  hipStream_t s = nullptr;
   hipEvent_t sc[2] = {nullptr, nullptr};   // scores of buffer i written (recorded on the caller's stream)
   hipEvent_t sel[2] = {nullptr, nullptr};  // selection of buffer i done (recorded on the side stream)
 };
-std::mutex g_side_mu;
-SideStream g_side[64];
+std::mutex g_index_mu;
+IndexEvents g_index_ev[64];
 
-hipError_t side_stream(SideStream*& out) {
+hipError_t index_events(IndexEvents*& out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  SideStream& ss = g_side[dev];
-  if (!ss.ready) {
-    e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+  IndexEvents& ev = g_index_ev[dev];
+  if (!ev.ready) {
     for (int i = 0; i < 2 && e == hipSuccess; ++i) {
-      e = hipEventCreateWithFlags(&ss.sc[i], hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.sel[i], hipEventDisableTiming);
+      e = hipEventCreateWithFlags(&ev.sc[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ev.sel[i], hipEventDisableTiming);
     }
     if (e != hipSuccess) return e;
-    ss.ready = true;
+    ev.ready = true;
   }
-  out = &ss;
+  out = &ev;
   return hipSuccess;
 }
 
@@ -1053,11 +1050,13 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
   const int64_t ld = score_ld(n_keys);
   const int R = chunk_rows(seqlen, n_keys);
   const bool overlap = n_chunks(batch, seqlen, R) > 1;
-  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
-  SideStream* ss = nullptr;
+  std::unique_lock<std::mutex> lock(g_index_mu, std::defer_lock);
+  IndexEvents* ev = nullptr;
+  hipStream_t side = nullptr;
   if (overlap) {
     lock.lock();
-    hipError_t e = side_stream(ss);
+    hipError_t e = index_events(ev);
+    if (e == hipSuccess) e = side_stream(&side);
     if (e != hipSuccess) return e;
   }
   int c = 0;  // chunk counter over the call
@@ -1068,7 +1067,7 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
       hipStream_t sel_st = st;
       if (overlap) {
         // the selection that last read this buffer is done
-        hipError_t e = hipStreamWaitEvent(st, ss->sel[c & 1], 0);
+        hipError_t e = hipStreamWaitEvent(st, ev->sel[c & 1], 0);
         if (e != hipSuccess) return e;
       }
       ScoreParams sp;
@@ -1113,10 +1112,10 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
         if (e != hipSuccess) return e;
       }
       if (overlap) {
-        hipError_t e = hipEventRecord(ss->sc[c & 1], st);
-        if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->sc[c & 1], 0);
+        hipError_t e = hipEventRecord(ev->sc[c & 1], st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev->sc[c & 1], 0);
         if (e != hipSuccess) return e;
-        sel_st = ss->s;
+        sel_st = side;
       }
       SelectParams pp{};
       pp.sc = buf;
@@ -1127,19 +1126,38 @@ hipError_t launch_index_topk_rows(const float* qI, const float* kI, const float*
       pp.block = block;
       hipLaunchKernelGGL(topk_select_kernel<false>, dim3(rows), dim3(256), 0, sel_st, pp);
       hipError_t e = hipGetLastError();
-      if (e == hipSuccess && overlap) e = hipEventRecord(ss->sel[c & 1], ss->s);
+      if (e == hipSuccess && overlap) e = hipEventRecord(ev->sel[c & 1], side);
       if (e != hipSuccess) return e;
     }
   }
   if (overlap) {
     // the caller's stream sees every selection (the side stream runs them in order)
-    hipError_t e = hipStreamWaitEvent(st, ss->sel[(c - 1) & 1], 0);
+    hipError_t e = hipStreamWaitEvent(st, ev->sel[(c - 1) & 1], 0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 }  // namespace
+
+hipError_t side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      streams[dev] = nullptr;
+      return e;
+    }
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
 
 size_t dsa_topk_workspace_bytes(int batch, int seqlen, int topk) {
   (void)topk;

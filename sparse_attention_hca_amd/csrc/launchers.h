@@ -86,6 +86,10 @@ hipError_t launch_hca_attn_bwd512(BwdArgs a, void* ws, hipStream_t st, const flo
 // bf16 with d_qk = d_v = 256 and a multiple of 64 query heads per KV head runs
 // the MFMA kernels (dsa_bwd256.hip); everything else the generic ones.
 bool dsa_bwd_uses_mfma(int dt, int d_qk, int d_v, int h_q, int h_kv);
+// The library's second stream of the current device (default priority,
+// non-blocking; created on first use): chunk pipelines run their side work on
+// it, ordered against the caller's stream by events.
+hipError_t side_stream(hipStream_t* out);
 size_t dsa_bwd256_workspace_bytes(int batch, int seqlen, int h_q, int h_kv, int topk);
 hipError_t launch_dsa_bwd256(const BwdArgs& a, void* ws, hipStream_t st);
 size_t dsa_bwd_workspace_bytes(int dt, int batch, int seqlen, int h_q, int h_kv, int d_qk, int d_v, int topk);
