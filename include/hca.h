@@ -550,7 +550,8 @@ hca_status_t hca_attn_compress_bwd(hca_dtype_t dt,
 /* Workspace bytes dsa_sparse_attn_bwd needs for these arguments (0 for
  * invalid sizes): an inverted index of idx, and on the bf16 / 256-wide path
  * the position-ordered contribution rows of one chunk of queries (at most
- * 8 GiB plus the index; proportionally less for short sequences). */
+ * 8 GiB plus the index; proportionally less for short sequences), twice when
+ * the call has more than one chunk (the chunks are pipelined). */
 size_t dsa_sparse_attn_bwd_workspace_size(hca_dtype_t dt, int batch, int seqlen, int h_q, int h_kv, int d_qk,
                                           int d_v, int topk);
 
@@ -572,7 +573,10 @@ size_t dsa_sparse_attn_bwd_workspace_size(hca_dtype_t dt, int batch, int seqlen,
  * over the gathered rows, dq accumulated in fp32, each (query, position)
  * pair's dk and dv contributions written as bf16 rows ordered by position and
  * summed in fp32 per position, queries taken in chunks (launches several
- * kernels per chunk); everything else the generic fp32 kernels.
+ * kernels per chunk; with more than one chunk, each chunk's index building
+ * and reduction run on the library's second stream of the current device
+ * beside the next chunk's MFMA kernel, ordered by events, and `stream` waits
+ * for the last of them); everything else the generic fp32 kernels.
  * Errors: HCA_ERR_INVALID for bad pointers, sizes or overlaps;
  * HCA_ERR_WORKSPACE for a missing or short workspace.
  * Supported: fp32 and bf16, d_qk and d_v <= 512 (multiples of 4), any
