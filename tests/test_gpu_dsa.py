@@ -62,6 +62,32 @@ def test_index_topk_indexer_shapes(h_i, d_i):
     assert np.array_equal(got, ref)
 
 
+def test_index_topk_on_other_streams_and_back_to_back():
+    """The chunk pipeline orders its side stream against whatever stream the
+    caller runs on: a call on a second torch stream, and two calls queued back
+    to back on it (the second rewrites the same workspace and output while the
+    first's selections may still run), give the default stream's sets."""
+    cfg = synth.small_dsa(seqlen=500, topk=48, batch=5)
+    _say("index_topk streams", cfg)
+    inp = make_tie_free(cfg)
+    qI, kI, w = dev_f32(inp["qI"]), dev_f32(inp["kI"]), dev_f32(inp["w"])
+    ref = hca.dsa_index_topk(qI, kI, w, cfg.topk)
+    torch.cuda.synchronize()
+    ref = _sorted_rows(ref.cpu().numpy())
+    s = torch.cuda.Stream()
+    ws = torch.empty(hca.dsa_index_topk_workspace_size(cfg.batch, cfg.seqlen, cfg.topk), dtype=torch.uint8,
+                     device="cuda:0")
+    out = torch.full((cfg.batch, cfg.seqlen, cfg.topk), -7, dtype=torch.int32, device="cuda:0")
+    with torch.cuda.stream(s):
+        hca.dsa_index_topk(qI, kI, w, cfg.topk, idx=out, workspace=ws)
+        first = out.clone()
+        hca.dsa_index_topk(qI, kI, w, cfg.topk, idx=out, workspace=ws)
+        second = out.clone()
+    s.synchronize()
+    assert np.array_equal(_sorted_rows(first.cpu().numpy()), ref)
+    assert np.array_equal(_sorted_rows(second.cpu().numpy()), ref)
+
+
 def test_index_topk_long_rows_exact():
     """Rows of 4096+ positions take the sampling selection path; tie-free rows
     must give exactly the oracle's sets."""
