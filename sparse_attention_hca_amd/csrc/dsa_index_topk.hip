@@ -6,7 +6,9 @@
 //   s(t, u) = sum_h w[t,h] * max(0, <qI[t,h,:], kI[u,:]>),  u <= t, fp32
 //
 // Two kernels per chunk of query rows (the host walks the chunks so the score
-// workspace stays bounded):
+// workspace stays bounded; with more than one chunk each chunk's selection
+// runs on the library's second stream beside the next chunk's scores, the
+// scores alternating between two buffers):
 //   1. index_scores: fp32 matrix cores (v_mfma_f32_32x32x2_f32).  One wave
 //      computes a 32-key x 32-query tile of S^T per index head and folds it
 //      as w * relu(.) into the score tile; operands come straight from global
@@ -20,7 +22,10 @@
 //      Otherwise (short rows, or a bracket that missed) an 11-bit LDS
 //      histogram locates the bin of T, one ordered pass emits everything above
 //      that bin and gathers the bin, and 11- and 10-bit passes find T; rows
-//      whose boundary bin is too large use four radix passes over the row.  In
+//      whose boundary bin is too large use four radix passes over the row.  A
+//      bracket that holds the k-th key but too many candidates (a mass of
+//      equal scores) first tries one histogram pass over the bracket: when the
+//      k-th key's bin holds a single value, one ordered pass finishes.  In
 //      every path keys > T and the lowest positions with key == T are emitted.
 #include <mutex>
 
