@@ -24,9 +24,12 @@
  *     (stride 1).  The other three axes take element strides through
  *     hca_strides_t.  Base pointers must be 16-byte aligned and every stride
  *     a multiple of 16 bytes.
- *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
- *     enqueued; no call synchronizes.  Device faults surface at the caller's
- *     next synchronization.
+ *   - `stream` is a hipStream_t (NULL = the default stream) of the current
+ *     device.  Work is only enqueued; no call synchronizes.  Device faults
+ *     surface at the caller's next synchronization.  The chunked calls
+ *     (dsa_index_topk, csa_index_topk, dsa_sparse_attn_bwd) may run part of
+ *     their work on a library-owned second stream of the current device,
+ *     joined back to `stream` by events before they return.
  *   - Errors: every argument is validated before anything is launched, so a
  *     call that returns an error has written nothing.  hca_last_error()
  *     returns a message for the last non-OK status on the calling thread.
