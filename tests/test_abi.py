@@ -249,7 +249,11 @@ def test_dsa_bwd_rejects_bad_arguments():
     assert need >= 100 * 8 * 4 + 100 * 16 * 4
     # the bf16 / 256-wide path keeps one chunk of position-ordered contribution rows (1 KB per entry here)
     assert lib.dsa_sparse_attn_bwd_workspace_size(1, 1, 300, 64, 1, 256, 256, 16) >= 300 * 16 * 1024
-    assert lib.dsa_sparse_attn_bwd_workspace_size(1, 1, 1 << 16, 64, 1, 256, 256, 2048) < (9 << 30)
+    # two buffer sets (chunks are pipelined), each at most 8 GiB of rows plus its index
+    assert lib.dsa_sparse_attn_bwd_workspace_size(1, 1, 1 << 16, 64, 1, 256, 256, 2048) < (18 << 30)
+    # one chunk only: one buffer set
+    one = lib.dsa_sparse_attn_bwd_workspace_size(1, 1, 300, 64, 1, 256, 256, 16)
+    assert one < 2 * 300 * 16 * 1024 + (1 << 20)
     assert lib.dsa_sparse_attn_bwd_workspace_size(7, 1, 100, 8, 2, 64, 64, 16) == 0
     sq = S(0, 8 * 64, 64)
     skv = S(0, 2 * 64, 64)
