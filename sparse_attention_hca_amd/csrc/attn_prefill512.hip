@@ -155,9 +155,6 @@ void prefill512_kernel(PrefillParams p) {
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * ks));
-    // settle the Q loads before the DMA pipeline (its waits are explicit)
-#pragma unroll
-    for (int ks = 0; ks < 32; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   const uint16_t* kcb = (const uint16_t*)a.kc + b * a.skc.b + (int64_t)g * a.skc.h;
@@ -430,6 +427,11 @@ void prefill512_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) dma_row(sk0, i);
       }
+      // The first K tile's DMA goes out while the Q loads are still in flight.
+      // The compiler's waits for Q (its loads were issued before the DMA, and
+      // loads complete in order) and the explicit wait below leave both landed.
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) asm volatile("" ::"v"(qf[ks]));
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       tile(F_{}, 0);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
