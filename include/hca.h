@@ -170,10 +170,11 @@ size_t hca_attn_fwd_workspace_size(int batch, int seqlen_q, int h_q, int h_kv, i
  * h_q % h_kv != 0, window < 1 or block < 1.
  * Kernels: bf16 with head_dim 512 runs the MFMA prefill kernel (seqlen_q > 1)
  * or the split-key decode kernel (seqlen_q == 1, which uses the workspace);
- * fp32 with head_dim 32, 64 or 128 runs the fp32 MFMA kernel (64 queries per
- * workgroup, any number of keys); fp32 with another head_dim (multiple of 4)
- * and bf16 with another head_dim (multiple of 8), both <= 512, run a
- * one-query-per-workgroup kernel limited to 16384 keys per query.
+ * fp32 with head_dim 32, 64 or 128 and bf16 with head_dim 64, 128 or 256 run
+ * MFMA kernels of 64 queries per workgroup (any number of keys); fp32 with
+ * another head_dim (multiple of 4) and bf16 with another head_dim (multiple
+ * of 8), both <= 512, run a one-query-per-workgroup kernel limited to 16384
+ * keys per query (HCA_ERR_UNSUPPORTED beyond).
  */
 hca_status_t hca_attn_fwd(hca_dtype_t dt,
                           const void* q, hca_strides_t sq,

@@ -20,6 +20,7 @@ SOURCES = [
     "append.hip",
     "attn_generic.hip",
     "attn_f32mfma.hip",
+    "attn_bf16mfma.hip",
     "attn_prefill512.hip",
     "attn_decode512.hip",
     "dsa_index_topk.hip",

@@ -396,7 +396,12 @@ hca_status_t hca_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq, const
     if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd fp32 launch");
     return HCA_OK;
   }
-  // one-query-per-workgroup kernel: fp32 with other head sizes, bf16 with head sizes other than 512
+  if (hca::attn_bf16mfma_supports(a.dt, head_dim)) {
+    hipError_t e = hca::launch_attn_bf16mfma(a, st);
+    if (e != hipSuccess) return hip_fail(e, "hca_attn_fwd bf16 launch");
+    return HCA_OK;
+  }
+  // one-query-per-workgroup kernel: fp32 and bf16 with the remaining head sizes
   if (head_dim > 512 || (head_dim % (16 / (int)es)) != 0)
     return fail(HCA_ERR_UNSUPPORTED, "hca_attn_fwd: head_dim %d unsupported for this dtype", head_dim);
   if (n_keys_of(t1, window, block) > hca::kGenericMaxKeys)

@@ -42,6 +42,9 @@ hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t st);
 // fp32 with head_dim 32, 64 or 128: the fp32 MFMA kernel (attn_f32mfma.hip).
 bool attn_f32mfma_supports(int dt, int head_dim);
 hipError_t launch_attn_f32mfma(const AttnArgs& a, hipStream_t st);
+// bf16 with head_dim 64, 128 or 256: the bf16 MFMA kernel (attn_bf16mfma.hip).
+bool attn_bf16mfma_supports(int dt, int head_dim);
+hipError_t launch_attn_bf16mfma(const AttnArgs& a, hipStream_t st);
 
 // bf16, head_dim 512, MFMA prefill.
 hipError_t launch_attn_prefill512(const AttnArgs& a, hipStream_t st);

@@ -18,6 +18,8 @@ hipError_t launch_ring_write(int, const void*, LStrides, const void*, LStrides, 
 hipError_t launch_attn_generic(const AttnArgs&, hipStream_t) { return hit(); }
 bool attn_f32mfma_supports(int dt, int head_dim) { return dt == 0 && (head_dim == 32 || head_dim == 64 || head_dim == 128); }
 hipError_t launch_attn_f32mfma(const AttnArgs&, hipStream_t) { return hit(); }
+bool attn_bf16mfma_supports(int dt, int head_dim) { return dt == 1 && (head_dim == 64 || head_dim == 128 || head_dim == 256); }
+hipError_t launch_attn_bf16mfma(const AttnArgs&, hipStream_t) { return hit(); }
 hipError_t launch_attn_prefill512(const AttnArgs&, hipStream_t) { return hit(); }
 size_t decode512_workspace_bytes(int batch, int h_q, int, int n_keys) {
   return (size_t)batch * h_q * (size_t)(n_keys / 64 + 1) * 2056;

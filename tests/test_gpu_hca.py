@@ -138,6 +138,14 @@ PREFILL_CASES = [
     ("f32-block1", "f32", 97, 2, 2, 128, 1, 3),
     ("f32-window-covers", "f32", 70, 2, 2, 128, 128, 100),
     ("f32-tiny", "f32", 3, 1, 1, 128, 128, 128),
+    # the bf16 MFMA kernel for narrower heads (64, 128, 256)
+    ("bf16-d128-gqa", "bf16", 700, 4, 2, 128, 64, 100),
+    ("bf16-d256", "bf16", 500, 2, 2, 256, 128, 128),
+    ("bf16-d64-ragged", "bf16", 333, 3, 1, 64, 8, 50),
+    ("bf16-d128-window1", "bf16", 130, 1, 1, 128, 4, 1),
+    ("bf16-d256-block1", "bf16", 97, 2, 2, 256, 1, 3),
+    ("bf16-d64-window-covers", "bf16", 70, 2, 2, 64, 128, 100),
+    ("bf16-d128-tiny", "bf16", 3, 1, 1, 128, 128, 128),
 ]
 
 
@@ -155,6 +163,43 @@ def test_prefill_parity(name, dtype, S, H, Hkv, d, block, W):
     _say(f"  rel err {err:.3e}")
     assert err < tol
     assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
+def test_prefill_bf16_narrow_heads_beyond_generic_key_limit():
+    """bf16, head_dim 128, block 1: late queries see ~17000 keys, more than the
+    one-query-per-workgroup kernel takes; the MFMA kernel has no key limit.
+    Sampled rows (including both sides of 16384 visible keys) against the oracle."""
+    cfg = synth.small_prefill("c2", name="long-d128", seqlen=17000, h_q=2, h_kv=1, head_dim=128, block=1,
+                              window=4, std=1.0 / math.sqrt(128))
+    _say("prefill", cfg)
+    inp = synth.make_prefill(cfg)
+    kc, vc, o, lse = _run_prefill(cfg, inp)
+    rows = [0, 1, 3, 4, 5, 127, 128, 4095, 8191, 16386, 16387, 16388, 16999]
+    _, _, ro, rlse = _oracle_prefill(cfg, inp, rows=rows)
+    err = rel_err(host(o[:, rows]), ro)
+    _say(f"  rel err {err:.3e} on {len(rows)} rows")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse[:, :, rows]) - rlse)) < LSE_TOL
+
+
+def test_prefill_bf16_narrow_heads_decode_row():
+    """bf16 head_dim 256 decode (one query) runs the same MFMA kernel; it agrees
+    with the prefill row of the same position."""
+    cfg = synth.small_prefill("c2", name="dec-d256", seqlen=700, h_q=4, h_kv=2, head_dim=256, block=64,
+                              window=100, std=1.0 / math.sqrt(256))
+    inp = synth.make_prefill(cfg)
+    q, k, v = (_to_dev(inp, n) for n in ("q", "k", "v"))
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale)
+    t = 650
+    lo = t - cfg.window + 1
+    od, lsed = hca.hca_attn_fwd(q[:, t:t + 1], k[:, lo:t + 1], v[:, lo:t + 1], kc, vc, window=cfg.window,
+                                block=cfg.block, scale=cfg.scale, q_pos0=t, kv_pos0=lo)
+    torch.cuda.synchronize()
+    # same keys, different tile grouping of the online softmax: equal up to rounding
+    assert rel_err(host(od[:, 0]), host(o[:, t])) < 1e-2
+    assert np.max(np.abs(host(lsed[:, :, 0]) - host(lse[:, :, t]))) < 1e-4
 
 
 def test_prefill_unit_variance_logits():
