@@ -182,6 +182,34 @@ def test_prefill_bf16_narrow_heads_beyond_generic_key_limit():
     assert np.max(np.abs(host(lse[:, :, rows]) - rlse)) < LSE_TOL
 
 
+def test_prefill_bf16_narrow_heads_strided_views_batch2():
+    """bf16 head_dim 128, two sequences, grouped heads (8 on 2), with q, k, v
+    and o as non-contiguous views (padded head and position strides): the
+    kernel follows the strides the call passes."""
+    cfg = synth.small_prefill("c2", name="strided-d128", seqlen=300, h_q=8, h_kv=2, head_dim=128, block=32,
+                              window=50, batch=2, std=1.0 / math.sqrt(128))
+    inp = synth.make_prefill(cfg)
+
+    def padded(x):
+        B, S, H, d = x.shape
+        big = torch.full((B, S + 3, H + 1, d + 64), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        big[:, :S, :H, :d] = x
+        return big[:, :S, :H, :d]
+
+    q, k, v = (padded(_to_dev(inp, n)) for n in ("q", "k", "v"))
+    assert not q.is_contiguous()
+    w = dev_f32(inp["w"])
+    kc, vc = hca.hca_compress_kv(k, v, w, w, cfg.block)
+    o = padded(torch.zeros_like(_to_dev(inp, "q")))
+    _, lse = hca.hca_attn_fwd(q, k, v, kc, vc, window=cfg.window, block=cfg.block, scale=cfg.scale, o=o)
+    torch.cuda.synchronize()
+    _, _, ro, rlse = _oracle_prefill(cfg, inp)
+    err = rel_err(host(o), ro)
+    _say(f"  rel err {err:.3e}")
+    assert err < BF16_TOL
+    assert np.max(np.abs(host(lse) - rlse)) < LSE_TOL
+
+
 def test_prefill_bf16_narrow_heads_decode_row():
     """bf16 head_dim 256 decode (one query) runs the same MFMA kernel; it agrees
     with the prefill row of the same position."""
