@@ -255,6 +255,12 @@ constexpr int HB = 2048;   // bins of the first pass of the fast path (top 11 bi
 // candidates resolved in LDS; with HB this keeps the selection under 40 KB of
 // LDS, so four workgroups share a CU
 constexpr int CAP = 3840;
+// The first stage of a decode selection runs few, long rows (65536 keys, k =
+// 2048: the bracket admits ~3300 candidates with a spread of ~450, so about
+// one row in ten would exceed CAP and take the multi-pass paths, and the
+// slowest row sets the launch's time).  It uses this capacity instead (69 KB
+// of LDS, two workgroups per CU).
+constexpr int CAP_WIDE = 7680;
 
 // Descending prefix over nb bins held in hist[] (256 threads, nb a multiple
 // of 256): returns in sel[0] the bin holding the need-th largest element and in
@@ -379,11 +385,13 @@ constexpr int NS = 1024;  // samples of a row used to bracket the k-th largest k
 // rather than being the element index; without it the row scans hold no
 // load besides the row's own, so the next step's loads stay in flight while
 // a step's elements are emitted.
-template <bool POS>
+// CAPN: the candidate capacity in LDS (CAP by default; see CAP_WIDE).
+template <bool POS, int CAPN = CAP>
 __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
+  static_assert(CAPN % 256 == 0 && CAPN >= 2048, "the candidate arrays double as 2048-bin tables");
   __shared__ uint32_t hist[HB];
-  __shared__ uint32_t ckey[CAP];
-  __shared__ int cpos[CAP];
+  __shared__ uint32_t ckey[CAPN];
+  __shared__ int cpos[CAPN];
   __shared__ uint32_t part[4];
   __shared__ uint32_t sel_info[4];
   __shared__ uint32_t wave_cnt[4];
@@ -505,7 +513,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
           // select the element by the bits of its index (no dynamic register indexing)
           const f32x4 h = (bit & 8) ? ((bit & 4) ? v3 : v2) : ((bit & 4) ? v1 : v0);
           const float x = (bit & 2) ? ((bit & 1) ? h[3] : h[2]) : ((bit & 1) ? h[1] : h[0]);
-          if (oi < (uint32_t)CAP) {
+          if (oi < (uint32_t)CAPN) {
             ckey[oi] = okey(x);
             cpos[oi] = P(ub + 1024 * (bit >> 2) + (bit & 3));
           }
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     }
     __syncthreads();
     const uint32_t c_hi = sel_info[2], nc = sel_info[3];
-    if (c_hi < (uint32_t)k && nc <= (uint32_t)CAP && c_hi + nc >= (uint32_t)k) {
+    if (c_hi < (uint32_t)k && nc <= (uint32_t)CAPN && c_hi + nc >= (uint32_t)k) {
       // exact threshold among the candidates: need-th largest key
       uint32_t need = (uint32_t)k - c_hi;
       uint32_t prefix = 0, pmask = 0;
@@ -602,15 +610,15 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
       __syncthreads();
       if (sel_info[3] <= (uint32_t)NB) {
         const uint32_t ne = sel_info[3];
-        uint32_t tp[CAP / 256];
+        uint32_t tp[NB / 256];  // ne <= NB here
 #pragma unroll
-        for (int j = 0; j < CAP / 256; ++j) {
+        for (int j = 0; j < NB / 256; ++j) {
           const int i = tid + 256 * j;
           tp[j] = i < (int)ne ? (uint32_t)cpos[hist[i]] : 0u;
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < CAP / 256; ++j)
+        for (int j = 0; j < NB / 256; ++j)
           if (tid + 256 * j < (int)ne) ckey[tid + 256 * j] = tp[j];
       } else {
         // many ties: compact their positions in place, in steps of 256 (every
@@ -752,7 +760,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
   const uint32_t above_b = sel_info[1];
   const uint32_t in_b = hist[B];
 
-  if (in_b <= (uint32_t)CAP) {
+  if (in_b <= (uint32_t)CAPN) {
     // ---- pass 2: emit bins above B, collect bin B in position order
     uint32_t nc = 0;
     for (int base = 0; base < n; base += 256) {
@@ -1251,7 +1259,7 @@ hipError_t launch_dsa_index_topk_decode(const float* qI, const float* kI, const 
   s1.nseg = nseg;
   s1.seg_len = SEG;
   s1.n_total = n_keys;
-  hipLaunchKernelGGL(topk_select_kernel<false>, dim3(batch * nseg), dim3(256), 0, st, s1);
+  hipLaunchKernelGGL((topk_select_kernel<false, CAP_WIDE>), dim3(batch * nseg), dim3(256), 0, st, s1);
   e = hipGetLastError();
   if (e != hipSuccess || nseg == 1) return e;
   // second stage: the segments' selections, in position order, hold the top-k

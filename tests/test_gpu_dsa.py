@@ -397,10 +397,12 @@ def _decode_indexer_inputs(B, n, k, seed, di=64, hi=4, max_attempts=20):
 
 
 @pytest.mark.parametrize("B,n,topk", [(2, 1000, 2048), (2, 5000, 512), (3, 70000, 2048), (2, 150001, 2048),
-                                      (1, 131072, 4096)])
+                                      (1, 131072, 4096), (4, 262144, 2048)])
 def test_index_topk_decode_exact_sets(B, n, topk):
     """One query per sequence over n keys, through one segment (n <= 65536) or
-    the two-stage selection (several segments, the last one ragged)."""
+    the two-stage selection (several segments, the last one ragged).  The
+    sixteen full segments of the last case include one whose sampled bracket
+    admits ~4300 candidates (more than the prefill selection's LDS holds)."""
     _say("index_topk_decode", B, n, topk)
     qI, kI, w = _decode_indexer_inputs(B, n, topk, seed=n + topk)
     idx = hca.dsa_index_topk_decode(dev_f32(qI), dev_f32(kI), dev_f32(w), topk)
