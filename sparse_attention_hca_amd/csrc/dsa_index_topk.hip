@@ -439,14 +439,17 @@ __global__ __launch_bounds__(256) void topk_select_kernel(SelectParams p) {
     if (tid == 0) sel_info[2] = sel_info[3] = 0;
     __syncthreads();
     // Bracket the k-th largest key between two order statistics of the
-    // 1024-key sample (ranks r -+ delta, about 3.5 standard deviations of the sample
-    // rank of the row's k-th key), on the top 16 key bits: a coarser bracket
-    // stays correct, it only admits a few more candidates.  One wave per
+    // 1024-key sample (ranks r -+ delta, 3 standard deviations of the sample
+    // rank of the row's k-th key plus 4), on the top 16 key bits: a coarser bracket
+    // stays correct, it only admits a few more candidates.  A bracket that
+    // misses the k-th key (a few rows in a thousand) or admits more than the
+    // LDS list holds sends the row to the multi-pass paths; at 3.5 deviations
+    // plus 6, one 65536-key row in twelve overflowed the 3840-entry list.  One wave per
     // statistic bisects over the whole sample (16 keys per lane, counts by
     // ballot): the largest T with #(sample >= T) >= rank + 1 is the sample key
     // of that rank (0 = largest).
     const int r = (int)((int64_t)k * NS / n);
-    const int delta = (int)(3.5f * sqrtf((float)r * (1.f - (float)r / NS))) + 6;
+    const int delta = (int)(3.0f * sqrtf((float)r * (1.f - (float)r / NS))) + 4;
     uint32_t hi = 0xffffffffu, lo = 0u;  // keys > hi are in, keys < lo are out
     {
       // wave 0 finds the upper statistic, wave 1 the lower one
