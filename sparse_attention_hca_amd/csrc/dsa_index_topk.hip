@@ -897,11 +897,12 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const float* qI, con
   sc[(int64_t)b * ld + u] = s;
 }
 
-// The same scores for 64-wide index keys with coalesced loads: each wave
-// covers 64 keys in 4 blocks of 16, four lanes per key; load c of a block
-// reads dims 16c .. 16c+15 of its 16 keys (lane l: key l/4, dims 16c + 4(l%4)
-// .. +3), so an instruction touches 16 cache lines instead of 64.  The four
-// partial dot products of a key are summed across its lane quad.
+// The same scores for 64-wide index keys with whole-line loads: each wave
+// covers 64 keys in 8 blocks of 8, eight lanes per key; load c of a block
+// reads dims 32c .. 32c+31 of its 8 keys (lane l: key l/8, dims 32c + 4(l%8)
+// .. +3), so every instruction reads 8 whole 128-byte lines, which no other
+// instruction touches: the loads are non-temporal.  The eight partial dot
+// products of a key are summed across its lane octet.
 template <int HI>
 __global__ __launch_bounds__(256) void decode_scores64_kernel(const float* qI, const float* kI, const float* w,
                                                               float* sc, int64_t ld, int n) {
@@ -915,27 +916,27 @@ __global__ __launch_bounds__(256) void decode_scores64_kernel(const float* qI, c
   __syncthreads();
   const int key0 = blockIdx.x * 256 + 64 * w4;
   if (key0 >= n) return;
-  const int q4 = lane & 3;
-  float acc[4][HI];
+  const int p8 = lane & 7;
+  float acc[8][HI];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
     for (int h = 0; h < HI; ++h) acc[kb][h] = 0.f;
-  f32x4 kv[4][4];
+  f32x4 kv[8][2];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int u = min(key0 + 16 * kb + (lane >> 2), n - 1);
-    const float* kr = kI + ((int64_t)b * n + u) * DI + 4 * q4;
+  for (int kb = 0; kb < 8; ++kb) {
+    const int u = min(key0 + 8 * kb + (lane >> 3), n - 1);
+    const float* kr = kI + ((int64_t)b * n + u) * DI + 4 * p8;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kv[kb][c] = *reinterpret_cast<const f32x4*>(kr + 16 * c);
+    for (int c = 0; c < 2; ++c) kv[kb][c] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kr + 32 * c));
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int h = 0; h < HI; ++h) {
-      const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + h * DI + 16 * c + 4 * q4);
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + h * DI + 32 * c + 4 * p8);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 8; ++kb) {
         acc[kb][h] = fmaf(kv[kb][c][0], qv[0], acc[kb][h]);
         acc[kb][h] = fmaf(kv[kb][c][1], qv[1], acc[kb][h]);
         acc[kb][h] = fmaf(kv[kb][c][2], qv[2], acc[kb][h]);
@@ -943,17 +944,18 @@ __global__ __launch_bounds__(256) void decode_scores64_kernel(const float* qI, c
       }
     }
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < 8; ++kb) {
     float s = 0.f;
 #pragma unroll
     for (int h = 0; h < HI; ++h) {
       float a = acc[kb][h];
       a += __shfl_xor(a, 1);
       a += __shfl_xor(a, 2);
+      a += __shfl_xor(a, 4);
       s = fmaf(wsh[h], relu(a), s);
     }
-    const int u = key0 + 16 * kb + (lane >> 2);
-    if (q4 == 0 && u < n) sc[(int64_t)b * ld + u] = s;
+    const int u = key0 + 8 * kb + (lane >> 3);
+    if (p8 == 0 && u < n) sc[(int64_t)b * ld + u] = s;
   }
 }
 
