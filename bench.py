@@ -338,7 +338,9 @@ def bench_dsa_decode(torch, hca, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((B, c["h_q"]), dtype=torch.float32, device="cuda:0")
     fi = lambda: hca.dsa_index_topk_decode(qI, kI, w, c["topk"], idx=idx, workspace=ws)
-    fa = lambda: hca.dsa_sparse_attn_decode(q, k, v, idx, scale=1.0 / 16, o=o, lse=lse)
+    wsa = torch.empty(max(1, hca.dsa_sparse_attn_decode_workspace_size(B, c["h_q"], c["topk"])), dtype=torch.uint8,
+                      device="cuda:0")
+    fa = lambda: hca.dsa_sparse_attn_decode(q, k, v, idx, scale=1.0 / 16, o=o, lse=lse, workspace=wsa)
     for _ in range(warmup):
         fi()
         fa()

@@ -315,7 +315,16 @@ hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt,
  *   q: [batch, 1, h_q, d_qk]; k: [batch, n_keys, h_kv, d_qk]; v: [batch, n_keys, h_kv, d_v];
  *   idx: [batch, 1, topk] int32 contiguous; o: [batch, 1, h_q, d_v]; lse: [batch, h_q] fp32 or NULL.
  * Supported: as dsa_sparse_attn_fwd.
+ * workspace: NULL runs one workgroup per sequence and 64 query heads.  Else
+ * it must hold dsa_sparse_attn_decode_workspace_size(batch, h_q, topk) bytes
+ * (16-byte aligned, caller-owned, overlapping no tensor; contents need no
+ * initialisation and are overwritten): the index row is then split into
+ * contiguous slices that run as separate workgroups (about one per CU), and a
+ * second kernel merges the slices' bf16 outputs by their log-sum-exps.  A size
+ * of 0 means the shape gains nothing from the split (workspace ignored).
+ * HCA_ERR_WORKSPACE when a non-NULL workspace is too small.
  */
+size_t dsa_sparse_attn_decode_workspace_size(int batch, int h_q, int topk);
 hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
                                     const void* q, hca_strides_t sq,
                                     const void* k, hca_strides_t sk,
@@ -325,6 +334,7 @@ hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt,
                                     float* lse,
                                     int batch, int n_keys, int h_q, int h_kv, int d_qk, int d_v,
                                     int topk, float scale,
+                                    void* workspace, size_t workspace_bytes,
                                     void* stream);
 
 /* ---------------------------------------------------------------------------

@@ -29,6 +29,7 @@ EXPORTS = (
     "hca_abi_version", "hca_last_error", "hca_compress_kv", "hca_append_kv", "hca_attn_fwd_workspace_size",
     "hca_attn_fwd", "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
+    "dsa_sparse_attn_decode_workspace_size",
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
     "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd", "attn_output_epilogue",
@@ -86,7 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_index_topk_decode.restype = I
     lib.dsa_index_topk_decode.argtypes = [P, P, P, P, I, I, I, I, I, P, SZ, P]
     lib.dsa_sparse_attn_decode.restype = I
-    lib.dsa_sparse_attn_decode.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P]
+    lib.dsa_sparse_attn_decode.argtypes = [I, P, S, P, S, P, S, P, P, S, P, I, I, I, I, I, I, I, F, P, SZ, P]
+    lib.dsa_sparse_attn_decode_workspace_size.restype = SZ
+    lib.dsa_sparse_attn_decode_workspace_size.argtypes = [I, I, I]
     lib.csa_index_topk_workspace_size.restype = SZ
     lib.csa_index_topk_workspace_size.argtypes = [I, I, I, I]
     lib.csa_index_topk.restype = I
@@ -323,11 +326,17 @@ def dsa_index_topk_decode(q_idx: torch.Tensor, k_idx: torch.Tensor, w_idx: torch
     return idx
 
 
+def dsa_sparse_attn_decode_workspace_size(batch: int, h_q: int, topk: int) -> int:
+    return load_library().dsa_sparse_attn_decode_workspace_size(batch, h_q, topk)
+
+
 def dsa_sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                            scale: Optional[float] = None, o: Optional[torch.Tensor] = None, return_lse: bool = True,
-                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                           lse: Optional[torch.Tensor] = None, split: bool = True,
+                           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention of one query per sequence (q [B, 1, Hq, d]) over the positions listed in idx [B, 1, topk]
-    of k, v [B, n_keys, Hkv, d]; returns (o [B, 1, Hq, dv], lse [B, Hq])."""
+    of k, v [B, n_keys, Hkv, d]; returns (o [B, 1, Hq, dv], lse [B, Hq]).  With split (the default) the
+    index row runs in slices merged by a second kernel, in `workspace` (uint8, allocated when not given)."""
     lib = load_library()
     _dev(q, k, v, idx)
     B, _, Hq, dqk = q.shape
@@ -341,9 +350,15 @@ def dsa_sparse_attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, id
         o = torch.empty((B, 1, Hq, dv), dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.dsa_sparse_attn_decode_workspace_size(B, Hq, topk) if split else 0
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if not ws_bytes:
+        workspace = None
     _check(lib.dsa_sparse_attn_decode(_dt(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                       _ptr(idx), _ptr(o), _strides(o), _ptr(lse), B, n, Hq, Hkv, dqk, dv, topk,
-                                      float(scale), _stream()))
+                                      float(scale), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                      _stream()))
     return o, lse
 
 
@@ -565,6 +580,7 @@ __all__ = [
     "hca_attn_fwd",
     "dsa_index_topk_workspace_size", "dsa_index_topk", "dsa_sparse_attn_fwd",
     "dsa_index_topk_decode_workspace_size", "dsa_index_topk_decode", "dsa_sparse_attn_decode",
+    "dsa_sparse_attn_decode_workspace_size",
     "hca_attn_bwd_workspace_size", "hca_attn_bwd", "hca_compress_kv_bwd", "hca_attn_compress_bwd",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd",
     "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_attn_fwd", "attn_output_epilogue",

@@ -439,7 +439,47 @@ void sparse_attn256_kernel(SparseParams p) {
   }
 }
 
+// Merge of a decode row whose selected positions ran as `parts` query rows
+// (one per contiguous slice of the index row): each part's normalised output
+// is weighted by exp(lse_p - max lse), the log-sum-exp of the parts' softmax
+// denominators.  A part with no position (lse -inf) weighs nothing; a row with
+// no position at all is written as 0 with lse -inf; a poisoned part (NaN)
+// poisons the row, as in the single-pass kernel.  One workgroup per (head,
+// sequence), one thread per value dim.
+__global__ __launch_bounds__(256) void decode_combine256_kernel(const uint16_t* op, const float* lp, int parts,
+                                                                uint16_t* o, LStrides so, float* lse, int h_q) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const float* l = lp + ((int64_t)b * h_q + h) * parts;
+  float m = -INFINITY;
+  bool nan = false;
+  for (int i = 0; i < parts; ++i) {
+    const float x = l[i];
+    nan |= x != x;
+    m = fmaxf(m, x);
+  }
+  float acc = 0.f, s = 0.f;
+  if (m != -INFINITY) {
+    for (int i = 0; i < parts; ++i) {
+      const float wgt = __expf(l[i] - m);  // 0 for a part with no position
+      s += wgt;
+      acc = fmaf(wgt, bf16_to_f32(op[(((int64_t)b * parts + i) * h_q + h) * 256 + d]), acc);
+    }
+  }
+  float out = s > 0.f ? acc / s : 0.f;
+  float ls = s > 0.f ? m + __logf(s) : -INFINITY;
+  if (nan) out = ls = __builtin_nanf("");
+  o[b * so.b + (int64_t)h * so.h + d] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
+  if (lse && d == 0) lse[(int64_t)b * h_q + h] = ls;
+}
+
 }  // namespace
+
+hipError_t launch_dsa_decode_combine256(const void* op, const float* lp, int parts, void* o, LStrides so, float* lse,
+                                        int batch, int h_q, hipStream_t st) {
+  hipLaunchKernelGGL(decode_combine256_kernel, dim3(h_q, batch), dim3(256), 0, st, (const uint16_t*)op, lp, parts,
+                     (uint16_t*)o, so, lse, h_q);
+  return hipGetLastError();
+}
 
 hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, LStrides sk, const void* v,
                                      LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,

@@ -1,6 +1,7 @@
 // C-ABI layer of libhca: argument validation, error reporting and kernel
 // dispatch.  Every argument is checked before anything is launched, so a call
 // that fails has written nothing.  No exception, abort or exit crosses the ABI.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -654,10 +655,30 @@ hca_status_t dsa_sparse_attn_bwd(hca_dtype_t dt, const void* q, hca_strides_t sq
 
 namespace {
 // Sparse attention of seqlen_q queries per sequence over n_kv key rows.
+// A decode row (one query per sequence) runs as `parts` query rows of the
+// sparse-attention kernel, each over a contiguous slice of the index row, so
+// that about 256 workgroups (one per CU) share the work instead of one per 64
+// heads of a sequence; slices hold at least 64 positions and divide topk.
+int decode_parts(int batch, int h_q, int topk) {
+  const int64_t wg = std::max<int64_t>(1, (int64_t)batch * (h_q / 64));
+  int parts = (int)std::min<int64_t>(64, (256 + wg - 1) / wg);
+  parts = std::min(parts, topk / 64);
+  while (parts > 1 && topk % parts) --parts;
+  return std::max(parts, 1);
+}
+size_t decode_out_bytes(int batch, int h_q, int parts) {
+  return ((size_t)batch * parts * h_q * 256 * 2 + 255) / 256 * 256;
+}
+size_t decode_ws_bytes(int batch, int h_q, int topk) {
+  const int parts = decode_parts(batch, h_q, topk);
+  if (parts <= 1) return 0;
+  return decode_out_bytes(batch, h_q, parts) + (size_t)batch * h_q * parts * sizeof(float);
+}
+
 hca_status_t sparse_attn(const char* name, hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k,
                          hca_strides_t sk, const void* v, hca_strides_t sv, const int32_t* idx, void* o,
                          hca_strides_t so, float* lse, int batch, int seqlen_q, int n_kv, int h_q, int h_kv, int d_qk,
-                         int d_v, int topk, float scale, void* stream) {
+                         int d_v, int topk, float scale, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
   if (dt != HCA_DTYPE_F32 && dt != HCA_DTYPE_BF16) return fail(HCA_ERR_INVALID, "unknown dtype %d", (int)dt);
   if (batch <= 0 || seqlen_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
     return fail(HCA_ERR_INVALID, "%s: sizes must be positive", name);
@@ -681,6 +702,33 @@ hca_status_t sparse_attn(const char* name, hca_dtype_t dt, const void* q, hca_st
         (lse && overlaps(ro, flat_extent(lse, (int64_t)batch * h_q * seqlen_q, 4))))
       return fail(HCA_ERR_INVALID, "o overlaps an input");
   }
+  const int parts = ws ? decode_parts(batch, h_q, topk) : 1;
+  if (seqlen_q == 1 && parts > 1) {
+    const size_t need = decode_ws_bytes(batch, h_q, topk);
+    if (ws_bytes < need)
+      return fail(HCA_ERR_WORKSPACE, "%s needs a %zu-byte workspace (got %zu)", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(HCA_ERR_INVALID, "workspace is not 16-byte aligned");
+    const Range rw = flat_extent(ws, (int64_t)need, 1);
+    if (overlaps(rw, extent(o, so, batch, 1, h_q, d_v, es)) ||
+        overlaps(rw, extent(q, sq, batch, 1, h_q, d_qk, es)) ||
+        overlaps(rw, extent(k, sk, batch, n_kv, h_kv, d_qk, es)) ||
+        overlaps(rw, extent(v, sv, batch, n_kv, h_kv, d_v, es)) ||
+        overlaps(rw, flat_extent(idx, (int64_t)batch * topk, 4)) ||
+        (lse && overlaps(rw, flat_extent(lse, (int64_t)batch * h_q, 4))))
+      return fail(HCA_ERR_INVALID, "%s: workspace overlaps a tensor", name);
+    // part i of sequence b is query row i over idx[b, i*topk/parts ..): q row
+    // stride 0, the index row read as parts rows of topk/parts
+    hca::LStrides sqp = ls(sq);
+    sqp.s = 0;
+    const hca::LStrides sop{(int64_t)parts * h_q * 256, (int64_t)h_q * 256, 256};
+    float* lp = (float*)((char*)ws + decode_out_bytes(batch, h_q, parts));
+    hipError_t e = hca::launch_dsa_sparse_attn256(q, sqp, k, ls(sk), v, ls(sv), idx, ws, sop, lp, batch, parts, n_kv,
+                                                  h_q, h_kv, topk / parts, scale, (hipStream_t)stream);
+    if (e == hipSuccess)
+      e = hca::launch_dsa_decode_combine256(ws, lp, parts, o, ls(so), lse, batch, h_q, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, name);
+    return HCA_OK;
+  }
   hipError_t e = hca::launch_dsa_sparse_attn256(q, ls(sq), k, ls(sk), v, ls(sv), idx, o, ls(so), lse, batch, seqlen_q,
                                                 n_kv, h_q, h_kv, topk, scale, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, name);
@@ -698,12 +746,17 @@ hca_status_t dsa_sparse_attn_fwd(hca_dtype_t dt, const void* q, hca_strides_t sq
                      h_kv, d_qk, d_v, topk, scale, stream);
 }
 
+size_t dsa_sparse_attn_decode_workspace_size(int batch, int h_q, int topk) {
+  if (batch <= 0 || h_q <= 0 || topk <= 0) return 0;
+  return decode_ws_bytes(batch, h_q, topk);
+}
+
 hca_status_t dsa_sparse_attn_decode(hca_dtype_t dt, const void* q, hca_strides_t sq, const void* k, hca_strides_t sk,
                                     const void* v, hca_strides_t sv, const int32_t* idx, void* o, hca_strides_t so,
                                     float* lse, int batch, int n_keys, int h_q, int h_kv, int d_qk, int d_v, int topk,
-                                    float scale, void* stream) {
+                                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_attn("dsa_sparse_attn_decode", dt, q, sq, k, sk, v, sv, idx, o, so, lse, batch, 1, n_keys, h_q, h_kv,
-                     d_qk, d_v, topk, scale, stream);
+                     d_qk, d_v, topk, scale, stream, workspace, workspace_bytes);
 }
 
 size_t csa_index_topk_workspace_size(int batch, int seqlen, int n_entries, int topk) {

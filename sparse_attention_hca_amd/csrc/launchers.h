@@ -122,6 +122,10 @@ hipError_t launch_csa_index_topk(const float* qI, const float* kIc, const float*
 hipError_t launch_dsa_sparse_attn256(const void* q, LStrides sq, const void* k, LStrides sk, const void* v,
                                      LStrides sv, const int32_t* idx, void* o, LStrides so, float* lse, int batch,
                                      int seqlen, int n_kv, int h_q, int h_kv, int topk, float scale, hipStream_t st);
+// Merge of a split decode row: op [batch, parts, h_q, 256] bf16 partial outputs,
+// lp [batch, h_q, parts] their log-sum-exps; writes o (row 0 of each sequence) and lse.
+hipError_t launch_dsa_decode_combine256(const void* op, const float* lp, int parts, void* o, LStrides so, float* lse,
+                                        int batch, int h_q, hipStream_t st);
 
 // Attention-output epilogue: y = sigmoid(c W_g^T) * (o + (U V) o across heads),
 // one fused kernel.  Token (b, t) of c at c + b*scb + t*scs (d_c contiguous);

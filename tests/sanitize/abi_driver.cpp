@@ -231,7 +231,20 @@ int main() {
                                                      0.0625f, nullptr), HCA_ERR_INVALID);
     const hca_strides_t sqd = C(1, Hq, D);
     EXPECT("sparse decode", dsa_sparse_attn_decode(BF, q, sqd, k, skv, v, skv, idx, o, sqd, lse, B, S, Hq, Hkv, D, D, K,
-                                                   0.0625f, nullptr), HCA_OK);
+                                                   0.0625f, nullptr, 0, nullptr), HCA_OK);
+    {
+      const size_t wsd = dsa_sparse_attn_decode_workspace_size(B, Hq, 128);
+      if (!wsd) EXPECT("sparse decode split size", HCA_ERR_INVALID, HCA_OK);
+      // top-128 over 64 heads: two slices of 64 positions (idx holds B * S * K >= 128 entries)
+      if (wsd) {
+        void* w = A(wsd);
+        EXPECT("sparse decode split", dsa_sparse_attn_decode(BF, q, sqd, k, skv, v, skv, idx, o, sqd, lse, B, S, Hq, Hkv,
+                                                             D, D, 128, 0.0625f, w, wsd, nullptr), HCA_OK);
+        EXPECT("sparse decode split small ws", dsa_sparse_attn_decode(BF, q, sqd, k, skv, v, skv, idx, o, sqd, lse, B, S,
+                                                                      Hq, Hkv, D, D, 128, 0.0625f, w, wsd - 1, nullptr),
+               HCA_ERR_WORKSPACE);
+      }
+    }
     void* dout = A(size_t(B) * S * Hq * D * 2);
     float* dq = AT<float>(size_t(B) * S * Hq * D); float* dk = AT<float>(size_t(B) * S * D);
     float* dv = AT<float>(size_t(B) * S * D);

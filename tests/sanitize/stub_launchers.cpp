@@ -58,6 +58,8 @@ hipError_t launch_csa_index_topk(const float*, const float*, const float*, int32
 hipError_t launch_dsa_sparse_attn256(const void*, LStrides, const void*, LStrides, const void*, LStrides,
                                      const int32_t*, void*, LStrides, float*, int, int, int, int, int, int, float,
                                      hipStream_t) { return hit(); }
+hipError_t launch_dsa_decode_combine256(const void*, const float*, int, void*, LStrides, float*, int, int,
+                                        hipStream_t) { return hit(); }
 hipError_t launch_attn_output_epilogue(const void*, LStrides, const void*, int64_t, int64_t, const void*,
                                        const float*, const float*, void*, LStrides, int, int, int, int, int, int,
                                        hipStream_t) { return hit(); }

@@ -168,13 +168,23 @@ def test_dsa_decode_rejects_bad_arguments():
     sp = lambda **kw: lib.dsa_sparse_attn_decode(kw.get("dt", 1), FAKE, S(0, 64 * 256, 256), FAKE, S(0, 256, 256),
                                                  FAKE, S(0, 256, 256), kw.get("idx", ctypes.c_void_p(1 << 33)),
                                                  kw.get("o", ctypes.c_void_p(1 << 34)), S(0, 64 * 256, 256), None,
-                                                 1, kw.get("n", 100000), 64, 1, kw.get("d", 256), 256, 16, 0.0625,
-                                                 None)
+                                                 1, kw.get("n", 100000), 64, 1, kw.get("d", 256), 256,
+                                                 kw.get("k", 16), 0.0625, kw.get("ws", None), kw.get("wsb", 0), None)
     assert sp(idx=None) == hca.HCA_ERR_INVALID
     assert sp(n=0) == hca.HCA_ERR_INVALID
     assert sp(d=128) == hca.HCA_ERR_UNSUPPORTED
     assert sp(o=FAKE) == hca.HCA_ERR_INVALID           # o aliases q
     assert sp(o=ctypes.c_void_p((1 << 20) + 4096)) == hca.HCA_ERR_INVALID  # o inside the 100000 key rows
+    # the split decode: 1 sequence x 64 heads, top-2048 -> 32 slices of 64 positions
+    wsd = lib.dsa_sparse_attn_decode_workspace_size(1, 64, 2048)
+    assert wsd == 32 * 64 * 256 * 2 + 64 * 32 * 4
+    assert lib.dsa_sparse_attn_decode_workspace_size(16, 64, 2048) == 16 * 16 * 64 * 256 * 2 + 16 * 64 * 16 * 4
+    assert lib.dsa_sparse_attn_decode_workspace_size(1, 64, 100) == 0      # slices under 64 positions: no split
+    assert lib.dsa_sparse_attn_decode_workspace_size(256, 64, 2048) == 0   # a full chip already
+    big = ctypes.c_void_p(1 << 36)
+    assert sp(k=2048, ws=big, wsb=wsd - 1) == hca.HCA_ERR_WORKSPACE
+    assert sp(k=2048, ws=ctypes.c_void_p((1 << 36) + 8), wsb=wsd) == hca.HCA_ERR_INVALID  # misaligned
+    assert sp(k=2048, ws=FAKE, wsb=wsd) == hca.HCA_ERR_INVALID             # workspace overlaps q
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

@@ -480,3 +480,48 @@ def test_sparse_attention_decode_rejects_out_of_range_positions():
     o, lse = hca.dsa_sparse_attn_decode(q, k, v, idx)
     torch.cuda.synchronize()
     assert torch.isfinite(o[0].float()).all() and torch.isnan(o[1].float()).all()
+
+
+@pytest.mark.gpu
+def test_sparse_attention_decode_split_matches_oracle_and_single_pass():
+    """The split decode (index row in slices, merged by log-sum-exp) against
+    the oracle and the single-pass kernel: full rows, a row padded with -1
+    so that most slices are empty, and a row with no position at all."""
+    B, Hq, d, n, topk = 4, 64, 256, 70000, 2048
+    rng = np.random.default_rng(91)
+    q = synth.bf16_round_bits(rng.standard_normal((B, 1, Hq, d)))
+    k = synth.bf16_round_bits(rng.standard_normal((B, n, 1, d)))
+    v = synth.bf16_round_bits(rng.standard_normal((B, n, 1, d)))
+    idx = np.full((B, 1, topk), -1, dtype=np.int32)
+    for b, m in enumerate((topk, topk - 37, 100, 0)):
+        idx[b, 0, :m] = rng.choice(n, m, replace=False)
+    assert hca.dsa_sparse_attn_decode_workspace_size(B, Hq, topk) > 0
+    _say("sparse decode split", B, n, topk)
+    qd, kd, vd, ix = dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(idx).cuda()
+    o, lse = hca.dsa_sparse_attn_decode(qd, kd, vd, ix, scale=1.0 / 16)
+    o1, lse1 = hca.dsa_sparse_attn_decode(qd, kd, vd, ix, scale=1.0 / 16, split=False)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.sparse_attention(f64(q[:3], True), f64(k[:3], True), f64(v[:3], True), idx[:3], 1.0 / 16,
+                                       rows=[0])
+    assert rel_err(host(o)[:3], ro) < BF16_TOL
+    assert np.max(np.abs(host(lse)[:3] - rlse[:, :, 0])) < LSE_TOL
+    assert rel_err(host(o)[:3], host(o1)[:3]) < BF16_TOL
+    # no position: zero output, lse -inf, as the single-pass kernel writes it
+    assert (host(o)[3] == 0).all() and np.isneginf(host(lse)[3]).all()
+    assert (host(o1)[3] == 0).all() and np.isneginf(host(lse1)[3]).all()
+
+
+@pytest.mark.gpu
+def test_sparse_attention_decode_split_poisons_row():
+    """An out-of-range position in one slice poisons the whole merged row."""
+    B, Hq, d, n, topk = 2, 64, 256, 3000, 2048
+    assert hca.dsa_sparse_attn_decode_workspace_size(B, Hq, topk) > 0
+    q = torch.randn(B, 1, Hq, d, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B, n, 1, d, device="cuda").to(torch.bfloat16)
+    v = torch.randn_like(k)
+    idx = torch.arange(topk, dtype=torch.int32, device="cuda").repeat(B, 1, 1).contiguous()
+    idx[1, 0, 1500] = n
+    o, lse = hca.dsa_sparse_attn_decode(q, k, v, idx)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o[0].float()).all() and torch.isfinite(lse[0]).all()
+    assert torch.isnan(o[1].float()).all() and torch.isnan(lse[1]).all()
