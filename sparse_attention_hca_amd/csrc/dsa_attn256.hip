@@ -452,6 +452,7 @@ __global__ __launch_bounds__(256) void decode_combine256_kernel(const uint16_t* 
   const float* l = lp + ((int64_t)b * h_q + h) * parts;
   float m = -INFINITY;
   bool nan = false;
+#pragma unroll 8
   for (int i = 0; i < parts; ++i) {
     const float x = l[i];
     nan |= x != x;
@@ -459,6 +460,8 @@ __global__ __launch_bounds__(256) void decode_combine256_kernel(const uint16_t* 
   }
   float acc = 0.f, s = 0.f;
   if (m != -INFINITY) {
+    // unrolled so that several slices' loads are in flight at once
+#pragma unroll 8
     for (int i = 0; i < parts; ++i) {
       const float wgt = __expf(l[i] - m);  // 0 for a part with no position
       s += wgt;
